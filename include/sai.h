@@ -1,0 +1,215 @@
+/*
+ * sai.h -- C ABI of the MI355X (gfx950) paged lightning-indexer library.
+ *
+ * The library implements DeepSeek-V3.2's sparse-attention indexer over a
+ * paged fp8 K cache: the K-cache write, the query producer, fp8 paged MQA
+ * logits, prefill logits over gathered K, per-row top-k and the
+ * request-local -> global slot-id map.  Every call is a set of hand-written
+ * HIP kernels launched on the caller's stream.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Pointers are DEVICE pointers owned by the caller; the library never
+ *    allocates, frees or keeps them, and holds no state between calls.
+ *    (Preallocated outputs written in place, as the review of
+ *    cp_gather_indexer_k_quant_cache in vLLM PR #25869 asks for.)
+ *  - Scalars are host values.  Validation reads host scalars only: no call
+ *    reads device memory on the host, synchronises, or allocates, so every
+ *    call can be captured into a hipGraph (the failure fixed by vLLM PR
+ *    #36250 "[kernel] Fix FP8 paged MQA fallback for CUDA graph capture",
+ *    Purpose, was a host read of a context length inside the op).
+ *  - Device-side values outside their documented range (a context longer
+ *    than the block table, a block id outside the pool, ...) are the
+ *    caller's error; kernels bounds-check every address they form and never
+ *    read or write outside the buffers described here; results for such
+ *    entries are documented per call.
+ *  - Return value: SAI_OK (0) or a negative SAI_E* code; nothing is launched
+ *    when a code other than SAI_OK or SAI_ELAUNCH is returned.
+ *  - Fixed shapes: 64 indexer heads, head_dim 128, 64-token cache blocks,
+ *    top-k of at most 2048.
+ *  - Alignment: q, K, the cache, the weights and the logits must be 16-byte
+ *    aligned; strides are in elements.
+ */
+#ifndef SAI_H
+#define SAI_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SAI_HEADS 64
+#define SAI_HEAD_DIM 128
+#define SAI_BLOCK_SIZE 64
+/* one cache block: 64*128 fp8 e4m3fn values, then 64 fp32 scales */
+#define SAI_BLOCK_BYTES 8448
+#define SAI_TOPK_MAX 2048
+#define SAI_NEXT_N_MAX 4
+
+#define SAI_OK 0
+#define SAI_EINVAL (-1)       /* null pointer, negative size, stride too small, misalignment */
+#define SAI_EUNSUPPORTED (-2) /* shape outside what the kernels are built for */
+#define SAI_EWORKSPACE (-3)   /* workspace missing or too small */
+#define SAI_ELAUNCH (-4)      /* the HIP runtime rejected a launch */
+
+/* Human-readable name of a status code (static storage). */
+const char* sai_status_string(int status);
+
+/*
+ * indexer_k_cache_write -- quantise K rows to fp8 and scatter them into the
+ * paged indexer K cache.
+ *
+ * Quantiser (prhub summary of vLLM PR #47090, key source excerpt of
+ * _fused_norm_rope_kernel, applied to one 128-value token row):
+ *   amax = max_i |k_i|;  scale = max(amax * fl32(1/448), 1.1754944e-38);
+ *   code_i = fp8_e4m3fn(k_i / scale), round to nearest even, saturating at
+ *   +-448; all float32.
+ * Layout (vLLM PR #25869, review of cp_gather_indexer_k_quant_cache): slot s
+ * is token s % 64 of block s / 64; its codes go to bytes [t*128, t*128+128)
+ * of the block and its scale to byte 8192 + 4t.
+ *
+ *   k_bf16        [n, k_row_stride] bf16, first 128 values of a row used
+ *   k_row_stride  elements between rows (>= 128, multiple of 8)
+ *   slot_mapping  [n] int64; a negative slot is skipped; a slot at or past
+ *                 num_blocks*64 is skipped
+ *   kv_cache      [num_blocks, 8448] uint8, written only at the owned bytes
+ */
+int indexer_k_cache_write(const void* k_bf16, int64_t k_row_stride,
+                          const int64_t* slot_mapping, int64_t n,
+                          void* kv_cache, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * indexer_q_quant -- query producer: fp8 query codes with one scale per
+ * token (over all 64x128 values), folded into that token's head weights.
+ *
+ * Same quantiser as indexer_k_cache_write over a whole token.  Because ReLU
+ * is positively homogeneous, w*ReLU(s*x) = (w*s)*ReLU(x) for s > 0, so the
+ * scale is folded: w_eff[r,h] = fl32(weights[r,h] * q_scale[r]).
+ *
+ *   q_bf16   [rows, 64, 128] bf16 (contiguous)
+ *   weights  [rows, 64] fp32
+ *   q_fp8    [rows, 64, 128] fp8 e4m3fn codes (output)
+ *   w_eff    [rows, 64] fp32 (output)
+ *   q_scale  [rows] fp32 (output, may be NULL)
+ */
+int indexer_q_quant(const void* q_bf16, const float* weights, int64_t rows,
+                    void* q_fp8, float* w_eff, float* q_scale, hipStream_t stream);
+
+/*
+ * gather_indexer_k -- paged -> contiguous copy of K codes and scales for
+ * prefill (vLLM PR #25869, review of cp_gather_indexer_k_quant_cache):
+ * request b owns output rows [cu[b], cu[b+1]); token t < cu[b+1]-cu[b]
+ * of request b is token t % 64 of block block_table[b*bt_stride + t/64].
+ * Empty requests are skipped.  Rows not owned by any request (before cu[0]
+ * or at/after cu[batch]) are left untouched.  A block id outside
+ * [0, num_blocks) yields NaN codes (0x7F) and NaN scales for its tokens.
+ *
+ *   block_table   [batch, bt_stride] int32
+ *   cu_seq_lens   [batch+1] int32, non-decreasing, cu[batch] <= total_tokens
+ *   out_k_fp8     [total_tokens, 128] fp8 codes;  out_scale [total_tokens] fp32
+ */
+int gather_indexer_k(const void* kv_cache, int64_t num_blocks,
+                     const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* cu_seq_lens, int32_t batch, int64_t total_tokens,
+                     void* out_k_fp8, float* out_scale, hipStream_t stream);
+
+/*
+ * paged_mqa_logits -- fp8 paged MQA logits of the indexer (the op vLLM PR
+ * #36250 names fp8_paged_mqa_logits; its formula, not printed on the pages,
+ * is the DeepSeek-V3.2 lightning-indexer score):
+ *
+ *   logits[r, s] = k_scale[s] * sum_{h<64} w_eff[r, h] * max(q[r,h,:] . k[s,:], 0)
+ *
+ * for query row r = b*next_n + j (token j of request b) and request-local
+ * key s < limit(r) = ctx_b - next_n + j + 1; columns limit(r) <= s <
+ * logits_stride are -inf ("clean logits", vLLM PR #36250 review thread).
+ * Every column of every row is written.  Dot products run on fp8 MFMA with
+ * fp32 accumulation; the ReLU, head weights and scale are fp32 (fp32, not
+ * fp16, dequantisation: vLLM PR #36250 review thread).
+ *
+ *   q_fp8         [batch*next_n, 64, 128] fp8 e4m3fn codes
+ *   weights       [batch*next_n, 64] fp32 (w_eff of indexer_q_quant)
+ *   kv_cache      [num_blocks, 8448] uint8 (layout of indexer_k_cache_write)
+ *   block_table   [batch, bt_stride] int32, entry c = physical block of keys
+ *                 [64c, 64c+64) of the request; only the first
+ *                 ceil(ctx_b/64) entries are read
+ *   context_lens  [batch] int32 (device); ctx_b is clamped to
+ *                 [0, min(logits_stride, 64*bt_stride)]
+ *   next_n        1..4 query tokens per request
+ *   logits        [batch*next_n, logits_stride] fp32 (output)
+ *   row_len_out   [batch*next_n] int32, limit(r) after clamping (may be NULL)
+ *   row_req_out   [batch*next_n] int32, request b of row r (may be NULL)
+ * A block id outside [0, num_blocks) makes that block's visible columns NaN.
+ */
+int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
+                     int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                     const int32_t* context_lens, int32_t batch, int32_t next_n,
+                     float* logits, int64_t logits_stride,
+                     int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
+
+/*
+ * mqa_logits -- prefill logits against contiguous K (the output of
+ * gather_indexer_k).  Not one of the calls the pages name: the prefill path
+ * scores gathered K (vLLM PR #25869, review of cp_gather_indexer_k_quant_cache;
+ * ROCm/ATOM PR #1094, Technical Details, "sparse MLA prefill KV mapping"),
+ * and no paged call takes contiguous K, so this entry is added.
+ *
+ * Same score as paged_mqa_logits.  Token p = cu[b] + i of request b sees the
+ * request's keys 0..i (causal); column j is the request-local key index
+ * (K row cu[b] + j).  Columns i+1 .. logits_stride-1 are -inf.  Rows of no
+ * request are left untouched.
+ *
+ *   q_fp8 [total_tokens, 64, 128]; weights [total_tokens, 64];
+ *   k_fp8 [total_tokens, 128]; k_scale [total_tokens];
+ *   cu_seq_lens [batch+1] int32 (device), cu[batch] <= total_tokens;
+ *   logits [total_tokens, logits_stride];
+ *   row_len_out / row_req_out: [total_tokens] int32, i+1 and b (may be NULL)
+ * A request longer than logits_stride is scored only on its first
+ * logits_stride tokens and keys; its later rows are left untouched.
+ */
+int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
+               const float* k_scale, const int32_t* cu_seq_lens, int32_t batch,
+               int64_t total_tokens, float* logits, int64_t logits_stride,
+               int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
+
+/*
+ * topk_rows -- per-row top-k of the indexer logits (ROCm/ATOM PR #1094,
+ * Technical Details: sparse top-k handed on in a 2-D index buffer).
+ *
+ * Row r ranks its columns s < n_r = clamp(row_len[r], 0, logits_stride) by
+ * (larger logit, then lower index); -0.0 and +0.0 are equal.  It writes the
+ * min(k, n_r) winners in ascending column order, then -1 up to k.  NaN
+ * inside a row is outside the contract.
+ *
+ *   logits   [rows, logits_stride] fp32
+ *   row_len  [rows] int32 (device)
+ *   k        1..2048
+ *   out_idx  [rows, k] int32 (output)
+ *   workspace / workspace_bytes: scratch of at least
+ *   topk_workspace_bytes(rows, logits_stride, k) bytes (may be NULL if that
+ *   is 0); contents need no initialisation.
+ */
+size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
+int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,
+              int32_t rows, int32_t k, int32_t* out_idx,
+              void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * topk_to_global_slots -- request-local top-k indices -> global paged KV
+ * slot ids (ROCm/ATOM PR #1094, Technical Details):
+ *   out[r, j] = block_table[b*bt_stride + i/64] * 64 + i % 64,
+ * with i = topk_idx[r, j] and b = row_req[r].  -1 stays -1; so does an index
+ * whose block-table entry is outside the table or negative, or a row whose
+ * request is outside [0, batch).
+ */
+int topk_to_global_slots(const int32_t* topk_idx, const int32_t* row_req,
+                         const int32_t* block_table, int64_t bt_stride, int32_t batch,
+                         int32_t rows, int32_t k, int32_t* out_slots, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* SAI_H */

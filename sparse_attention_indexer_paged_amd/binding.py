@@ -1,0 +1,247 @@
+"""ctypes binding of libsai.so (argument marshalling only).
+
+Each function has the name of the C entry point it calls (include/sai.h),
+checks dtypes, devices, shapes and contiguity of the torch tensors, passes
+their device pointers and the current HIP stream, and raises on a non-zero
+status.  Every step of the indexer runs in the library's HIP kernels; torch
+only provides device memory and the stream.  There is no fallback: without
+the built library every call raises.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsai.so")
+
+HEADS = 64
+DIM = 128
+BLOCK = 64
+BLOCK_BYTES = 8448
+TOPK_MAX = 2048
+
+_c_void_p = ctypes.c_void_p
+_i32 = ctypes.c_int32
+_i64 = ctypes.c_int64
+
+# name -> argtypes (restype int unless listed in _RESTYPE)
+SIGNATURES = {
+    "sai_status_string": [ctypes.c_int],
+    "indexer_k_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
+    "indexer_q_quant": [_c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "gather_indexer_k": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32, _i64, _c_void_p,
+                         _c_void_p, _c_void_p],
+    "paged_mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32,
+                         _i32, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p],
+    "mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _c_void_p,
+                   _i64, _c_void_p, _c_void_p, _c_void_p],
+    "topk_workspace_bytes": [_i32, _i64, _i32],
+    "topk_rows": [_c_void_p, _i64, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, ctypes.c_size_t,
+                  _c_void_p],
+    "topk_to_global_slots": [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
+                             _c_void_p],
+}
+_RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t}
+
+_lib = None
+
+
+def load():
+    """Load libsai.so once; raise if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"{LIB_PATH} is missing: build it with "
+                "`python -m sparse_attention_indexer_paged_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, args in SIGNATURES.items():
+            fn = getattr(lib, name)
+            fn.argtypes = args
+            fn.restype = _RESTYPE.get(name, ctypes.c_int)
+        _lib = lib
+    return _lib
+
+
+def status_string(code):
+    return load().sai_status_string(code).decode()
+
+
+def _check(code, name):
+    if code != 0:
+        raise RuntimeError(f"{name} failed: {status_string(code)} ({code})")
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else ctypes.c_void_p(0)
+
+
+def _need(t, dtype, name, ndim=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+# ---------------------------------------------------------------- calls
+def indexer_k_cache_write(k_bf16, slot_mapping, kv_cache):
+    """Quantise K rows [n, 128] bf16 into the paged cache [num_blocks, 8448] u8 in place."""
+    _need(k_bf16, torch.bfloat16, "k_bf16", 2)
+    _need(slot_mapping, torch.int64, "slot_mapping", 1)
+    _need(kv_cache, torch.uint8, "kv_cache", 2)
+    if k_bf16.shape[1] != DIM or kv_cache.shape[1] != BLOCK_BYTES:
+        raise ValueError("k_bf16 must be [n,128] and kv_cache [num_blocks, 8448]")
+    if slot_mapping.shape[0] != k_bf16.shape[0]:
+        raise ValueError("slot_mapping must have one entry per K row")
+    if k_bf16.shape[0] == 0:
+        return kv_cache
+    _check(load().indexer_k_cache_write(_ptr(k_bf16), k_bf16.stride(0), _ptr(slot_mapping),
+                                        k_bf16.shape[0], _ptr(kv_cache), kv_cache.shape[0],
+                                        _stream()), "indexer_k_cache_write")
+    return kv_cache
+
+
+def indexer_q_quant(q_bf16, weights, q_fp8=None, w_eff=None, q_scale=None):
+    """q [T,64,128] bf16, weights [T,64] fp32 -> (q_fp8 u8 [T,64,128], w_eff [T,64], q_scale [T])."""
+    _need(q_bf16, torch.bfloat16, "q_bf16", 3)
+    _need(weights, torch.float32, "weights", 2)
+    T = q_bf16.shape[0]
+    if tuple(q_bf16.shape[1:]) != (HEADS, DIM) or tuple(weights.shape) != (T, HEADS):
+        raise ValueError("q_bf16 must be [T,64,128] and weights [T,64]")
+    dev = q_bf16.device
+    q_fp8 = torch.empty((T, HEADS, DIM), dtype=torch.uint8, device=dev) if q_fp8 is None else q_fp8
+    w_eff = torch.empty((T, HEADS), dtype=torch.float32, device=dev) if w_eff is None else w_eff
+    q_scale = torch.empty((T,), dtype=torch.float32, device=dev) if q_scale is None else q_scale
+    _need(q_fp8, torch.uint8, "q_fp8")
+    _need(w_eff, torch.float32, "w_eff")
+    _need(q_scale, torch.float32, "q_scale")
+    _check(load().indexer_q_quant(_ptr(q_bf16), _ptr(weights), T, _ptr(q_fp8), _ptr(w_eff),
+                                  _ptr(q_scale), _stream()), "indexer_q_quant")
+    return q_fp8, w_eff, q_scale
+
+
+def gather_indexer_k(kv_cache, block_table, cu_seq_lens, total_tokens, out_k=None, out_scale=None):
+    """Paged -> contiguous K for prefill: (k_fp8 u8 [total,128], k_scale f32 [total])."""
+    _need(kv_cache, torch.uint8, "kv_cache", 2)
+    _need(block_table, torch.int32, "block_table", 2)
+    _need(cu_seq_lens, torch.int32, "cu_seq_lens", 1)
+    batch = cu_seq_lens.shape[0] - 1
+    if block_table.shape[0] < batch:
+        raise ValueError("block_table has fewer rows than requests")
+    dev = kv_cache.device
+    out_k = torch.empty((total_tokens, DIM), dtype=torch.uint8, device=dev) if out_k is None else out_k
+    out_scale = torch.empty((total_tokens,), dtype=torch.float32, device=dev) if out_scale is None else out_scale
+    _need(out_k, torch.uint8, "out_k")
+    _need(out_scale, torch.float32, "out_scale")
+    _check(load().gather_indexer_k(_ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
+                                   block_table.stride(0), _ptr(cu_seq_lens), batch, total_tokens,
+                                   _ptr(out_k), _ptr(out_scale), _stream()), "gather_indexer_k")
+    return out_k, out_scale
+
+
+def paged_mqa_logits(q_fp8, weights, kv_cache, block_table, context_lens, width=None,
+                     logits=None, row_len=None, row_req=None):
+    """Decode logits.  q_fp8 u8 [B, next_n, 64, 128]; weights f32 [B*next_n, 64];
+    block_table i32 [B, bt_width]; context_lens i32 [B].  Row width defaults to
+    bt_width*64.  Returns (logits f32 [B*next_n, width], row_len i32, row_req i32)."""
+    _need(q_fp8, torch.uint8, "q_fp8", 4)
+    _need(weights, torch.float32, "weights", 2)
+    _need(kv_cache, torch.uint8, "kv_cache", 2)
+    _need(block_table, torch.int32, "block_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, next_n = q_fp8.shape[0], q_fp8.shape[1]
+    if tuple(q_fp8.shape[2:]) != (HEADS, DIM) or tuple(weights.shape) != (B * next_n, HEADS):
+        raise ValueError("q_fp8 must be [B,next_n,64,128] and weights [B*next_n,64]")
+    if context_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("context_lens and block_table need one row per request")
+    rows = B * next_n
+    width = block_table.shape[1] * BLOCK if width is None else width
+    dev = q_fp8.device
+    logits = torch.empty((rows, width), dtype=torch.float32, device=dev) if logits is None else logits
+    row_len = torch.empty((rows,), dtype=torch.int32, device=dev) if row_len is None else row_len
+    row_req = torch.empty((rows,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    _check(load().paged_mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(kv_cache), kv_cache.shape[0],
+                                   _ptr(block_table), block_table.stride(0), _ptr(context_lens),
+                                   B, next_n, _ptr(logits), logits.stride(0), _ptr(row_len),
+                                   _ptr(row_req), _stream()), "paged_mqa_logits")
+    return logits, row_len, row_req
+
+
+def mqa_logits(q_fp8, weights, k_fp8, k_scale, cu_seq_lens, width, logits=None, row_len=None,
+               row_req=None):
+    """Prefill logits over contiguous K.  q_fp8 u8 [total,64,128]; weights f32
+    [total,64]; k_fp8 u8 [total,128]; k_scale f32 [total]; cu_seq_lens i32 [B+1]."""
+    _need(q_fp8, torch.uint8, "q_fp8", 3)
+    _need(weights, torch.float32, "weights", 2)
+    _need(k_fp8, torch.uint8, "k_fp8", 2)
+    _need(k_scale, torch.float32, "k_scale", 1)
+    _need(cu_seq_lens, torch.int32, "cu_seq_lens", 1)
+    total = q_fp8.shape[0]
+    if k_fp8.shape[0] != total or k_scale.shape[0] != total or weights.shape[0] != total:
+        raise ValueError("q, weights, k and k_scale need one row per token")
+    batch = cu_seq_lens.shape[0] - 1
+    dev = q_fp8.device
+    logits = torch.empty((total, width), dtype=torch.float32, device=dev) if logits is None else logits
+    row_len = torch.empty((total,), dtype=torch.int32, device=dev) if row_len is None else row_len
+    row_req = torch.empty((total,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    _check(load().mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(k_fp8), _ptr(k_scale),
+                             _ptr(cu_seq_lens), batch, total, _ptr(logits), logits.stride(0),
+                             _ptr(row_len), _ptr(row_req), _stream()), "mqa_logits")
+    return logits, row_len, row_req
+
+
+def topk_workspace_bytes(rows, logits_stride, k):
+    return int(load().topk_workspace_bytes(rows, logits_stride, k))
+
+
+def topk_rows(logits, row_len, k=TOPK_MAX, out=None, workspace=None):
+    """Top-k column indices per row (ascending, -1 padded): int32 [rows, k]."""
+    _need(logits, torch.float32, "logits", 2)
+    _need(row_len, torch.int32, "row_len", 1)
+    rows = logits.shape[0]
+    if row_len.shape[0] != rows:
+        raise ValueError("row_len needs one entry per row")
+    dev = logits.device
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev) if out is None else out
+    _need(out, torch.int32, "out")
+    ws_bytes = topk_workspace_bytes(rows, logits.stride(0), k)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    _check(load().topk_rows(_ptr(logits), logits.stride(0), _ptr(row_len), rows, k, _ptr(out),
+                            _ptr(workspace), workspace.numel() if workspace is not None else 0,
+                            _stream()), "topk_rows")
+    return out
+
+
+def topk_to_global_slots(topk_idx, row_req, block_table, out=None):
+    """Request-local top-k indices -> global paged KV slot ids (int32, -1 kept)."""
+    _need(topk_idx, torch.int32, "topk_idx", 2)
+    _need(row_req, torch.int32, "row_req", 1)
+    _need(block_table, torch.int32, "block_table", 2)
+    rows, k = topk_idx.shape
+    out = torch.empty_like(topk_idx) if out is None else out
+    _need(out, torch.int32, "out")
+    _check(load().topk_to_global_slots(_ptr(topk_idx), _ptr(row_req), _ptr(block_table),
+                                       block_table.stride(0), block_table.shape[0], rows, k,
+                                       _ptr(out), _stream()), "topk_to_global_slots")
+    return out
+
+
+def decode_indexer(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None):
+    """The decode hot path: logits -> top-k -> global slot ids, one stream, no host sync."""
+    logits, row_len, row_req = paged_mqa_logits(q_fp8, weights, kv_cache, block_table,
+                                                context_lens, width)
+    idx = topk_rows(logits, row_len, k)
+    slots = topk_to_global_slots(idx, row_req, block_table)
+    return logits, idx, slots

@@ -1,0 +1,225 @@
+// K-cache write, query producer, paged->contiguous gather and slot-id map.
+//
+// All four are bandwidth/latency-bound byte movers with a little fp32 math;
+// none is a contraction, so they use no MFMA: 16-byte vector loads and stores
+// laid out so consecutive lanes touch consecutive bytes.
+#include "sai_device.h"
+
+using namespace sai;
+
+extern "C" const char* sai_status_string(int status) {
+  switch (status) {
+    case SAI_OK: return "SAI_OK";
+    case SAI_EINVAL: return "SAI_EINVAL: invalid argument";
+    case SAI_EUNSUPPORTED: return "SAI_EUNSUPPORTED: unsupported shape";
+    case SAI_EWORKSPACE: return "SAI_EWORKSPACE: workspace missing or too small";
+    case SAI_ELAUNCH: return "SAI_ELAUNCH: kernel launch failed";
+    default: return "SAI: unknown status";
+  }
+}
+
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static inline int launch_status() {
+  return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
+}
+
+// ---------------------------------------------------------------- K1
+// 16 lanes per token row: lane i of the group holds values [8i, 8i+8).
+// One 256-thread workgroup writes 16 tokens.
+__global__ __launch_bounds__(256) void k_cache_write_kernel(
+    const uint16_t* __restrict__ k, int64_t row_stride, const int64_t* __restrict__ slots,
+    int64_t n, uint8_t* __restrict__ cache, int64_t num_blocks) {
+  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
+  const int sub = threadIdx.x & 15;
+  const bool live = tok < n;
+  uint4 raw = make_uint4(0, 0, 0, 0);
+  int64_t slot = -1;
+  if (live) {
+    raw = *reinterpret_cast<const uint4*>(k + tok * row_stride + sub * 8);
+    slot = slots[tok];
+  }
+  float x[8];
+  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+#pragma unroll
+  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  const float scale = fp8_scale(amax);
+  uint32_t lo = 0, hi = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(x[i] / scale) << (8 * i);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(x[4 + i] / scale) << (8 * i);
+  if (!live || slot < 0 || slot >= num_blocks * kBlock) return;
+  uint8_t* blk = cache + (slot / kBlock) * kBlockBytes;
+  const int off = (int)(slot % kBlock);
+  *reinterpret_cast<uint2*>(blk + off * kDim + sub * 8) = make_uint2(lo, hi);
+  if (sub == 0) *reinterpret_cast<float*>(blk + kValueBytes + 4 * off) = scale;
+}
+
+extern "C" int indexer_k_cache_write(const void* k_bf16, int64_t k_row_stride,
+                                     const int64_t* slot_mapping, int64_t n, void* kv_cache,
+                                     int64_t num_blocks, hipStream_t stream) {
+  if (n < 0 || num_blocks < 0) return SAI_EINVAL;
+  if (n == 0) return SAI_OK;
+  if (k_row_stride < kDim || (k_row_stride & 7)) return SAI_EINVAL;
+  if (!k_bf16 || !slot_mapping || !kv_cache || !aligned16(k_bf16) || !aligned16(kv_cache))
+    return SAI_EINVAL;
+  const int64_t grid = (n + 15) / 16;
+  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  hipLaunchKernelGGL(k_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n,
+                     (uint8_t*)kv_cache, num_blocks);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- q producer
+// One 256-thread workgroup per query token (64 heads x 128 = 8192 values):
+// thread t owns values [32t, 32t+32) as four 16-byte loads.
+__global__ __launch_bounds__(256) void q_quant_kernel(
+    const uint16_t* __restrict__ q, const float* __restrict__ wts, uint8_t* __restrict__ q8,
+    float* __restrict__ w_eff, float* __restrict__ q_scale) {
+  __shared__ float s_amax[4];
+  const int64_t row = blockIdx.x;
+  const int t = threadIdx.x;
+  const uint16_t* src = q + row * (kHeads * kDim) + t * 32;
+  float x[32];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) {
+    uint4 raw = *reinterpret_cast<const uint4*>(src + v * 8);
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[v * 8 + 2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      x[v * 8 + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  amax = wave_max(amax);
+  if ((t & 63) == 0) s_amax[t >> 6] = amax;
+  __syncthreads();
+  amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
+  const float scale = fp8_scale(amax);
+  uint32_t packed[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    uint32_t p = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) p |= f32_to_e4m3fn(x[4 * i + j] / scale) << (8 * j);
+    packed[i] = p;
+  }
+  uint8_t* dst = q8 + row * (kHeads * kDim) + t * 32;
+  *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+  *reinterpret_cast<uint4*>(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+  if (t < kHeads) w_eff[row * kHeads + t] = wts[row * kHeads + t] * scale;
+  if (t == 0 && q_scale) q_scale[row] = scale;
+}
+
+extern "C" int indexer_q_quant(const void* q_bf16, const float* weights, int64_t rows,
+                               void* q_fp8, float* w_eff, float* q_scale, hipStream_t stream) {
+  if (rows < 0) return SAI_EINVAL;
+  if (rows == 0) return SAI_OK;
+  if (!q_bf16 || !weights || !q_fp8 || !w_eff || !aligned16(q_bf16) || !aligned16(q_fp8))
+    return SAI_EINVAL;
+  if (rows > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  hipLaunchKernelGGL(q_quant_kernel, dim3((unsigned)rows), dim3(256), 0, stream,
+                     (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- gather
+// 8 lanes per destination token (16 bytes each); 32 tokens per workgroup.
+// The owning request of a destination row is found by binary search of
+// cu_seq_lens, so the launch needs only host sizes.
+__global__ __launch_bounds__(256) void gather_kernel(
+    const uint8_t* __restrict__ cache, int64_t num_blocks, const int32_t* __restrict__ bt,
+    int64_t bt_stride, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
+    uint8_t* __restrict__ out_k, float* __restrict__ out_s) {
+  const int64_t row = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
+  if (row >= total) return;
+  if (row < cu[0] || row >= cu[batch]) return;
+  int lo = 0, hi = batch;  // largest b with cu[b] <= row
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (cu[mid] <= row) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int64_t t = row - cu[b];
+  const int64_t c = t / kBlock;
+  if (c >= bt_stride) return;
+  const int32_t blk = bt[(int64_t)b * bt_stride + c];
+  const int off = (int)(t % kBlock);
+  uint4 v = make_uint4(0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu, 0x7F7F7F7Fu);
+  float s = __uint_as_float(0x7FC00000u);
+  if (blk >= 0 && blk < num_blocks) {
+    const uint8_t* src = cache + (int64_t)blk * kBlockBytes;
+    v = *reinterpret_cast<const uint4*>(src + off * kDim + sub * 16);
+    if (sub == 0) s = *reinterpret_cast<const float*>(src + kValueBytes + 4 * off);
+  }
+  *reinterpret_cast<uint4*>(out_k + row * kDim + sub * 16) = v;
+  if (sub == 0) out_s[row] = s;
+}
+
+extern "C" int gather_indexer_k(const void* kv_cache, int64_t num_blocks, const int32_t* block_table,
+                                int64_t bt_stride, const int32_t* cu_seq_lens, int32_t batch,
+                                int64_t total_tokens, void* out_k_fp8, float* out_scale,
+                                hipStream_t stream) {
+  if (batch < 0 || total_tokens < 0 || num_blocks < 0 || bt_stride < 0) return SAI_EINVAL;
+  if (batch == 0 || total_tokens == 0) return SAI_OK;
+  if (!kv_cache || !block_table || !cu_seq_lens || !out_k_fp8 || !out_scale) return SAI_EINVAL;
+  if (!aligned16(kv_cache) || !aligned16(out_k_fp8)) return SAI_EINVAL;
+  const int64_t grid = (total_tokens + 31) / 32;
+  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+                     (const uint8_t*)kv_cache, num_blocks, block_table, bt_stride, cu_seq_lens,
+                     batch, total_tokens, (uint8_t*)out_k_fp8, out_scale);
+  return launch_status();
+}
+
+// ---------------------------------------------------------------- slot ids
+// One thread per output element; a workgroup covers 256 consecutive entries
+// of the flattened [rows, k] array.
+__global__ __launch_bounds__(256) void slots_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_req,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int32_t batch, int64_t total, int32_t k,
+    int32_t* __restrict__ out) {
+  const int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (e >= total) return;
+  const int64_t r = e / k;
+  const int32_t i = idx[e];
+  int32_t slot = -1;
+  if (i >= 0) {
+    const int32_t b = row_req[r];
+    const int64_t c = i / kBlock;
+    if (b >= 0 && b < batch && c < bt_stride) {
+      const int32_t blk = bt[(int64_t)b * bt_stride + c];
+      if (blk >= 0) slot = blk * kBlock + (i % kBlock);
+    }
+  }
+  out[e] = slot;
+}
+
+extern "C" int topk_to_global_slots(const int32_t* topk_idx, const int32_t* row_req,
+                                    const int32_t* block_table, int64_t bt_stride, int32_t batch,
+                                    int32_t rows, int32_t k, int32_t* out_slots,
+                                    hipStream_t stream) {
+  if (rows < 0 || k < 0 || batch < 0 || bt_stride < 0) return SAI_EINVAL;
+  if (rows == 0 || k == 0) return SAI_OK;
+  if (!topk_idx || !row_req || !block_table || !out_slots) return SAI_EINVAL;
+  const int64_t total = (int64_t)rows * k;
+  const int64_t grid = (total + 255) / 256;
+  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  hipLaunchKernelGGL(slots_kernel, dim3((unsigned)grid), dim3(256), 0, stream, topk_idx, row_req,
+                     block_table, bt_stride, batch, total, k, out_slots);
+  return launch_status();
+}

@@ -1,0 +1,490 @@
+// Indexer logits on gfx950: fp8 MFMA contraction + fused ReLU / head-weight /
+// scale epilogue.
+//
+// Score (the DeepSeek-V3.2 lightning indexer; vLLM PR #36250 names the op
+// fp8_paged_mqa_logits):
+//   L[r, s] = k_scale[s] * sum_h w[r, h] * max(q[r, h, :] . k[s, :], 0)
+//
+// Mapping onto v_mfma_f32_16x16x128_f8f6f4 (fp8 e4m3 x fp8 e4m3 -> fp32):
+//   A (16 x 128) = 16 heads of one query row, B (128 x 16) = 16 keys,
+//   so one MFMA gives 16 heads x 16 keys of dot products, and a 64-key cache
+//   block of one row takes 4 head groups x 4 key tiles = 16 MFMAs.
+// Operand layout: lane l = 16*g + n holds row/column n and 32 bytes of the
+// 128-long contraction.  The contraction order only has to agree between A
+// and B, so lane (g, n) takes bytes [16g, 16g+16) and [64+16g, 64+16g+16) of
+// its head or key row: each dwordx4 load instruction then reads a contiguous
+// 64-byte half of every key row it touches, straight from HBM into VGPRs in
+// operand order (no LDS round trip; each K byte is used by one wave only).
+// Accumulator layout: lane (g, n), register i = head 4g + i of the group, key n.
+// Epilogue: each lane folds its 16 heads of one key (4 groups x 4 registers)
+// with fp32 max + fma; two cross-lane swaps (v_permlane32_swap,
+// v_permlane16_swap) then sum the four lanes that share a key and at the same
+// time scatter the 4 key tiles so that lane l ends with key l of the block:
+// one coalesced 256-byte store per row.
+#include <algorithm>
+
+#include "sai_device.h"
+
+using namespace sai;
+
+namespace {
+
+__device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+
+static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// Key tile t of a 64-key block covers keys tile_key(t) .. tile_key(t)+15.
+// After the reduce-scatter, tiles 0,2,1,3 land in lanes 0-15, 16-31, 32-47,
+// 48-63; with this assignment lane l holds key l.
+__device__ __forceinline__ int tile_key(int t) { return ((t & 1) << 5) | ((t & 2) << 3); }
+
+// The per-lane share of one 64-key block: 4 key tiles x 32 operand bytes,
+// plus the scale of key `lane`.
+struct KFrag {
+  uint4 v[8];
+  float s;
+};
+
+__device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
+  v8i r;
+  r[0] = a.x; r[1] = a.y; r[2] = a.z; r[3] = a.w;
+  r[4] = b.x; r[5] = b.y; r[6] = b.z; r[7] = b.w;
+  return r;
+}
+
+// Paged block: values at `blk`, scales at blk + 8192.
+__device__ __forceinline__ void load_kfrag_paged(KFrag& f, const uint8_t* __restrict__ blk) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint8_t* row = blk + (tile_key(t) + n) * kDim + 16 * g;
+    f.v[2 * t] = *reinterpret_cast<const uint4*>(row);
+    f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(row + 64);
+  }
+  f.s = *reinterpret_cast<const float*>(blk + kValueBytes + 4 * lane);
+}
+
+// Contiguous K: keys [key0, key0+64) of `k` ([*,128] codes) and `ks`; keys at
+// or past `nvalid` (relative to key0) are not read and contribute zeros.
+__device__ __forceinline__ void load_kfrag_contig(KFrag& f, const uint8_t* __restrict__ k,
+                                                  const float* __restrict__ ks, int64_t key0,
+                                                  int nvalid) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int key = tile_key(t) + n;
+    if (key < nvalid) {
+      const uint8_t* row = k + (key0 + key) * kDim + 16 * g;
+      f.v[2 * t] = *reinterpret_cast<const uint4*>(row);
+      f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(row + 64);
+    } else {
+      f.v[2 * t] = make_uint4(0, 0, 0, 0);
+      f.v[2 * t + 1] = make_uint4(0, 0, 0, 0);
+    }
+  }
+  f.s = lane < nvalid ? ks[key0 + lane] : 0.0f;
+}
+
+__device__ __forceinline__ void zero_kfrag(KFrag& f) {
+#pragma unroll
+  for (int i = 0; i < 8; ++i) f.v[i] = make_uint4(0, 0, 0, 0);
+  f.s = 0.0f;
+}
+
+// A operands of one query row ([64 heads][128] codes): head group hg holds
+// heads 16hg .. 16hg+15.
+__device__ __forceinline__ void load_qfrag(v8i (&qa)[4], const uint8_t* __restrict__ qrow) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) {
+    const uint8_t* p = qrow + (16 * hg + n) * kDim + 16 * g;
+    qa[hg] = make_v8i(*reinterpret_cast<const uint4*>(p), *reinterpret_cast<const uint4*>(p + 64));
+  }
+}
+
+// Head weights matching the accumulator layout: lane (g, n) needs heads
+// 16hg + 4g + i, i = 0..3.
+__device__ __forceinline__ void load_wfrag(float4 (&wv)[4], const float* __restrict__ wrow) {
+  const int g = (threadIdx.x & 63) >> 4;
+#pragma unroll
+  for (int hg = 0; hg < 4; ++hg) wv[hg] = *reinterpret_cast<const float4*>(wrow + 16 * hg + 4 * g);
+}
+
+__device__ __forceinline__ float relu_dot4(const float4 w, const v4f c, float acc) {
+  acc = fmaf(w.x, fmaxf(c[0], 0.0f), acc);
+  acc = fmaf(w.y, fmaxf(c[1], 0.0f), acc);
+  acc = fmaf(w.z, fmaxf(c[2], 0.0f), acc);
+  acc = fmaf(w.w, fmaxf(c[3], 0.0f), acc);
+  return acc;
+}
+
+// Sum the four lanes {n, n+16, n+32, n+48} of each of the 4 key tiles and
+// scatter: lanes 16p + n receive tile [0, 2, 1, 3][p], column n.
+__device__ __forceinline__ float reduce_scatter4(float p0, float p1, float p2, float p3) {
+  auto a = __builtin_amdgcn_permlane32_swap(__float_as_uint(p0), __float_as_uint(p1), false, false);
+  auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(p2), __float_as_uint(p3), false, false);
+  const float x01 = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const float x23 = __uint_as_float(b[0]) + __uint_as_float(b[1]);
+  auto c = __builtin_amdgcn_permlane16_swap(__float_as_uint(x01), __float_as_uint(x23), false, false);
+  return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
+// Unscaled head-reduced scores of one 64-key block for one query row; lane l
+// returns key l.
+__device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], const float4 (&wv)[4]) {
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float p[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const v8i b = make_v8i(kf.v[2 * t], kf.v[2 * t + 1]);
+    float acc = 0.0f;
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) {
+      const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[hg], b, zero, 0, 0, 0, 0, 0, 0);
+      acc = relu_dot4(wv[hg], c, acc);
+    }
+    p[t] = acc;
+  }
+  return reduce_scatter4(p[0], p[1], p[2], p[3]);
+}
+
+__device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
+
+// ------------------------------------------------------------------ decode
+// Work: unit (b, c) = key block c of request b, for all next_n rows of b.
+// Units are flattened in (b, c) order and split evenly over every wave of the
+// grid (the split needs only device-side context lengths: no host sync); a
+// wave also takes an even share of the -inf fill of column blocks past each
+// request's last key block.  Workgroup g runs on XCD g % 8; logical
+// workgroup (g % 8) * (G / 8) + g / 8 makes each XCD take one contiguous
+// range of units, so a request's query rows are fetched into one L2.
+template <int NN>
+__global__ __launch_bounds__(256) void paged_logits_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ cache,
+    int64_t num_blocks, const int32_t* __restrict__ bt, int64_t bt_stride,
+    const int32_t* __restrict__ ctx_lens, int32_t batch, float* __restrict__ logits,
+    int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out) {
+  extern __shared__ int smem[];
+  int* s_unit = smem;                   // [batch+1] prefix of key blocks
+  int* s_fill = smem + (batch + 1);     // [batch+1] prefix of fill column blocks
+  int* s_ctx = smem + 2 * (batch + 1);  // [batch] clamped context
+  int* scratch = smem + 3 * (batch + 1);
+
+  const int lane = threadIdx.x & 63;
+  const int maxc = (int)min64(stride, bt_stride * kBlock);
+  const int wblocks = (int)((stride + kBlock - 1) / kBlock);
+
+  int run_u = 0, run_f = 0;
+  for (int base = 0; base < batch; base += 256) {
+    const int b = base + threadIdx.x;
+    int nu = 0, nf = 0;
+    if (b < batch) {
+      const int c = min(max(ctx_lens[b], 0), maxc);
+      s_ctx[b] = c;
+      nu = cdiv_i(c, kBlock);
+      nf = wblocks - nu;
+    }
+    int tu, tf;
+    const int eu = block_exclusive_scan<256>(nu, scratch, &tu);
+    const int ef = block_exclusive_scan<256>(nf, scratch, &tf);
+    if (b < batch) {
+      s_unit[b] = run_u + eu;
+      s_fill[b] = run_f + ef;
+    }
+    run_u += tu;
+    run_f += tf;
+  }
+  if (threadIdx.x == 0) {
+    s_unit[batch] = run_u;
+    s_fill[batch] = run_f;
+  }
+  __syncthreads();
+
+  const int G = gridDim.x;
+  const int lg = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int wv = __builtin_amdgcn_readfirstlane(lg * 4 + (threadIdx.x >> 6));
+  const int nwv = G * 4;
+
+  // row metadata
+  const int rows = batch * NN;
+  for (int r = wv * 64 + lane; r < rows; r += nwv * 64) {
+    const int b = r / NN, j = r - b * NN;
+    if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
+    if (row_req_out) row_req_out[r] = b;
+  }
+
+  const int U = s_unit[batch];
+  int u = (int)((int64_t)U * wv / nwv);
+  const int u1 = (int)((int64_t)U * (wv + 1) / nwv);
+  if (u < u1) {
+    // request of unit u: the last b with s_unit[b] <= u
+    int lo = 0, hi = batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_unit[mid] <= u) lo = mid; else hi = mid;
+    }
+    int ub = lo;
+    int qb = -1;
+    v8i qa[NN][4];
+    float4 wf[NN][4];
+    KFrag fa, fb;
+
+    auto block_of = [&](int unit, int b, bool& ok) -> const uint8_t* {
+      const int c = unit - s_unit[b];
+      const int32_t blk = bt[(int64_t)b * bt_stride + c];
+      ok = blk >= 0 && blk < num_blocks;
+      return cache + (int64_t)(ok ? blk : 0) * kBlockBytes;
+    };
+    bool ok_a, ok_b;
+    {
+      const uint8_t* p = block_of(u, ub, ok_a);
+      if (ok_a) load_kfrag_paged(fa, p); else zero_kfrag(fa);
+    }
+
+    auto step = [&](KFrag& cur, bool& ok_cur, KFrag& nxt, bool& ok_nxt) -> bool {
+      const int un = u + 1;
+      int bn = ub;
+      if (un < u1) {
+        while (s_unit[bn + 1] <= un) ++bn;
+        const uint8_t* p = block_of(un, bn, ok_nxt);
+        if (ok_nxt) load_kfrag_paged(nxt, p); else zero_kfrag(nxt);
+      }
+      if (ub != qb) {
+        qb = ub;
+#pragma unroll
+        for (int j = 0; j < NN; ++j) {
+          load_qfrag(qa[j], q + ((int64_t)qb * NN + j) * (kHeads * kDim));
+          load_wfrag(wf[j], wts + ((int64_t)qb * NN + j) * kHeads);
+        }
+      }
+      const int c = u - s_unit[ub];
+      const int col = c * kBlock + lane;
+      const int ctx = s_ctx[ub];
+#pragma unroll
+      for (int j = 0; j < NN; ++j) {
+        const float sc = score_row(cur, qa[j], wf[j]);
+        const int limit = ctx - NN + j + 1;
+        float v = ok_cur ? sc * cur.s : __uint_as_float(0x7FC00000u);
+        v = col < limit ? v : -INFINITY;
+        if (col < stride) logits[((int64_t)ub * NN + j) * stride + col] = v;
+      }
+      if (un >= u1) return false;
+      u = un;
+      ub = bn;
+      return true;
+    };
+    while (step(fa, ok_a, fb, ok_b) && step(fb, ok_b, fa, ok_a)) {
+    }
+  }
+
+  // -inf fill of the column blocks past each request's last key block
+  const int F = s_fill[batch];
+  int f = (int)((int64_t)F * wv / nwv);
+  const int f1 = (int)((int64_t)F * (wv + 1) / nwv);
+  if (f < f1) {
+    int lo = 0, hi = batch;
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (s_fill[mid] <= f) lo = mid; else hi = mid;
+    }
+    int b = lo;
+    for (; f < f1; ++f) {
+      while (s_fill[b + 1] <= f) ++b;
+      const int cb = (s_unit[b + 1] - s_unit[b]) + (f - s_fill[b]);
+      const int col = cb * kBlock + lane;
+      if (col < stride) {
+#pragma unroll
+        for (int j = 0; j < NN; ++j) logits[((int64_t)b * NN + j) * stride + col] = -INFINITY;
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------ prefill
+// Workgroup = (query tile of 16 consecutive tokens of one request, key chunk
+// of kChunk columns).  Its 4 waves take 4 rows each, hold their Q operands in
+// VGPRs and stream the chunk's K blocks (the 4 waves read the same blocks,
+// so 3 of 4 reads hit the CU's L1); every column of the chunk is written for
+// the tile's rows (-inf past each row's causal limit).  Grid ids are ordered
+// tile-major and remapped so that the chunks of one tile run on one XCD and
+// share its Q in that XCD's L2.
+constexpr int kRowsPerWave = 4;
+constexpr int kTileRows = 16;
+constexpr int kChunk = 1024;
+
+__global__ __launch_bounds__(256) void prefill_logits_kernel(
+    const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ k,
+    const float* __restrict__ ks, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
+    float* __restrict__ logits, int64_t stride, int32_t* __restrict__ row_len_out,
+    int32_t* __restrict__ row_req_out, int32_t nchunks, int32_t ntiles_max) {
+  extern __shared__ int smem[];
+  int* s_tile = smem;                  // [batch+1] prefix of query tiles
+  int* scratch = smem + (batch + 1);
+  __shared__ float4 s_w[kTileRows][16];
+
+  int run = 0;
+  for (int base = 0; base < batch; base += 256) {
+    const int b = base + threadIdx.x;
+    int nt = 0;
+    if (b < batch) {
+      const int len = max(cu[b + 1] - cu[b], 0);
+      nt = cdiv_i(len, kTileRows);
+    }
+    int tot;
+    const int e = block_exclusive_scan<256>(nt, scratch, &tot);
+    if (b < batch) s_tile[b] = run + e;
+    run += tot;
+  }
+  if (threadIdx.x == 0) s_tile[batch] = run;
+  __syncthreads();
+
+  const int G = gridDim.x;
+  const int lg = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
+  const int tile = lg / nchunks, chunk = lg - tile * nchunks;
+  if (tile >= s_tile[batch] || tile >= ntiles_max) return;
+  int lo = 0, hi = batch;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (s_tile[mid] <= tile) lo = mid; else hi = mid;
+  }
+  const int b = lo;
+  const int64_t base_tok = cu[b];
+  const int len = (int)min64(max(cu[b + 1] - cu[b], 0), stride);
+  const int i0 = (tile - s_tile[b]) * kTileRows;
+
+  // head weights of the tile's rows, in LDS
+  {
+    const int r = threadIdx.x >> 4, h4 = threadIdx.x & 15;
+    float4 w = make_float4(0, 0, 0, 0);
+    if (i0 + r < len) w = *reinterpret_cast<const float4*>(wts + (base_tok + i0 + r) * kHeads + 4 * h4);
+    s_w[r][h4] = w;
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int ir0 = i0 + wave * kRowsPerWave;  // first request-local row of this wave
+  const int nrows = max(0, min(kRowsPerWave, len - ir0));
+  if (nrows == 0) return;
+
+  if (chunk == 0 && lane < nrows) {
+    if (row_len_out) row_len_out[base_tok + ir0 + lane] = ir0 + lane + 1;
+    if (row_req_out) row_req_out[base_tok + ir0 + lane] = b;
+  }
+
+  const int col0 = chunk * kChunk;
+  const int col_end = (int)min64((int64_t)col0 + kChunk, stride);
+  const int maxlim = ir0 + nrows;  // keys visible to the wave's last row
+  const int kend = min(col_end, maxlim);
+  const int nblk = kend > col0 ? cdiv_i(kend - col0, kBlock) : 0;
+
+  v8i qa[kRowsPerWave][4];
+#pragma unroll
+  for (int r = 0; r < kRowsPerWave; ++r) {
+    if (r < nrows && nblk > 0) {
+      load_qfrag(qa[r], q + (base_tok + ir0 + r) * (kHeads * kDim));
+    } else {
+#pragma unroll
+      for (int hg = 0; hg < 4; ++hg) qa[r][hg] = v8i{0, 0, 0, 0, 0, 0, 0, 0};
+    }
+  }
+
+  KFrag fa, fb;
+  int c = 0;
+  if (nblk > 0) load_kfrag_contig(fa, k, ks, base_tok + col0, len - col0);
+  auto step = [&](KFrag& cur, KFrag& nxt) -> bool {
+    const int key0 = col0 + c * kBlock;
+    if (c + 1 < nblk) load_kfrag_contig(nxt, k, ks, base_tok + key0 + kBlock, len - key0 - kBlock);
+    const int col = key0 + lane;
+#pragma unroll
+    for (int r = 0; r < kRowsPerWave; ++r) {
+      if (r < nrows) {
+        const int wr = wave * kRowsPerWave + r;
+        const float4 wf[4] = {s_w[wr][4 * 0 + (lane >> 4)], s_w[wr][4 * 1 + (lane >> 4)],
+                              s_w[wr][4 * 2 + (lane >> 4)], s_w[wr][4 * 3 + (lane >> 4)]};
+        const float sc = score_row(cur, qa[r], wf);
+        const int limit = ir0 + r + 1;
+        const float v = col < limit ? sc * cur.s : -INFINITY;
+        if (col < col_end) logits[(base_tok + ir0 + r) * stride + col] = v;
+      }
+    }
+    ++c;
+    return c < nblk;
+  };
+  if (nblk > 0) {
+    while (step(fa, fb) && step(fb, fa)) {
+    }
+  }
+  // -inf for the chunk's columns past the computed blocks
+  for (int col = col0 + nblk * kBlock + lane; col < col_end; col += 64) {
+    for (int r = 0; r < nrows; ++r) logits[(base_tok + ir0 + r) * stride + col] = -INFINITY;
+  }
+}
+
+template <int NN>
+int launch_paged(const void* q, const float* w, const void* cache, int64_t num_blocks,
+                 const int32_t* bt, int64_t bt_stride, const int32_t* ctx, int32_t batch,
+                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, hipStream_t s,
+                 int target_waves) {
+  const int64_t wblocks = (stride + kBlock - 1) / kBlock;
+  const int64_t units_max = (int64_t)batch * wblocks;
+  int64_t waves = std::min<int64_t>(target_waves, std::max<int64_t>(units_max, 1));
+  int64_t G = (waves + 3) / 4;
+  G = (G + 7) / 8 * 8;
+  const size_t lds = (size_t)(3 * (batch + 1) + 8) * sizeof(int);
+  hipLaunchKernelGGL(paged_logits_kernel<NN>, dim3((unsigned)G), dim3(256), lds, s,
+                     (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt, bt_stride, ctx,
+                     batch, logits, stride, rl, rr);
+  return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
+}
+
+}  // namespace
+
+// Waves the decode kernel spreads its units over (8 per CU on 256 CUs).
+static int g_decode_waves = 2048;
+
+extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
+                                int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                                const int32_t* context_lens, int32_t batch, int32_t next_n,
+                                float* logits, int64_t logits_stride, int32_t* row_len_out,
+                                int32_t* row_req_out, hipStream_t stream) {
+  if (batch < 0 || num_blocks < 0 || bt_stride < 0 || logits_stride < 0) return SAI_EINVAL;
+  if (next_n < 1 || next_n > SAI_NEXT_N_MAX) return SAI_EUNSUPPORTED;
+  if (batch == 0) return SAI_OK;
+  if (!q_fp8 || !weights || !kv_cache || !block_table || !context_lens || !logits) return SAI_EINVAL;
+  if (!aligned16(q_fp8) || !aligned16(weights) || !aligned16(kv_cache)) return SAI_EINVAL;
+  if (logits_stride == 0) return SAI_EINVAL;
+  if (batch > 4096) return SAI_EUNSUPPORTED;
+  const int64_t wblocks = (logits_stride + kBlock - 1) / kBlock;
+  if ((int64_t)batch * wblocks > 0x7FFFFFFF / 2 || logits_stride > 0x7FFFFFFF - kBlock)
+    return SAI_EUNSUPPORTED;
+  switch (next_n) {
+    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
+    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
+    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
+    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
+  }
+}
+
+extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
+                          const float* k_scale, const int32_t* cu_seq_lens, int32_t batch,
+                          int64_t total_tokens, float* logits, int64_t logits_stride,
+                          int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
+  if (batch < 0 || total_tokens < 0 || logits_stride < 0) return SAI_EINVAL;
+  if (batch == 0 || total_tokens == 0) return SAI_OK;
+  if (!q_fp8 || !weights || !k_fp8 || !k_scale || !cu_seq_lens || !logits || logits_stride == 0)
+    return SAI_EINVAL;
+  if (!aligned16(q_fp8) || !aligned16(weights) || !aligned16(k_fp8)) return SAI_EINVAL;
+  if (batch > 4096 || logits_stride > 0x7FFFFFFF - kChunk) return SAI_EUNSUPPORTED;
+  const int64_t nchunks = (logits_stride + kChunk - 1) / kChunk;
+  const int64_t ntiles = (total_tokens + kTileRows - 1) / kTileRows + batch;
+  int64_t G = nchunks * ntiles;
+  G = (G + 7) / 8 * 8;
+  if (G > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  const size_t lds = (size_t)((batch + 1) + 8) * sizeof(int);
+  hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)G), dim3(256), lds, stream,
+                     (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_seq_lens,
+                     batch, total_tokens, logits, logits_stride, row_len_out, row_req_out,
+                     (int32_t)nchunks, (int32_t)ntiles);
+  return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
+}

@@ -1,0 +1,98 @@
+// Device-side building blocks shared by the gfx950 indexer kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "sai.h"
+
+namespace sai {
+
+constexpr int kHeads = SAI_HEADS;          // 64
+constexpr int kDim = SAI_HEAD_DIM;         // 128
+constexpr int kBlock = SAI_BLOCK_SIZE;     // 64 tokens
+constexpr int kValueBytes = kBlock * kDim; // 8192
+constexpr int kBlockBytes = SAI_BLOCK_BYTES;
+constexpr int kWave = 64;
+
+typedef int v8i __attribute__((ext_vector_type(8)));
+typedef float v4f __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------- fp8
+// float32 -> fp8 e4m3fn, round to nearest even, saturating at +-448, sign
+// kept (so -0.0 -> 0x80).  Normal range: round the float32 mantissa to 3 bits
+// on the bit pattern and rebias the exponent (127 -> 7); subnormal range
+// (|y| < 2^-6): the code is the integer round(|y| * 2^9) in 0..8, where 8 is
+// the smallest normal 2^-6.  Input must not be NaN.
+__device__ __forceinline__ uint32_t f32_to_e4m3fn(float y) {
+  const uint32_t sign = (__float_as_uint(y) >> 24) & 0x80u;
+  const float a = fminf(fabsf(y), 448.0f);
+  uint32_t mag;
+  if (a >= 0.015625f) {
+    const uint32_t u = __float_as_uint(a);
+    const uint32_t r = u + 0x7FFFFu + ((u >> 20) & 1u);
+    mag = (r >> 20) - (120u << 3);
+  } else {
+    mag = (uint32_t)rintf(a * 512.0f);
+  }
+  return sign | mag;
+}
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// quantiser scale: max(amax * fl32(1/448), FLT_MIN), float32
+__device__ __forceinline__ float fp8_scale(float amax) {
+  return fmaxf(amax * (1.0f / 448.0f), 1.17549435e-38f);
+}
+
+// Order-preserving float -> uint32 key (larger float, larger key).  -0.0 is
+// folded onto +0.0 so the two tie.
+__device__ __forceinline__ uint32_t f32_order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// ---------------------------------------------------------------- wave ops
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+__device__ __forceinline__ int wave_inclusive_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o, 64);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Exclusive scan over a whole workgroup of NT threads (NT multiple of 64,
+// at most 64 waves).  `scratch` holds NT/64 + 1 ints of LDS.  Returns the
+// exclusive prefix of `v`; *total receives the workgroup sum.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* total) {
+  constexpr int NW = NT / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  int inc = wave_inclusive_scan(v);
+  if (lane == 63) scratch[w] = inc;
+  __syncthreads();
+  if (w == 0) {
+    int s = lane < NW ? scratch[lane] : 0;
+    int si = wave_inclusive_scan(s);
+    if (lane < NW) scratch[lane] = si - s;
+    if (lane == NW - 1) scratch[NW] = si;
+  }
+  __syncthreads();
+  int res = scratch[w] + inc - v;
+  *total = scratch[NW];
+  __syncthreads();
+  return res;
+}
+
+}  // namespace sai

@@ -1,0 +1,80 @@
+"""The C-ABI library loads, exports every symbol include/sai.h declares, and its
+host-side validation rejects bad arguments without touching a GPU."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+from sparse_attention_indexer_paged_amd import binding
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sai.h")
+
+SAI_OK, SAI_EINVAL, SAI_EUNSUPPORTED = 0, -1, -2
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.fail("libsai.so is not built (run __graft_entry__.build())")
+    return binding.load()
+
+
+def test_header_declares_the_boundary():
+    names = declared_functions()
+    assert names == sorted([
+        "sai_status_string", "indexer_k_cache_write", "indexer_q_quant", "gather_indexer_k",
+        "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
+        "topk_to_global_slots"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", binding.LIB_PATH],
+                         capture_output=True, text=True, check=True).stdout
+    exported = {ln.split()[-1] for ln in out.splitlines() if " T " in ln}
+    for name in declared_functions():
+        assert name in exported, name
+        assert getattr(lib, name) is not None
+    assert set(binding.SIGNATURES) == set(declared_functions())
+
+
+def test_status_strings(lib):
+    for code in (0, -1, -2, -3, -4, 7):
+        assert binding.status_string(code).startswith("SAI")
+
+
+def test_validation_needs_no_gpu(lib):
+    nul = ctypes.c_void_p(0)
+    fake = ctypes.c_void_p(4096)        # never dereferenced: validation fails first
+    # null pointers with a non-empty problem
+    assert lib.paged_mqa_logits(nul, nul, nul, 10, nul, 4, nul, 2, 1, nul, 256, nul, nul, nul) == SAI_EINVAL
+    # next_n outside 1..4, k outside 1..2048
+    assert lib.paged_mqa_logits(fake, fake, fake, 10, fake, 4, fake, 2, 5, fake, 256, nul, nul, nul) == SAI_EUNSUPPORTED
+    assert lib.paged_mqa_logits(fake, fake, fake, 10, fake, 4, fake, 2, 0, fake, 256, nul, nul, nul) == SAI_EUNSUPPORTED
+    assert lib.topk_rows(fake, 256, fake, 3, 0, fake, nul, 0, nul) == SAI_EUNSUPPORTED
+    assert lib.topk_rows(fake, 256, fake, 3, 2049, fake, nul, 0, nul) == SAI_EUNSUPPORTED
+    # negative sizes
+    assert lib.indexer_k_cache_write(fake, 128, fake, -1, fake, 4, nul) == SAI_EINVAL
+    assert lib.indexer_k_cache_write(fake, 100, fake, 3, fake, 4, nul) == SAI_EINVAL   # stride < 128
+    assert lib.gather_indexer_k(fake, 4, fake, 2, fake, -1, 10, fake, fake, nul) == SAI_EINVAL
+    assert lib.mqa_logits(fake, fake, fake, fake, fake, 1, -5, fake, 64, nul, nul, nul) == SAI_EINVAL
+    assert lib.topk_to_global_slots(fake, fake, fake, 4, 1, -1, 8, fake, nul) == SAI_EINVAL
+    assert lib.indexer_q_quant(nul, nul, 3, nul, nul, nul, nul) == SAI_EINVAL
+    # misaligned q
+    assert lib.paged_mqa_logits(ctypes.c_void_p(4097), fake, fake, 10, fake, 4, fake, 2, 1, fake, 256, nul, nul, nul) == SAI_EINVAL
+    # empty problems are no-ops
+    assert lib.paged_mqa_logits(nul, nul, nul, 0, nul, 0, nul, 0, 1, nul, 0, nul, nul, nul) == SAI_OK
+    assert lib.topk_rows(nul, 16, nul, 0, 8, nul, nul, 0, nul) == SAI_OK
+    assert lib.indexer_k_cache_write(nul, 128, nul, 0, nul, 0, nul) == SAI_OK
+
+
+def test_topk_workspace_query(lib):
+    assert binding.topk_workspace_bytes(64, 16384, 2048) >= 0

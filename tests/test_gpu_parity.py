@@ -1,0 +1,277 @@
+"""GPU parity of every entry point against the CPU oracle on small seeded
+inputs that still span several 64-key blocks, ragged tails, poisoned stale
+bytes and every next_n; integer and byte outputs bit-exact, logits within
+1e-4 + 1e-3*|ref|."""
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sparse_attention_indexer_paged_amd import binding as sai
+from sparse_attention_indexer_paged_amd import synth
+
+from gpu_common import DEV, GpuWorkload, OracleWorkload, assert_logits_close, bf16_tensor
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ---------------------------------------------------------------- producers
+def test_k_cache_write_bit_exact_tiny_decode():
+    _say("k_cache_write: tiny decode workload")
+    wl = synth.make(0)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    assert np.array_equal(g.pool.cpu().numpy(), o.pool)
+
+
+def test_k_cache_write_edge_values():
+    _say("k_cache_write: edge values")
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((64, 128)).astype(np.float32)
+    x[0] = 0.0                                  # all zero -> FLT_MIN scale
+    x[1] = -0.0
+    x[2, :] = 3.0                               # constant row
+    x[3] *= 1e30                                # huge
+    x[4] *= 1e-30                               # tiny (normal)
+    x[5, ::2] = 0.0
+    x[6] = np.where(np.arange(128) % 2, 1e-3, -448.0)
+    x[7, 0] = 2.0 ** -133                       # bf16 subnormal next to zeros
+    x[7, 1:] = 0.0
+    x[8] = rng.standard_normal(128) * 1e-38     # subnormal-heavy row
+    bits = synth.f32_to_bf16_bits(x)
+    xf = synth.bf16_bits_to_f32(bits)
+    slots = np.arange(64, dtype=np.int64) * 3 % 190 - 1       # includes -1 (skipped)
+    pool_np = np.full((3, synth.BLOCK_BYTES), 0x5A, np.uint8)
+    ref = O.k_cache_write(xf, slots, pool_np.copy())
+    pool = torch.from_numpy(pool_np).to(DEV)
+    sai.indexer_k_cache_write(bf16_tensor(bits), torch.from_numpy(slots).to(DEV), pool)
+    got = pool.cpu().numpy()
+    if not np.array_equal(got, ref):
+        diff = np.argwhere(got != ref)
+        raise AssertionError(f"{len(diff)} bytes differ, first at {diff[:5].tolist()}")
+
+
+def test_q_quant_bit_exact():
+    _say("q_quant: tiny decode queries + edge rows")
+    wl = synth.make(0)
+    q = synth.bf16_bits_to_f32(wl.q())
+    w = wl.w()
+    q = np.concatenate([q, np.zeros((1, 64, 128), np.float32), q[:1] * 1e-20])
+    w = np.concatenate([w, w[:1], w[:1]])
+    bits = synth.f32_to_bf16_bits(q)
+    qf = synth.bf16_bits_to_f32(bits)
+    codes, weff, qs = O.quantize_q(qf, w)
+    gc, gw, gs = sai.indexer_q_quant(bf16_tensor(bits), torch.from_numpy(w).to(DEV))
+    assert np.array_equal(gc.cpu().numpy(), codes)
+    assert np.array_equal(gs.cpu().numpy().view(np.uint32), qs.view(np.uint32))
+    assert np.array_equal(gw.cpu().numpy().view(np.uint32), weff.view(np.uint32))
+
+
+# ---------------------------------------------------------------- logits
+def _check_decode(wl, requests=None, rows=None):
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl, requests=requests)
+    nn = wl.next_n
+    logits, row_len, row_req = sai.paged_mqa_logits(
+        g.q_fp8.view(wl.batch, nn, 64, 128), g.w_eff, g.pool, g.block_table, g.ctx)
+    torch.cuda.synchronize()
+    lim, req = O.decode_limits(wl.ctx, nn)
+    assert np.array_equal(row_len.cpu().numpy(), lim.clip(min=0))
+    assert np.array_equal(row_req.cpu().numpy(), req)
+    ref = O.paged_mqa_logits(o.q_codes.reshape(wl.batch, nn, 64, 128), o.w_eff, o.pool,
+                             wl.block_table, wl.ctx, nn, wl.width, rows=rows)
+    gl = logits.cpu().numpy()
+    sel = slice(None) if rows is None else np.asarray(rows)
+    worst = assert_logits_close(gl[sel], ref[sel], wl.name)
+    _say(f"{wl.name}: worst err/tol {worst:.3g}")
+    return g, logits, row_len, row_req
+
+
+def test_paged_logits_tiny_decode():
+    _say("paged_mqa_logits: tiny decode (batch 2, ctx 3000/5000)")
+    _check_decode(synth.make(0))
+
+
+@pytest.mark.parametrize("next_n", [1, 2, 3, 4])
+def test_paged_logits_ragged_next_n(next_n):
+    _say(f"paged_mqa_logits: ragged contexts, next_n={next_n}")
+    ctx = [next_n, 63, 64, 65, 127, 129, 700, 1, 64 * 5 + 17][: 9 if next_n == 1 else 8]
+    ctx = [max(c, next_n) for c in ctx]
+    wl = synth.custom(len(ctx), next_n, ctx, num_blocks=64, bt_width=12, seed=100 + next_n)
+    _check_decode(wl)
+
+
+def test_paged_logits_width_not_multiple_of_64_and_empty_request():
+    _say("paged_mqa_logits: stride 1000, an empty request")
+    wl = synth.custom(3, 1, [900, 0, 257], num_blocks=40, bt_width=16, seed=7)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    logits = torch.full((3, 1000), 7.0, device=DEV)
+    logits, row_len, _ = sai.paged_mqa_logits(g.q_fp8.view(3, 1, 64, 128), g.w_eff, g.pool,
+                                              g.block_table, g.ctx, width=1000, logits=logits)
+    ref = O.paged_mqa_logits(o.q_codes.reshape(3, 1, 64, 128), o.w_eff, o.pool, wl.block_table,
+                             wl.ctx, 1, 1000)
+    assert_logits_close(logits.cpu().numpy(), ref, "stride1000")
+    assert row_len.cpu().tolist() == [900, 0, 257]
+
+
+def test_paged_logits_deterministic_and_permutation_invariant():
+    _say("paged_mqa_logits: determinism + block permutation")
+    wl = synth.custom(4, 2, [1000, 333, 64, 2000], num_blocks=80, bt_width=40, seed=9)
+    g = GpuWorkload(wl)
+    args = (g.q_fp8.view(4, 2, 64, 128), g.w_eff)
+    l1, _, _ = sai.paged_mqa_logits(*args, g.pool, g.block_table, g.ctx)
+    l2, _, _ = sai.paged_mqa_logits(*args, g.pool, g.block_table, g.ctx)
+    pi = torch.from_numpy(np.random.default_rng(1).permutation(80)).to(DEV)
+    pool2 = torch.empty_like(g.pool)
+    pool2[pi] = g.pool
+    bt2 = torch.where(g.block_table >= 0, pi[g.block_table.clamp(min=0).long()].int(), g.block_table)
+    l3, _, _ = sai.paged_mqa_logits(*args, pool2, bt2.contiguous(), g.ctx)
+    assert torch.equal(l1, l2)
+    assert torch.equal(l1, l3)
+
+
+# ---------------------------------------------------------------- top-k / slots
+def test_decode_topk_and_slots_bit_exact_tiny():
+    _say("topk_rows + topk_to_global_slots: tiny decode")
+    wl = synth.make(0)
+    g, logits, row_len, row_req = _check_decode(wl)
+    idx = sai.topk_rows(logits, row_len, 2048)
+    slots = sai.topk_to_global_slots(idx, row_req, g.block_table)
+    gl = logits.cpu().numpy()
+    want = O.topk_rows(gl, row_len.cpu().numpy(), 2048)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    want_s = O.topk_to_global_slots(want, row_req.cpu().numpy(), wl.block_table)
+    assert np.array_equal(slots.cpu().numpy(), want_s)
+
+
+def _adversarial_rows():
+    rng = np.random.default_rng(3)
+    W = 9000
+    rows = []
+    rows.append(rng.standard_normal(W))
+    rows.append(np.zeros(W))                                   # all equal
+    r = np.zeros(W); r[::2] = -0.0; rows.append(r)             # +-0 ties
+    rows.append(np.arange(W, dtype=np.float64))                # increasing
+    rows.append(-np.arange(W, dtype=np.float64))               # decreasing
+    rows.append(np.round(rng.standard_normal(W) * 2))          # heavy ties
+    r = rng.standard_normal(W); r[rng.random(W) < 0.3] = -np.inf; rows.append(r)
+    rows.append(np.full(W, -np.inf))                           # all -inf
+    r = rng.standard_normal(W) * 1e-38; rows.append(r)         # subnormals
+    r = np.full(W, 1.0); r[5000:] = 2.0; rows.append(r)        # threshold inside a tie block
+    L = np.stack(rows).astype(np.float32)
+    lens = np.array([W, W, W, W, W, W, W, W, W, W, 2048, 2047, 1, 0, 5000, 8999], np.int32)
+    L = np.concatenate([L, L[:6]])
+    return L, lens
+
+
+@pytest.mark.parametrize("k", [2048, 1, 37, 1000])
+def test_topk_adversarial_rows(k):
+    _say(f"topk_rows: adversarial rows, k={k}")
+    L, lens = _adversarial_rows()
+    got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
+    want = O.topk_rows(L, lens, k)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+def test_topk_unaligned_stride():
+    _say("topk_rows: odd stride")
+    rng = np.random.default_rng(4)
+    L = rng.standard_normal((5, 4099)).astype(np.float32)
+    lens = np.array([4099, 3000, 2049, 4098, 100], np.int32)
+    full = torch.from_numpy(L).to(DEV)
+    got = sai.topk_rows(full, torch.from_numpy(lens).to(DEV), 2048)
+    assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, 2048))
+
+
+def test_slots_edge_cases():
+    _say("topk_to_global_slots: -1, out-of-table, bad request")
+    bt = np.array([[5, 9, -1], [2, 0, 7]], np.int32)
+    idx = np.array([[0, 63, 64, 127, -1, 128, 191, 192],
+                    [0, 1, 64, 130, 191, -1, -1, -1],
+                    [0, 1, 2, 3, 4, 5, 6, 7]], np.int32)
+    req = np.array([0, 1, 5], np.int32)
+    got = sai.topk_to_global_slots(torch.from_numpy(idx).to(DEV), torch.from_numpy(req).to(DEV),
+                                   torch.from_numpy(bt).to(DEV)).cpu().numpy()
+    assert got[0].tolist() == [320, 383, 576, 639, -1, -1, -1, -1]
+    assert got[1].tolist() == [128, 129, 0, 450, 511, -1, -1, -1]
+    assert got[2].tolist() == [-1] * 8
+
+
+# ---------------------------------------------------------------- prefill
+def test_gather_bit_exact():
+    _say("gather_indexer_k: ragged requests incl. empty")
+    wl = synth.custom(4, 0, [130, 0, 64, 301], num_blocks=24, bt_width=5, seed=21)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    total = wl.total_tokens
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, g.cu, total)
+    rv, rs = O.gather_indexer_k(o.pool, wl.block_table, wl.cu_seq_lens, total)
+    assert np.array_equal(kv.cpu().numpy(), rv)
+    assert np.array_equal(ks.cpu().numpy().view(np.uint32), rs.view(np.uint32))
+
+
+def test_prefill_logits_two_requests():
+    _say("gather + mqa_logits: two requests 300 + 77 tokens")
+    wl = synth.custom(2, 0, [300, 77], num_blocks=12, bt_width=5, seed=22)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    total = wl.total_tokens
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, g.cu, total)
+    width = 320
+    logits, row_len, row_req = sai.mqa_logits(g.q_fp8, g.w_eff, kv, ks, g.cu, width)
+    rv, rs = O.gather_indexer_k(o.pool, wl.block_table, wl.cu_seq_lens, total)
+    ref = O.mqa_logits(o.q_codes, o.w_eff, rv, rs, wl.cu_seq_lens, width)
+    assert_logits_close(logits.cpu().numpy(), ref, "prefill")
+    assert row_len.cpu().tolist() == list(range(1, 301)) + list(range(1, 78))
+    assert row_req.cpu().tolist() == [0] * 300 + [1] * 77
+    idx = sai.topk_rows(logits, row_len, 64)
+    assert np.array_equal(idx.cpu().numpy(), O.topk_rows(logits.cpu().numpy(), row_len.cpu().numpy(), 64))
+
+
+def test_prefill_matches_decode_next_n():
+    """Same score on both paths: B=1, next_n=N=ctx on the paged cache equals
+    prefill over the gathered K (bitwise: identical kernels' arithmetic order)."""
+    _say("mqa_logits vs paged_mqa_logits (next_n=4, ctx=4)")
+    wl = synth.custom(1, 4, [4], num_blocks=3, bt_width=1, seed=23)
+    g = GpuWorkload(wl)
+    ld, _, _ = sai.paged_mqa_logits(g.q_fp8.view(1, 4, 64, 128), g.w_eff, g.pool, g.block_table, g.ctx)
+    cu = torch.tensor([0, 4], dtype=torch.int32, device=DEV)
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, cu, 4)
+    lp, _, _ = sai.mqa_logits(g.q_fp8, g.w_eff, kv, ks, cu, 64)
+    assert torch.equal(ld, lp)
+
+
+# ---------------------------------------------------------------- graph capture
+def test_decode_pipeline_graph_capture_replays_match_eager():
+    _say("hipGraph capture of the decode pipeline")
+    wl = synth.custom(6, 2, [3000, 100, 2049, 5000, 64, 4000], num_blocks=300, bt_width=80, seed=31)
+    g = GpuWorkload(wl)
+    q = g.q_fp8.view(6, 2, 64, 128)
+    eager = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)   # warm-up on side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+    for rep in range(3):
+        for t in out:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        eager2 = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+        torch.cuda.synchronize()
+        for a, b in zip(eager2, eager):
+            assert torch.equal(a, b)
