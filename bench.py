@@ -1,0 +1,342 @@
+#!/usr/bin/env python3
+"""Throughput of the paged lightning-indexer hot path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  decode:  paged_mqa_logits -> topk_rows (top-2048) -> topk_to_global_slots
+  prefill: gather_indexer_k -> mqa_logits -> topk_rows -> topk_to_global_slots
+The default workload is the decode batch the headline metric is quoted on:
+batch 64, next_n 1, contexts uniform in [4096, 16384], a 20000-block paged
+fp8 K cache (169 MB) with a random block table.
+
+Inputs are resident in HBM before the timed region.  The cache is copied into
+several pools (4 x 169 MB > the 256 MB Infinity Cache) and steps rotate over
+them, so every step streams its K from HBM rather than from the MALL.
+
+Printed: one JSON line with the metric, per-step time, the roofline of the
+dominant kernel (paged_mqa_logits; its average duration from HIP events on
+its stream over the timed region), a parity check of the run's own outputs
+against the CPU oracle on sampled rows, and the oracle's own throughput on
+the host cores (cpu_baseline).
+"""
+import argparse
+import ctypes
+import json
+import os
+import re
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "indexer query-tokens/s + K-cache HBM GB/s (% peak), B=64 decode 16K ctx"
+HBM_PEAK_GBPS = 8000.0
+FP8_PEAK_TFLOPS = 5000.0
+K_BYTES_PER_TOKEN = 132          # 128 fp8 codes + one fp32 scale
+Q_BYTES_PER_ROW = 64 * 128       # fp8 query codes
+W_BYTES_PER_ROW = 64 * 4         # fp32 head weights
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_counters.txt")
+COPY_BYTES = 256 << 20
+
+
+class HipEvents:
+    """hipEvent timing through the HIP runtime directly (low host overhead)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            # no system-scope fence: the events only order work on one device
+            assert self.hip.hipEventCreateWithFlags(ctypes.byref(e), 0x20000000) == 0
+            evs.append(e)
+        return evs
+
+    def elapsed_ms(self, a, b):
+        assert self.hip.hipEventSynchronize(b) == 0
+        out = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(out), a, b) == 0
+        return float(out.value)
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def kernel_source_hash():
+    from sparse_attention_indexer_paged_amd.profile_summary import logits_source_hash
+    return logits_source_hash()
+
+
+def counter_traffic():
+    """HBM bytes per paged_mqa_logits launch from the committed rocprofv3 PMC
+    summary, or None if absent or taken on different kernel source."""
+    if not os.path.exists(PROFILE_COUNTERS):
+        return None
+    text = open(PROFILE_COUNTERS).read()
+    m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
+    m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+        return None
+    return float(m_val.group(1))
+
+
+def bf16_tensor(torch, bits, dev):
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def build_inputs(torch, sai, wl, dev, npools):
+    pool = torch.from_numpy(wl.poisoned_pool()).to(dev)
+    for b in range(wl.batch):
+        sai.indexer_k_cache_write(bf16_tensor(torch, wl.k_request(b), dev),
+                                  torch.from_numpy(wl.slots_request(b)).to(dev), pool)
+    q_fp8, w_eff, _ = sai.indexer_q_quant(bf16_tensor(torch, wl.q(), dev),
+                                          torch.from_numpy(wl.w()).to(dev))
+    pools = [pool] + [pool.clone() for _ in range(npools - 1)]
+    return pools, q_fp8, w_eff
+
+
+def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
+    """Time the oracle (as it stands) on a bounded sample of the workload and
+    check the GPU's logits / top-k on those rows."""
+    import oracle as O
+    from sparse_attention_indexer_paged_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    pool = wl.poisoned_pool()
+    for b in sample_requests:
+        O.k_cache_write(synth.bf16_bits_to_f32(wl.k_request(b)), wl.slots_request(b), pool)
+    qc, weff, _ = O.quantize_q(synth.bf16_bits_to_f32(wl.q()), wl.w())
+    nn = wl.next_n
+    rows = [b * nn + j for b in sample_requests for j in range(nn)]
+    lim, req = O.decode_limits(wl.ctx, nn)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref = O.paged_mqa_logits(qc.reshape(wl.batch, nn, 64, 128), weff, pool, wl.block_table,
+                                 wl.ctx, nn, wl.width, rows=rows)
+        top = O.topk_rows(ref[rows], lim[rows], 2048)
+        O.topk_to_global_slots(top, req[rows], wl.block_table)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    # parity of this run's GPU outputs on the sampled rows
+    g = gpu_logits[rows].astype(np.float64)
+    fin = np.isfinite(ref[rows])
+    ok = bool(np.all(np.abs(g[fin] - ref[rows][fin]) <= 1e-4 + 1e-3 * np.abs(ref[rows][fin]))
+              and np.all(np.isneginf(g[~fin])))
+    return {
+        "value": round(reps * len(rows) / el, 2),
+        "unit": "query-tokens/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(rows)} of {wl.rows} query rows (requests {sample_requests[0]}.."
+                   f"{sample_requests[-1]}, {int(wl.ctx[sample_requests].sum())} keys) x {reps} "
+                   f"passes of logits+top-2048+slot ids, {el:.1f} s, numpy/OpenBLAS fp64"),
+    }, ok
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1,
+                    help="workload preset (0 tiny decode, 1 decode B=64, 2 MTP decode, 4 long decode)")
+    ap.add_argument("--pools", type=int, default=4, help="cache copies rotated across steps")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--cpu-sample", type=int, default=16, help="requests in the oracle sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay figure")
+    ap.add_argument("--profile-copy", action="store_true",
+                    help="after timing, copy 256 MiB device-to-device once (a known-size "
+                         "transfer that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}): the indexer decode shards by "
+              "request with no cross-GPU exchange, so a single GPU's throughput is the figure.",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.config == 3:
+        print("the prefill workload is a parity case, not a bench line", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from sparse_attention_indexer_paged_amd import binding as sai
+    from sparse_attention_indexer_paged_amd import synth
+
+    dev = "cuda:0"
+    torch.cuda.set_device(0)
+    lib = sai.load()
+    wl = synth.make(args.config)
+    nn = wl.next_n
+    rows = wl.rows
+    pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, args.pools)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    ctx = torch.from_numpy(wl.ctx).to(dev)
+    width = wl.width
+    logits = torch.empty((rows, width), dtype=torch.float32, device=dev)
+    row_len = torch.empty((rows,), dtype=torch.int32, device=dev)
+    row_req = torch.empty((rows,), dtype=torch.int32, device=dev)
+    idx = torch.empty((rows, 2048), dtype=torch.int32, device=dev)
+    slots = torch.empty((rows, 2048), dtype=torch.int32, device=dev)
+    ws_bytes = sai.topk_workspace_bytes(rows, width, 2048)
+    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    torch.cuda.synchronize()
+
+    stream = torch.cuda.current_stream()
+    s_ptr = ctypes.c_void_p(stream.cuda_stream)
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    logit_args = [(P(q_fp8), P(w_eff), P(p), p.shape[0], P(bt), bt.stride(0), P(ctx), wl.batch, nn,
+                   P(logits), width, P(row_len), P(row_req), s_ptr) for p in pools]
+    topk_args = (P(logits), width, P(row_len), rows, 2048, P(idx), P(ws), ws_bytes, s_ptr)
+    slot_args = (P(idx), P(row_req), P(bt), bt.stride(0), wl.batch, rows, 2048, P(slots), s_ptr)
+
+    def step(i):
+        rc = lib.paged_mqa_logits(*logit_args[i % len(pools)])
+        rc |= lib.topk_rows(*topk_args)
+        rc |= lib.topk_to_global_slots(*slot_args)
+        return rc
+
+    ev = HipEvents()
+    for i in range(args.warmup):
+        assert step(i) == 0
+    torch.cuda.synchronize()
+
+    K = args.steps
+    e0, e1, e2 = ev.create(K), ev.create(K), ev.create(K)
+    rec = ev.hip.hipEventRecord
+    plogits, ptopk, pslots = lib.paged_mqa_logits, lib.topk_rows, lib.topk_to_global_slots
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        rec(e0[i], s_ptr)
+        plogits(*logit_args[i % len(pools)])
+        rec(e1[i], s_ptr)
+        ptopk(*topk_args)
+        pslots(*slot_args)
+        rec(e2[i], s_ptr)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    t_logits = np.array([ev.elapsed_ms(e0[i], e1[i]) for i in range(K)])
+    t_rest = np.array([ev.elapsed_ms(e1[i], e2[i]) for i in range(K)])
+    ev.destroy(e0 + e1 + e2)
+
+    # hipGraph replay of the same step (reported alongside; not the headline value)
+    graph_ms = None
+    try:
+        if args.no_graph:
+            raise RuntimeError("disabled by --no-graph")
+        graphs = []
+        side = torch.cuda.Stream()
+        for p in range(len(pools)):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=side):
+                sai.paged_mqa_logits(q_fp8.view(wl.batch, nn, 64, 128), w_eff, pools[p], bt, ctx,
+                                     width, logits=logits, row_len=row_len, row_req=row_req)
+                sai.topk_rows(logits, row_len, 2048, out=idx, workspace=ws if ws_bytes else None)
+                sai.topk_to_global_slots(idx, row_req, bt, out=slots)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        tg = time.perf_counter()
+        for i in range(K):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        graph_ms = (time.perf_counter() - tg) * 1e3 / K
+    except Exception as exc:  # noqa: BLE001
+        print(f"graph replay skipped: {exc}", file=sys.stderr)
+
+    if args.profile_copy:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
+    # algorithmic bytes and flops of one paged_mqa_logits launch
+    ctx_np = wl.ctx.astype(np.int64)
+    k_bytes = int(ctx_np.sum()) * K_BYTES_PER_TOKEN
+    other_bytes = rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
+    alg_bytes = k_bytes + other_bytes
+    lim = np.repeat(ctx_np, nn) - nn + np.tile(np.arange(nn), wl.batch) + 1
+    flops = float(np.clip(lim, 0, None).sum()) * 64 * 128 * 2
+    t_log_s = float(t_logits.mean()) * 1e-3
+    achieved = alg_bytes / t_log_s / 1e9
+    traffic = counter_traffic()
+
+    ms_per_step = elapsed * 1e3 / K
+    value = rows * K / elapsed
+
+    # parity of this run + oracle throughput on the host
+    gl = logits.cpu().numpy()
+    sample = list(range(min(args.cpu_sample, wl.batch)))
+    cpu = None
+    parity_ok = None
+    if not args.no_cpu_baseline:
+        cpu, parity_ok = cpu_baseline(wl, sample, gl, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "query-tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8-e4m3 x fp8-e4m3 -> fp32",
+        "data": "synthetic (seeded N(0,1) bf16 q/k quantised to fp8 by the library, random block table)",
+        "config": {
+            "workload": wl.name,
+            "batch": wl.batch,
+            "next_n": nn,
+            "context_tokens": int(ctx_np.sum()),
+            "context_range": [int(ctx_np.min()), int(ctx_np.max())],
+            "heads": 64, "head_dim": 128, "block_size": 64, "topk": 2048,
+            "pool_blocks": wl.num_blocks, "pool_copies_rotated": len(pools),
+            "logits_width": width,
+        },
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBPS, 4),
+            "traffic": traffic,
+            "kernel": "paged_mqa_logits",
+            "alg_bytes_per_launch": alg_bytes,
+            "avg_launch_us": round(t_log_s * 1e6, 3),
+        },
+        "k_stream_gbps": round(k_bytes / t_log_s / 1e9, 1),
+        "fp8_mfma_frac": round(flops / t_log_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "topk_plus_slots_us": round(float(t_rest.mean()) * 1e3, 3),
+        "logits_us_p10_p50_p90": [round(float(np.percentile(t_logits, p)) * 1e3, 3) for p in (10, 50, 90)],
+        "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
+        "parity_sampled_rows": parity_ok,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -145,13 +145,13 @@ def k_cache_write(k, slot_mapping, cache):
     cache: uint8 [num_blocks, BLOCK_BYTES] (modified).
     """
     codes, scale = quantize_rows(k)
-    for t, slot in enumerate(np.asarray(slot_mapping).tolist()):
-        if slot < 0:
-            continue
-        blk, off = slot // BLOCK, slot % BLOCK
-        cache[blk, off * DIM:(off + 1) * DIM] = codes[t]
-        cache[blk, VALUE_BYTES + 4 * off:VALUE_BYTES + 4 * off + 4] = \
-            np.frombuffer(scale[t:t + 1].tobytes(), dtype=np.uint8)
+    slot_mapping = np.asarray(slot_mapping, dtype=np.int64)
+    keep = slot_mapping >= 0
+    blk, off = slot_mapping[keep] // BLOCK, slot_mapping[keep] % BLOCK
+    values = cache[:, :VALUE_BYTES].reshape(-1, BLOCK, DIM)      # views into the cache
+    scales = cache[:, VALUE_BYTES:BLOCK_BYTES].view(np.float32)  # [num_blocks, 64]
+    values[blk, off] = codes[keep]
+    scales[blk, off] = scale[keep]
     return cache
 
 

@@ -15,18 +15,26 @@ INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsai.so")
 
 SOURCES = ["cache_ops.hip", "logits.hip", "topk.hip"]
+OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [
     "--offload-arch=gfx950",
     "-O3",
     "-std=c++17",
     "-fPIC",
-    "-shared",
     # packed fp32 VALU ops stay off: plain fp32 math only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall",
     "-Wno-unused-command-line-argument",
 ]
+
+# The logits kernels never rely on NaN semantics of fp operations (masks are
+# integer selects): without NaN handling ReLU is one v_max_f32 instead of a
+# canonicalise + max pair, and MFMA results go straight to VGPRs (no AGPR
+# copies).
+PER_FILE = {
+    "logits.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
 
 
 def hipcc():
@@ -34,10 +42,7 @@ def hipcc():
     return os.path.join(rocm, "bin", "hipcc")
 
 
-def build(verbose=False):
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc()] + FLAGS + ["-I", INCLUDE, "-I", CSRC] + srcs + ["-o", tmp]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -49,8 +54,25 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + "\n".join(msgs))
     if verbose and msgs:
         print("\n".join(msgs))
-    os.replace(tmp, LIB)
-    return LIB
+
+
+def build(verbose=False, defines=(), out=None):
+    """Compile every source to an object, then link libsai.so.  ``defines``
+    (e.g. ["SAI_DECODE_CHUNK=8"]) and ``out`` serve launch-shape sweeps."""
+    os.makedirs(OBJDIR, exist_ok=True)
+    dflags = ["-D" + d for d in defines]
+    tag = "_".join(d.replace("=", "") for d in defines)
+    objs = []
+    for src in SOURCES:
+        obj = os.path.join(OBJDIR, src.replace(".hip", (("_" + tag) if tag else "") + ".o"))
+        _run([hipcc()] + FLAGS + PER_FILE.get(src, []) + dflags + ["-I", INCLUDE, "-I", CSRC, "-c",
+             os.path.join(CSRC, src), "-o", obj], verbose)
+        objs.append(obj)
+    lib = out or LIB
+    tmp = lib + ".tmp"
+    _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC"] + objs + ["-o", tmp], verbose)
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -27,7 +27,45 @@
 
 using namespace sai;
 
+#ifndef SAI_DECODE_WAVES
+#define SAI_DECODE_WAVES 2048
+#endif
+#ifndef SAI_DECODE_DEPTH
+#define SAI_DECODE_DEPTH 2
+#endif
+#ifndef SAI_DECODE_CAP
+#define SAI_DECODE_CAP 8
+#endif
+
 namespace {
+
+// Decode launch shape: waves of the persistent grid (8 per CU), blocks in
+// the per-wave register ring (DEPTH-1 blocks in flight while one is scored),
+// and units whose results are held in registers before they are stored.
+constexpr int kDecodeWaves = SAI_DECODE_WAVES;
+constexpr int kDecodeDepth = SAI_DECODE_DEPTH;
+constexpr int kDecodeCap = SAI_DECODE_CAP;
+
+// Masking by integer select on the bit patterns, so the choice is never an
+// fp operation the no-NaN compile mode may reason about.
+__device__ __forceinline__ float select_f(bool c, float a, uint32_t b_bits) {
+  return __uint_as_float(c ? __float_as_uint(a) : b_bits);
+}
+constexpr uint32_t kNegInfBits = 0xFF800000u;
+
+#ifndef SAI_NT_STORE
+#define SAI_NT_STORE 1
+#endif
+// Logits are written once and read by the next kernel from L2/HBM: stream
+// them past the caches (non-temporal) when SAI_NT_STORE is set.
+__device__ __forceinline__ void store_logit(float* p, float v) {
+#if SAI_NT_STORE
+  __builtin_nontemporal_store(v, p);
+#else
+  *p = v;
+#endif
+}
+constexpr uint32_t kNaNBits = 0x7FC00000u;
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
 
@@ -151,48 +189,60 @@ __device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], 
 __device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ decode
-// Work: unit (b, c) = key block c of request b, for all next_n rows of b.
-// Units are flattened in (b, c) order and split evenly over every wave of the
-// grid (the split needs only device-side context lengths: no host sync); a
-// wave also takes an even share of the -inf fill of column blocks past each
-// request's last key block.  Workgroup g runs on XCD g % 8; logical
-// workgroup (g % 8) * (G / 8) + g / 8 makes each XCD take one contiguous
-// range of units, so a request's query rows are fetched into one L2.
-template <int NN>
+// Grid of persistent waves, each with an equal share of the work: units
+// (b, c) = key block c of request b are flattened in (b, c) order and wave w
+// of NW scores units [w*U/NW, (w+1)*U/NW); the -inf fill of column blocks
+// past each request's last key block is flattened and split the same way.
+// Each workgroup builds the two prefix sums over the requests' block counts
+// in LDS from the device-side context lengths (no host sync).  A wave first
+// issues its query rows, then keeps DEPTH-1 K blocks in flight while it
+// scores one, and stores results in groups of CAP units after the group's
+// loads have been issued.
+template <int NN, int DEPTH, int CAP>
 __global__ __launch_bounds__(256) void paged_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ bt, int64_t bt_stride,
     const int32_t* __restrict__ ctx_lens, int32_t batch, float* __restrict__ logits,
     int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out) {
+  static_assert(CAP % DEPTH == 0, "ring slots must repeat within a store group");
   extern __shared__ int smem[];
   int* s_unit = smem;                   // [batch+1] prefix of key blocks
   int* s_fill = smem + (batch + 1);     // [batch+1] prefix of fill column blocks
   int* s_ctx = smem + 2 * (batch + 1);  // [batch] clamped context
-  int* scratch = smem + 3 * (batch + 1);
+  int* s_tot = smem + 3 * (batch + 1);  // [8] per-wave totals
 
-  const int lane = threadIdx.x & 63;
+  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
   const int maxc = (int)min64(stride, bt_stride * kBlock);
   const int wblocks = (int)((stride + kBlock - 1) / kBlock);
 
   int run_u = 0, run_f = 0;
   for (int base = 0; base < batch; base += 256) {
-    const int b = base + threadIdx.x;
+    const int bb = base + threadIdx.x;
     int nu = 0, nf = 0;
-    if (b < batch) {
-      const int c = min(max(ctx_lens[b], 0), maxc);
-      s_ctx[b] = c;
+    if (bb < batch) {
+      const int c = min(max(ctx_lens[bb], 0), maxc);
+      s_ctx[bb] = c;
       nu = cdiv_i(c, kBlock);
       nf = wblocks - nu;
     }
-    int tu, tf;
-    const int eu = block_exclusive_scan<256>(nu, scratch, &tu);
-    const int ef = block_exclusive_scan<256>(nf, scratch, &tf);
-    if (b < batch) {
-      s_unit[b] = run_u + eu;
-      s_fill[b] = run_f + ef;
+    const int iu = wave_inclusive_scan(nu), jf = wave_inclusive_scan(nf);
+    if (lane == 63) {
+      s_tot[wid] = iu;
+      s_tot[4 + wid] = jf;
     }
-    run_u += tu;
-    run_f += tf;
+    __syncthreads();
+    int pu = run_u, pf = run_f;
+    for (int k = 0; k < wid; ++k) {
+      pu += s_tot[k];
+      pf += s_tot[4 + k];
+    }
+    if (bb < batch) {
+      s_unit[bb] = pu + iu - nu;
+      s_fill[bb] = pf + jf - nf;
+    }
+    run_u += s_tot[0] + s_tot[1] + s_tot[2] + s_tot[3];
+    run_f += s_tot[4] + s_tot[5] + s_tot[6] + s_tot[7];
+    __syncthreads();
   }
   if (threadIdx.x == 0) {
     s_unit[batch] = run_u;
@@ -202,99 +252,110 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
 
   const int G = gridDim.x;
   const int lg = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int wv = __builtin_amdgcn_readfirstlane(lg * 4 + (threadIdx.x >> 6));
-  const int nwv = G * 4;
+  const int w = __builtin_amdgcn_readfirstlane(lg * 4 + wid);
+  const int nw = G * 4;
 
-  // row metadata
-  const int rows = batch * NN;
-  for (int r = wv * 64 + lane; r < rows; r += nwv * 64) {
+  for (int r = w * 64 + lane; r < batch * NN; r += nw * 64) {
     const int b = r / NN, j = r - b * NN;
     if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
     if (row_req_out) row_req_out[r] = b;
   }
 
-  const int U = s_unit[batch];
-  int u = (int)((int64_t)U * wv / nwv);
-  const int u1 = (int)((int64_t)U * (wv + 1) / nwv);
-  if (u < u1) {
-    // request of unit u: the last b with s_unit[b] <= u
+  auto find = [&](const int* pre, int u) {  // last b with pre[b] <= u
     int lo = 0, hi = batch;
     while (hi - lo > 1) {
       const int mid = (lo + hi) >> 1;
-      if (s_unit[mid] <= u) lo = mid; else hi = mid;
+      if (pre[mid] <= u) lo = mid; else hi = mid;
     }
-    int ub = lo;
-    int qb = -1;
+    return lo;
+  };
+
+  const int U = s_unit[batch];
+  const int u0 = (int)((int64_t)U * w / nw);
+  const int u1 = (int)((int64_t)U * (w + 1) / nw);
+  if (u0 < u1) {
+    int b_ld = find(s_unit, u0), u_ld = u0;  // load frontier
+    int b_cp = b_ld, u_cp = u0;              // scoring position
+    int qb = b_cp;
     v8i qa[NN][4];
     float4 wf[NN][4];
-    KFrag fa, fb;
-
-    auto block_of = [&](int unit, int b, bool& ok) -> const uint8_t* {
-      const int c = unit - s_unit[b];
-      const int32_t blk = bt[(int64_t)b * bt_stride + c];
-      ok = blk >= 0 && blk < num_blocks;
-      return cache + (int64_t)(ok ? blk : 0) * kBlockBytes;
-    };
-    bool ok_a, ok_b;
-    {
-      const uint8_t* p = block_of(u, ub, ok_a);
-      if (ok_a) load_kfrag_paged(fa, p); else zero_kfrag(fa);
-    }
-
-    auto step = [&](KFrag& cur, bool& ok_cur, KFrag& nxt, bool& ok_nxt) -> bool {
-      const int un = u + 1;
-      int bn = ub;
-      if (un < u1) {
-        while (s_unit[bn + 1] <= un) ++bn;
-        const uint8_t* p = block_of(un, bn, ok_nxt);
-        if (ok_nxt) load_kfrag_paged(nxt, p); else zero_kfrag(nxt);
-      }
-      if (ub != qb) {
-        qb = ub;
 #pragma unroll
-        for (int j = 0; j < NN; ++j) {
-          load_qfrag(qa[j], q + ((int64_t)qb * NN + j) * (kHeads * kDim));
-          load_wfrag(wf[j], wts + ((int64_t)qb * NN + j) * kHeads);
+    for (int r = 0; r < NN; ++r) {
+      load_qfrag(qa[r], q + ((int64_t)qb * NN + r) * (kHeads * kDim));
+      load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
+    }
+    KFrag buf[DEPTH];
+    bool okb[DEPTH];
+    auto issue = [&](KFrag& f, bool& ok) {
+      const int32_t blk = bt[(int64_t)b_ld * bt_stride + (u_ld - s_unit[b_ld])];
+      ok = blk >= 0 && blk < num_blocks;
+      if (ok) load_kfrag_paged(f, cache + (int64_t)blk * kBlockBytes); else zero_kfrag(f);
+      ++u_ld;
+      if (u_ld < u1) while (s_unit[b_ld + 1] <= u_ld) ++b_ld;
+    };
+#pragma unroll
+    for (int i = 0; i < DEPTH - 1; ++i)
+      if (u_ld < u1) issue(buf[i], okb[i]);
+
+    float res[CAP][NN];
+    int64_t roff[CAP];  // offset of the unit's first row
+    int ccol[CAP];      // first column of the unit's block
+    while (u_cp < u1) {
+      int used = 0;
+#pragma unroll
+      for (int sl = 0; sl < CAP; ++sl) {
+        if (u_cp >= u1) break;
+        if (DEPTH > 1 && u_ld < u1) issue(buf[(sl + DEPTH - 1) % DEPTH], okb[(sl + DEPTH - 1) % DEPTH]);
+        if (DEPTH == 1) issue(buf[0], okb[0]);
+        if (b_cp != qb) {
+          qb = b_cp;
+#pragma unroll
+          for (int r = 0; r < NN; ++r) {
+            load_qfrag(qa[r], q + ((int64_t)qb * NN + r) * (kHeads * kDim));
+            load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
+          }
+        }
+        const KFrag& cur = buf[sl % DEPTH];
+        const int c = u_cp - s_unit[b_cp];
+        const int col = c * kBlock + lane;
+        const int ctx = s_ctx[b_cp];
+#pragma unroll
+        for (int r = 0; r < NN; ++r) {
+          const float sc = score_row(cur, qa[r], wf[r]);
+          const float v = select_f(okb[sl % DEPTH], sc * cur.s, kNaNBits);
+          res[sl][r] = select_f(col < ctx - NN + r + 1, v, kNegInfBits);
+        }
+        roff[sl] = (int64_t)b_cp * NN * stride;
+        ccol[sl] = c * kBlock;
+        used = sl + 1;
+        ++u_cp;
+        if (u_cp < u1) while (s_unit[b_cp + 1] <= u_cp) ++b_cp;
+      }
+#pragma unroll
+      for (int sl = 0; sl < CAP; ++sl) {
+        if (sl >= used) break;
+        const int col = ccol[sl] + lane;
+        if (col < stride) {
+#pragma unroll
+          for (int r = 0; r < NN; ++r) store_logit(logits + roff[sl] + (int64_t)r * stride + col, res[sl][r]);
         }
       }
-      const int c = u - s_unit[ub];
-      const int col = c * kBlock + lane;
-      const int ctx = s_ctx[ub];
-#pragma unroll
-      for (int j = 0; j < NN; ++j) {
-        const float sc = score_row(cur, qa[j], wf[j]);
-        const int limit = ctx - NN + j + 1;
-        float v = ok_cur ? sc * cur.s : __uint_as_float(0x7FC00000u);
-        v = col < limit ? v : -INFINITY;
-        if (col < stride) logits[((int64_t)ub * NN + j) * stride + col] = v;
-      }
-      if (un >= u1) return false;
-      u = un;
-      ub = bn;
-      return true;
-    };
-    while (step(fa, ok_a, fb, ok_b) && step(fb, ok_b, fa, ok_a)) {
     }
   }
 
-  // -inf fill of the column blocks past each request's last key block
   const int F = s_fill[batch];
-  int f = (int)((int64_t)F * wv / nwv);
-  const int f1 = (int)((int64_t)F * (wv + 1) / nwv);
+  int f = (int)((int64_t)F * w / nw);
+  const int f1 = (int)((int64_t)F * (w + 1) / nw);
   if (f < f1) {
-    int lo = 0, hi = batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (s_fill[mid] <= f) lo = mid; else hi = mid;
-    }
-    int b = lo;
+    int b = find(s_fill, f);
+    const float ninf = __uint_as_float(kNegInfBits);
     for (; f < f1; ++f) {
       while (s_fill[b + 1] <= f) ++b;
       const int cb = (s_unit[b + 1] - s_unit[b]) + (f - s_fill[b]);
       const int col = cb * kBlock + lane;
       if (col < stride) {
 #pragma unroll
-        for (int j = 0; j < NN; ++j) logits[((int64_t)b * NN + j) * stride + col] = -INFINITY;
+        for (int r = 0; r < NN; ++r) store_logit(logits + ((int64_t)b * NN + r) * stride + col, ninf);
       }
     }
   }
@@ -404,7 +465,7 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
                               s_w[wr][4 * 2 + (lane >> 4)], s_w[wr][4 * 3 + (lane >> 4)]};
         const float sc = score_row(cur, qa[r], wf);
         const int limit = ir0 + r + 1;
-        const float v = col < limit ? sc * cur.s : -INFINITY;
+        const float v = select_f(col < limit, sc * cur.s, kNegInfBits);
         if (col < col_end) logits[(base_tok + ir0 + r) * stride + col] = v;
       }
     }
@@ -416,32 +477,30 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
     }
   }
   // -inf for the chunk's columns past the computed blocks
+  const float ninf = __uint_as_float(kNegInfBits);
   for (int col = col0 + nblk * kBlock + lane; col < col_end; col += 64) {
-    for (int r = 0; r < nrows; ++r) logits[(base_tok + ir0 + r) * stride + col] = -INFINITY;
+    for (int r = 0; r < nrows; ++r) logits[(base_tok + ir0 + r) * stride + col] = ninf;
   }
 }
 
 template <int NN>
 int launch_paged(const void* q, const float* w, const void* cache, int64_t num_blocks,
                  const int32_t* bt, int64_t bt_stride, const int32_t* ctx, int32_t batch,
-                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, hipStream_t s,
-                 int target_waves) {
+                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, hipStream_t s) {
+  if (batch > 4096) return SAI_EUNSUPPORTED;  // LDS prefix arrays
   const int64_t wblocks = (stride + kBlock - 1) / kBlock;
   const int64_t units_max = (int64_t)batch * wblocks;
-  int64_t waves = std::min<int64_t>(target_waves, std::max<int64_t>(units_max, 1));
+  const int64_t waves = std::min<int64_t>(kDecodeWaves, std::max<int64_t>(units_max, 1));
   int64_t G = (waves + 3) / 4;
   G = (G + 7) / 8 * 8;
   const size_t lds = (size_t)(3 * (batch + 1) + 8) * sizeof(int);
-  hipLaunchKernelGGL(paged_logits_kernel<NN>, dim3((unsigned)G), dim3(256), lds, s,
-                     (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt, bt_stride, ctx,
-                     batch, logits, stride, rl, rr);
+  hipLaunchKernelGGL((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap>), dim3((unsigned)G),
+                     dim3(256), lds, s, (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt,
+                     bt_stride, ctx, batch, logits, stride, rl, rr);
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
 
 }  // namespace
-
-// Waves the decode kernel spreads its units over (8 per CU on 256 CUs).
-static int g_decode_waves = 2048;
 
 extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
                                 int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
@@ -454,15 +513,14 @@ extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const v
   if (!q_fp8 || !weights || !kv_cache || !block_table || !context_lens || !logits) return SAI_EINVAL;
   if (!aligned16(q_fp8) || !aligned16(weights) || !aligned16(kv_cache)) return SAI_EINVAL;
   if (logits_stride == 0) return SAI_EINVAL;
-  if (batch > 4096) return SAI_EUNSUPPORTED;
   const int64_t wblocks = (logits_stride + kBlock - 1) / kBlock;
   if ((int64_t)batch * wblocks > 0x7FFFFFFF / 2 || logits_stride > 0x7FFFFFFF - kBlock)
     return SAI_EUNSUPPORTED;
   switch (next_n) {
-    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
-    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
-    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
-    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream, g_decode_waves);
+    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
+    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
+    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
+    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
   }
 }
 

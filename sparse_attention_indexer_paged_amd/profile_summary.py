@@ -1,0 +1,116 @@
+"""Summarise rocprofv3 output into the short text files kept under profiles/.
+
+  kernel stats:   python -m sparse_attention_indexer_paged_amd.profile_summary stats \\
+                      --csv <..._kernel_stats.csv> --command "<rocprofv3 command>" --out <txt>
+  HBM traffic:    python -m sparse_attention_indexer_paged_amd.profile_summary traffic \\
+                      --fetch <fetch ..._counter_collection.csv> --write <write ..._counter_collection.csv> \\
+                      --kernel paged_logits_kernel --copy-bytes 268435456 \\
+                      --command "<both rocprofv3 commands>" --out <txt>
+
+FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  They are scaled by what the
+same counters read for a plain device-to-device copy of --copy-bytes bytes
+(the copy kernel reads and writes exactly that many bytes), and the traffic
+line also records the hash of the logits kernel source it was taken on.
+"""
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+
+def logits_source_hash():
+    h = hashlib.sha256()
+    for f in ("logits.hip", "sai_device.h"):
+        with open(os.path.join(HERE, "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def _per_dispatch(path, counter):
+    """kernel name -> list of per-dispatch counter values (summed over the
+    counter's instances within a dispatch)."""
+    disp = {}
+    for row in csv.DictReader(open(path)):
+        if row.get("Counter_Name") != counter:
+            continue
+        key = (row["Dispatch_Id"], row["Kernel_Name"])
+        disp[key] = disp.get(key, 0.0) + float(row["Counter_Value"])
+    out = {}
+    for (_, name), v in disp.items():
+        out.setdefault(name, []).append(v)
+    return out
+
+
+def _pick(d, needle):
+    names = [n for n in d if needle in n]
+    if not names:
+        raise SystemExit(f"no kernel matching {needle!r}; have {sorted(d)[:8]}")
+    return names[0], d[names[0]]
+
+
+def traffic(args):
+    fetch = _per_dispatch(args.fetch, "FETCH_SIZE")
+    write = _per_dispatch(args.write, "WRITE_SIZE")
+    _, copy_f = _pick(fetch, args.copy_kernel)
+    _, copy_w = _pick(write, args.copy_kernel)
+    kib = args.copy_bytes / 1024.0
+    f_fetch = kib / max(copy_f)
+    f_write = kib / max(copy_w)
+    name, kf = _pick(fetch, args.kernel)
+    _, kw = _pick(write, args.kernel)
+    fk = statistics.mean(kf) * f_fetch
+    wk = statistics.mean(kw) * f_write
+    lines = [
+        f"# HBM traffic of {name} per dispatch (rocprofv3 PMC, KiB per dispatch, scaled)",
+        f"commands: {args.command}",
+        f"copy calibration: {args.copy_kernel} of {args.copy_bytes} bytes read "
+        f"FETCH_SIZE {max(copy_f):.1f} KiB, WRITE_SIZE {max(copy_w):.1f} KiB -> factors "
+        f"{f_fetch:.4f} / {f_write:.4f}",
+        f"dispatches: {len(kf)} (fetch run), {len(kw)} (write run)",
+        f"fetch_kib_per_dispatch_raw: {statistics.mean(kf):.1f}",
+        f"write_kib_per_dispatch_raw: {statistics.mean(kw):.1f}",
+        f"fetch_bytes_per_launch: {fk * 1024:.0f}",
+        f"write_bytes_per_launch: {wk * 1024:.0f}",
+        f"traffic_bytes_per_launch: {(fk + wk) * 1024:.0f}",
+        f"kernel_source_hash: {logits_source_hash()}",
+    ]
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = [f"# rocprofv3 kernel statistics", f"command: {args.command}",
+             "name | calls | average_us | min_us | max_us | percent"]
+    for r in rows:
+        lines.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+                     f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
+                     f"{float(r['Percentage']):.2f}")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    sub = ap.add_subparsers(dest="cmd", required=True)
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch", required=True)
+    t.add_argument("--write", required=True)
+    t.add_argument("--kernel", default="paged_logits_kernel")
+    t.add_argument("--copy-kernel", default="copyBuffer")
+    t.add_argument("--copy-bytes", type=int, default=256 << 20)
+    t.add_argument("--command", required=True)
+    t.add_argument("--out", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--command", required=True)
+    s.add_argument("--out", required=True)
+    args = ap.parse_args()
+    traffic(args) if args.cmd == "traffic" else stats(args)
+
+
+if __name__ == "__main__":
+    main()
