@@ -187,8 +187,45 @@ extern "C" int gather_indexer_k(const void* kv_cache, int64_t num_blocks, const 
 }
 
 // ---------------------------------------------------------------- slot ids
-// One thread per output element; a workgroup covers 256 consecutive entries
-// of the flattened [rows, k] array.
+// One 256-thread workgroup per row: the row's top-k indices are loaded into
+// registers while the request's block-table row is staged in LDS, so each
+// index maps to its slot with an LDS lookup instead of a dependent global
+// gather.  Tables wider than kSlotLdsEntries use the elementwise kernel.
+constexpr int kSlotLdsEntries = 8192;
+constexpr int kSlotPerThread = 8;  // k <= 2048 = 256 threads x 8
+
+__global__ __launch_bounds__(256) void slots_row_kernel(
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ row_req,
+    const int32_t* __restrict__ bt, int64_t bt_stride, int32_t batch, int32_t k,
+    int32_t* __restrict__ out) {
+  __shared__ int32_t s_bt[kSlotLdsEntries];
+  const int64_t r = blockIdx.x;
+  const int tid = threadIdx.x;
+  int32_t iv[kSlotPerThread];
+#pragma unroll
+  for (int e = 0; e < kSlotPerThread; ++e) {
+    const int j = tid + 256 * e;
+    iv[e] = j < k ? idx[r * k + j] : -1;
+  }
+  const int32_t b = row_req[r];
+  const bool okb = b >= 0 && b < batch;
+  for (int64_t c = tid; c < bt_stride; c += 256) s_bt[c] = okb ? bt[(int64_t)b * bt_stride + c] : -1;
+  __syncthreads();
+#pragma unroll
+  for (int e = 0; e < kSlotPerThread; ++e) {
+    const int j = tid + 256 * e;
+    if (j >= k) break;
+    const int32_t i = iv[e];
+    int32_t slot = -1;
+    if (i >= 0 && (i / kBlock) < bt_stride) {
+      const int32_t blk = s_bt[i / kBlock];
+      if (blk >= 0) slot = blk * kBlock + (i % kBlock);
+    }
+    out[r * k + j] = slot;
+  }
+}
+
+// One thread per output element (tables wider than the LDS stage).
 __global__ __launch_bounds__(256) void slots_kernel(
     const int32_t* __restrict__ idx, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ bt, int64_t bt_stride, int32_t batch, int64_t total, int32_t k,
@@ -216,10 +253,15 @@ extern "C" int topk_to_global_slots(const int32_t* topk_idx, const int32_t* row_
   if (rows < 0 || k < 0 || batch < 0 || bt_stride < 0) return SAI_EINVAL;
   if (rows == 0 || k == 0) return SAI_OK;
   if (!topk_idx || !row_req || !block_table || !out_slots) return SAI_EINVAL;
+  if (k <= 256 * kSlotPerThread && bt_stride <= kSlotLdsEntries) {
+    hipLaunchKernelGGL(slots_row_kernel, dim3(rows), dim3(256), 0, stream, topk_idx, row_req,
+                       block_table, bt_stride, batch, k, out_slots);
+    return launch_status();
+  }
   const int64_t total = (int64_t)rows * k;
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  hipLaunchKernelGGL(slots_kernel, dim3((unsigned)grid), dim3(256), 0, stream, topk_idx, row_req,
+  hipLaunchKernelGGL(slots_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, row_req,
                      block_table, bt_stride, batch, total, k, out_slots);
   return launch_status();
 }

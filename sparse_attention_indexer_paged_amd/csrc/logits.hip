@@ -274,9 +274,23 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
   if (u0 < u1) {
-    int b_ld = find(s_unit, u0), u_ld = u0;  // load frontier
-    int b_cp = b_ld, u_cp = u0;              // scoring position
+    int u_ld = u0;                        // load frontier
+    int b_cp = find(s_unit, u0), u_cp = u0;  // scoring position
     int qb = b_cp;
+    // Block ids of the wave's next 64 units, one per lane, fetched with one
+    // vector load so the ring never waits on a block-table read per unit.
+    int t_blk = -1, win0 = u0;
+    auto fill_table = [&](int first) {
+      const int u = first + lane;
+      int blk = -1;
+      if (u < u1) {
+        const int b = find(s_unit, u);
+        blk = bt[(int64_t)b * bt_stride + (u - s_unit[b])];
+      }
+      t_blk = blk;
+      win0 = first;
+    };
+    fill_table(u0);
     v8i qa[NN][4];
     float4 wf[NN][4];
 #pragma unroll
@@ -287,11 +301,11 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     KFrag buf[DEPTH];
     bool okb[DEPTH];
     auto issue = [&](KFrag& f, bool& ok) {
-      const int32_t blk = bt[(int64_t)b_ld * bt_stride + (u_ld - s_unit[b_ld])];
+      if (u_ld - win0 >= 64) fill_table(u_ld);
+      const int32_t blk = __builtin_amdgcn_readlane(t_blk, u_ld - win0);
       ok = blk >= 0 && blk < num_blocks;
       if (ok) load_kfrag_paged(f, cache + (int64_t)blk * kBlockBytes); else zero_kfrag(f);
       ++u_ld;
-      if (u_ld < u1) while (s_unit[b_ld + 1] <= u_ld) ++b_ld;
     };
 #pragma unroll
     for (int i = 0; i < DEPTH - 1; ++i)

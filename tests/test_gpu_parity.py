@@ -275,3 +275,35 @@ def test_decode_pipeline_graph_capture_replays_match_eager():
         torch.cuda.synchronize()
         for a, b in zip(eager2, eager):
             assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000])
+def test_topk_every_row_width_path(width):
+    """Row widths on both sides of each register-resident size and the
+    streaming kernel beyond them; rows of every length class."""
+    _say(f"topk_rows: width {width}")
+    rng = np.random.default_rng(width)
+    rows = 6
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    L[1] = np.round(L[1] * 3)                              # heavy ties
+    L[2, : width // 2] = -np.inf
+    lens = np.array([width, width, width, min(width, 2049), max(width // 3, 1), 2048], np.int32)
+    got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), 2048)
+    assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, 2048))
+
+
+def test_slots_wide_table_elementwise_path():
+    _say("topk_to_global_slots: block table wider than the LDS stage")
+    rng = np.random.default_rng(8)
+    bt = rng.integers(-1, 50000, (3, 9000)).astype(np.int32)
+    idx = rng.integers(-1, 9000 * 64, (4, 300)).astype(np.int32)
+    req = np.array([0, 2, 1, 7], np.int32)
+    got = sai.topk_to_global_slots(torch.from_numpy(idx).to(DEV), torch.from_numpy(req).to(DEV),
+                                   torch.from_numpy(bt).to(DEV)).cpu().numpy()
+    want = np.full_like(idx, -1)
+    for r in range(3):
+        b = req[r]
+        blk = bt[b][np.maximum(idx[r], 0) // 64]
+        ok = (idx[r] >= 0) & (blk >= 0)
+        want[r, ok] = blk[ok] * 64 + idx[r][ok] % 64
+    assert np.array_equal(got, want)
