@@ -150,13 +150,121 @@ def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
     }, ok
 
 
+def decode_pipeline(torch, sai, lib, wl, dev, npools):
+    """Decode step: paged_mqa_logits -> topk_rows -> topk_to_global_slots."""
+    nn, rows, width = wl.next_n, wl.rows, wl.width
+    pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    ctx = torch.from_numpy(wl.ctx).to(dev)
+    t = dict(pools=pools, q=q_fp8, w=w_eff, bt=bt, ctx=ctx,
+             logits=torch.empty((rows, width), dtype=torch.float32, device=dev),
+             row_len=torch.empty((rows,), dtype=torch.int32, device=dev),
+             row_req=torch.empty((rows,), dtype=torch.int32, device=dev),
+             idx=torch.empty((rows, 2048), dtype=torch.int32, device=dev),
+             slots=torch.empty((rows, 2048), dtype=torch.int32, device=dev))
+    P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def launches(s):
+        return [
+            ("paged_mqa_logits", lambda i: lib.paged_mqa_logits(
+                P(q_fp8), P(w_eff), P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0),
+                P(ctx), wl.batch, nn, P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), s)),
+            ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
+                                                  P(t["idx"]), None, 0, s)),
+            ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
+                P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
+                P(t["slots"]), s)),
+        ]
+    ctx_np = wl.ctx.astype(np.int64)
+    k_bytes = int(ctx_np.sum()) * K_BYTES_PER_TOKEN
+    alg_bytes = k_bytes + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
+    lim = np.repeat(ctx_np, nn) - nn + np.tile(np.arange(nn), wl.batch) + 1
+    flops = float(np.clip(lim, 0, None).sum()) * 64 * 128 * 2
+    return t, launches, 0, dict(bound="hbm", alg_bytes=alg_bytes, k_bytes=k_bytes, flops=flops)
+
+
+def prefill_pipeline(torch, sai, lib, wl, dev, npools):
+    """Prefill step: gather_indexer_k -> mqa_logits -> topk_rows -> topk_to_global_slots."""
+    rows, width, total = wl.rows, wl.width, wl.total_tokens
+    pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
+    bt = torch.from_numpy(wl.block_table).to(dev)
+    cu = torch.from_numpy(wl.cu_seq_lens).to(dev)
+    t = dict(pools=pools, q=q_fp8, w=w_eff, bt=bt, cu=cu,
+             k=torch.empty((total, 128), dtype=torch.uint8, device=dev),
+             ks=torch.empty((total,), dtype=torch.float32, device=dev),
+             logits=torch.empty((rows, width), dtype=torch.float32, device=dev),
+             row_len=torch.empty((rows,), dtype=torch.int32, device=dev),
+             row_req=torch.empty((rows,), dtype=torch.int32, device=dev),
+             idx=torch.empty((rows, 2048), dtype=torch.int32, device=dev),
+             slots=torch.empty((rows, 2048), dtype=torch.int32, device=dev))
+    P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def launches(s):
+        return [
+            ("gather_indexer_k", lambda i: lib.gather_indexer_k(
+                P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0), P(cu), wl.batch, total,
+                P(t["k"]), P(t["ks"]), s)),
+            ("mqa_logits", lambda i: lib.mqa_logits(
+                P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu), wl.batch, total, P(t["logits"]),
+                width, P(t["row_len"]), P(t["row_req"]), s)),
+            ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
+                                                  P(t["idx"]), None, 0, s)),
+            ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
+                P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
+                P(t["slots"]), s)),
+        ]
+    lim = np.concatenate([np.arange(1, int(c) + 1) for c in wl.ctx]).astype(np.float64)
+    flops = float(lim.sum()) * 64 * 128 * 2
+    alg_bytes = total * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + 132 + width * 4)
+    return t, launches, 1, dict(bound="mfma", alg_bytes=alg_bytes, k_bytes=total * 132, flops=flops)
+
+
+def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
+    """Oracle throughput on a sample of prefill rows spread over the request."""
+    import oracle as O
+    from sparse_attention_indexer_paged_amd import synth
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    pool = wl.poisoned_pool()
+    for b in range(wl.batch):
+        O.k_cache_write(synth.bf16_bits_to_f32(wl.k_request(b)), wl.slots_request(b), pool)
+    qc, weff, _ = O.quantize_q(synth.bf16_bits_to_f32(wl.q()), wl.w())
+    total = wl.total_tokens
+    rows = np.linspace(0, total - 1, nrows).astype(int).tolist()
+    kv, ks = O.gather_indexer_k(pool, wl.block_table, wl.cu_seq_lens, total)
+    row_len = np.arange(1, total + 1)
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref = O.mqa_logits(qc, weff, kv, ks, wl.cu_seq_lens, wl.width, rows=rows)
+        top = O.topk_rows(ref[rows], row_len[rows], 2048)
+        O.topk_to_global_slots(top, np.zeros(len(rows), np.int64), wl.block_table)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    g = gpu_logits[rows].astype(np.float64)
+    fin = np.isfinite(ref[rows])
+    ok = bool(np.all(np.abs(g[fin] - ref[rows][fin]) <= 1e-4 + 1e-3 * np.abs(ref[rows][fin]))
+              and np.all(np.isneginf(g[~fin])))
+    return {
+        "value": round(reps * len(rows) / el, 2), "unit": "query-tokens/s", "cores": threads,
+        "kind": "oracle",
+        "sample": f"{len(rows)} of {total} prefill rows spread over the request x {reps} passes of "
+                  f"gather+logits+top-2048+slot ids, {el:.1f} s, numpy/OpenBLAS fp64",
+    }, ok
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1,
-                    help="workload preset (0 tiny decode, 1 decode B=64, 2 MTP decode, 4 long decode)")
+                    help="workload preset: 0 tiny decode, 1 decode B=64 (default), 2 MTP decode, "
+                         "3 prefill 8192, 4 long decode")
     ap.add_argument("--pools", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests in the oracle sample")
@@ -172,9 +280,6 @@ def main():
               "request with no cross-GPU exchange, so a single GPU's throughput is the figure.",
               file=sys.stderr)
         sys.exit(2)
-    if args.config == 3:
-        print("the prefill workload is a parity case, not a bench line", file=sys.stderr)
-        sys.exit(2)
 
     import torch
     from sparse_attention_indexer_paged_amd import binding as sai
@@ -184,33 +289,21 @@ def main():
     torch.cuda.set_device(0)
     lib = sai.load()
     wl = synth.make(args.config)
-    nn = wl.next_n
-    rows = wl.rows
-    pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, args.pools)
-    bt = torch.from_numpy(wl.block_table).to(dev)
-    ctx = torch.from_numpy(wl.ctx).to(dev)
-    width = wl.width
-    logits = torch.empty((rows, width), dtype=torch.float32, device=dev)
-    row_len = torch.empty((rows,), dtype=torch.int32, device=dev)
-    row_req = torch.empty((rows,), dtype=torch.int32, device=dev)
-    idx = torch.empty((rows, 2048), dtype=torch.int32, device=dev)
-    slots = torch.empty((rows, 2048), dtype=torch.int32, device=dev)
-    ws_bytes = sai.topk_workspace_bytes(rows, width, 2048)
-    ws = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
+    prefill = wl.prefill
+    npools = 1 if prefill or args.config == 4 else args.pools
+    make = prefill_pipeline if prefill else decode_pipeline
+    t, launches, dom, work = make(torch, sai, lib, wl, dev, npools)
+    rows, width = wl.rows, wl.width
     torch.cuda.synchronize()
 
     stream = torch.cuda.current_stream()
     s_ptr = ctypes.c_void_p(stream.cuda_stream)
-    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
-    logit_args = [(P(q_fp8), P(w_eff), P(p), p.shape[0], P(bt), bt.stride(0), P(ctx), wl.batch, nn,
-                   P(logits), width, P(row_len), P(row_req), s_ptr) for p in pools]
-    topk_args = (P(logits), width, P(row_len), rows, 2048, P(idx), P(ws), ws_bytes, s_ptr)
-    slot_args = (P(idx), P(row_req), P(bt), bt.stride(0), wl.batch, rows, 2048, P(slots), s_ptr)
+    calls = launches(s_ptr)
 
     def step(i):
-        rc = lib.paged_mqa_logits(*logit_args[i % len(pools)])
-        rc |= lib.topk_rows(*topk_args)
-        rc |= lib.topk_to_global_slots(*slot_args)
+        rc = 0
+        for _, fn in calls:
+            rc |= fn(i)
         return rc
 
     ev = HipEvents()
@@ -219,38 +312,39 @@ def main():
     torch.cuda.synchronize()
 
     K = args.steps
-    e0, e1, e2 = ev.create(K), ev.create(K), ev.create(K)
+    e0, e1 = ev.create(K), ev.create(K)
     rec = ev.hip.hipEventRecord
-    plogits, ptopk, pslots = lib.paged_mqa_logits, lib.topk_rows, lib.topk_to_global_slots
+    before = [fn for _, fn in calls[:dom]]
+    dom_fn = calls[dom][1]
+    after = [fn for _, fn in calls[dom + 1:]]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
+        for fn in before:
+            fn(i)
         rec(e0[i], s_ptr)
-        plogits(*logit_args[i % len(pools)])
+        dom_fn(i)
         rec(e1[i], s_ptr)
-        ptopk(*topk_args)
-        pslots(*slot_args)
-        rec(e2[i], s_ptr)
+        for fn in after:
+            fn(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
-    t_logits = np.array([ev.elapsed_ms(e0[i], e1[i]) for i in range(K)])
-    t_rest = np.array([ev.elapsed_ms(e1[i], e2[i]) for i in range(K)])
-    ev.destroy(e0 + e1 + e2)
+    t_dom = np.array([ev.elapsed_ms(e0[i], e1[i]) for i in range(K)])
+    ev.destroy(e0 + e1)
 
     # hipGraph replay of the same step (reported alongside; not the headline value)
     graph_ms = None
     try:
         if args.no_graph:
             raise RuntimeError("disabled by --no-graph")
-        graphs = []
         side = torch.cuda.Stream()
-        for p in range(len(pools)):
+        gcalls = launches(ctypes.c_void_p(side.cuda_stream))
+        graphs = []
+        for p in range(npools):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=side):
-                sai.paged_mqa_logits(q_fp8.view(wl.batch, nn, 64, 128), w_eff, pools[p], bt, ctx,
-                                     width, logits=logits, row_len=row_len, row_req=row_req)
-                sai.topk_rows(logits, row_len, 2048, out=idx, workspace=ws if ws_bytes else None)
-                sai.topk_to_global_slots(idx, row_req, bt, out=slots)
+                for _, fn in gcalls:
+                    assert fn(p) == 0
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
@@ -271,28 +365,33 @@ def main():
         torch.cuda.synchronize()
         del src, dst
 
-    # algorithmic bytes and flops of one paged_mqa_logits launch
-    ctx_np = wl.ctx.astype(np.int64)
-    k_bytes = int(ctx_np.sum()) * K_BYTES_PER_TOKEN
-    other_bytes = rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
-    alg_bytes = k_bytes + other_bytes
-    lim = np.repeat(ctx_np, nn) - nn + np.tile(np.arange(nn), wl.batch) + 1
-    flops = float(np.clip(lim, 0, None).sum()) * 64 * 128 * 2
-    t_log_s = float(t_logits.mean()) * 1e-3
-    achieved = alg_bytes / t_log_s / 1e9
-    traffic = counter_traffic()
+    t_dom_s = float(t_dom.mean()) * 1e-3
+    dom_name = calls[dom][0]
+    if work["bound"] == "hbm":
+        achieved = work["alg_bytes"] / t_dom_s / 1e9
+        roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                "traffic": counter_traffic() if args.config == 1 else None}
+    else:
+        achieved = work["flops"] / t_dom_s / 1e12
+        roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+    roof.update({"kernel": dom_name, "alg_bytes_per_launch": work["alg_bytes"],
+                 "flops_per_launch": work["flops"], "avg_launch_us": round(t_dom_s * 1e6, 3)})
 
     ms_per_step = elapsed * 1e3 / K
     value = rows * K / elapsed
 
-    # parity of this run + oracle throughput on the host
-    gl = logits.cpu().numpy()
-    sample = list(range(min(args.cpu_sample, wl.batch)))
+    gl = t["logits"].cpu().numpy()
     cpu = None
     parity_ok = None
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not prefill:
+        sample = list(range(min(args.cpu_sample, wl.batch)))
         cpu, parity_ok = cpu_baseline(wl, sample, gl, args.cpu_seconds)
+    elif not args.no_cpu_baseline:
+        cpu, parity_ok = cpu_baseline_prefill(wl, gl, args.cpu_seconds)
 
+    ctx_np = wl.ctx.astype(np.int64)
     out = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -309,28 +408,19 @@ def main():
         "config": {
             "workload": wl.name,
             "batch": wl.batch,
-            "next_n": nn,
+            "next_n": wl.next_n,
+            "query_rows": rows,
             "context_tokens": int(ctx_np.sum()),
             "context_range": [int(ctx_np.min()), int(ctx_np.max())],
             "heads": 64, "head_dim": 128, "block_size": 64, "topk": 2048,
-            "pool_blocks": wl.num_blocks, "pool_copies_rotated": len(pools),
+            "pool_blocks": wl.num_blocks, "pool_copies_rotated": npools,
             "logits_width": width,
+            "step": [name for name, _ in calls],
         },
-        "roofline": {
-            "bound": "hbm",
-            "achieved": round(achieved, 1),
-            "peak": HBM_PEAK_GBPS,
-            "unit": "GB/s",
-            "frac": round(achieved / HBM_PEAK_GBPS, 4),
-            "traffic": traffic,
-            "kernel": "paged_mqa_logits",
-            "alg_bytes_per_launch": alg_bytes,
-            "avg_launch_us": round(t_log_s * 1e6, 3),
-        },
-        "k_stream_gbps": round(k_bytes / t_log_s / 1e9, 1),
-        "fp8_mfma_frac": round(flops / t_log_s / 1e12 / FP8_PEAK_TFLOPS, 4),
-        "topk_plus_slots_us": round(float(t_rest.mean()) * 1e3, 3),
-        "logits_us_p10_p50_p90": [round(float(np.percentile(t_logits, p)) * 1e3, 3) for p in (10, 50, 90)],
+        "roofline": roof,
+        "k_stream_gbps": round(work["k_bytes"] / t_dom_s / 1e9, 1),
+        "fp8_mfma_frac": round(work["flops"] / t_dom_s / 1e12 / FP8_PEAK_TFLOPS, 4),
+        "dominant_us_p10_p50_p90": [round(float(np.percentile(t_dom, p)) * 1e3, 3) for p in (10, 50, 90)],
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "parity_sampled_rows": parity_ok,
         "cpu_baseline": cpu,

@@ -94,6 +94,14 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _out(t, dtype, name, shape):
+    """Caller-provided outputs: the kernels write every element of ``shape``
+    (row pitch = the row length), so the tensor must be exactly that."""
+    _need(t, dtype, name)
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+
+
 # ---------------------------------------------------------------- calls
 def indexer_k_cache_write(k_bf16, slot_mapping, kv_cache):
     """Quantise K rows [n, 128] bf16 into the paged cache [num_blocks, 8448] u8 in place."""
@@ -123,9 +131,9 @@ def indexer_q_quant(q_bf16, weights, q_fp8=None, w_eff=None, q_scale=None):
     q_fp8 = torch.empty((T, HEADS, DIM), dtype=torch.uint8, device=dev) if q_fp8 is None else q_fp8
     w_eff = torch.empty((T, HEADS), dtype=torch.float32, device=dev) if w_eff is None else w_eff
     q_scale = torch.empty((T,), dtype=torch.float32, device=dev) if q_scale is None else q_scale
-    _need(q_fp8, torch.uint8, "q_fp8")
-    _need(w_eff, torch.float32, "w_eff")
-    _need(q_scale, torch.float32, "q_scale")
+    _out(q_fp8, torch.uint8, "q_fp8", (T, HEADS, DIM))
+    _out(w_eff, torch.float32, "w_eff", (T, HEADS))
+    _out(q_scale, torch.float32, "q_scale", (T,))
     _check(load().indexer_q_quant(_ptr(q_bf16), _ptr(weights), T, _ptr(q_fp8), _ptr(w_eff),
                                   _ptr(q_scale), _stream()), "indexer_q_quant")
     return q_fp8, w_eff, q_scale
@@ -142,8 +150,8 @@ def gather_indexer_k(kv_cache, block_table, cu_seq_lens, total_tokens, out_k=Non
     dev = kv_cache.device
     out_k = torch.empty((total_tokens, DIM), dtype=torch.uint8, device=dev) if out_k is None else out_k
     out_scale = torch.empty((total_tokens,), dtype=torch.float32, device=dev) if out_scale is None else out_scale
-    _need(out_k, torch.uint8, "out_k")
-    _need(out_scale, torch.float32, "out_scale")
+    _out(out_k, torch.uint8, "out_k", (total_tokens, DIM))
+    _out(out_scale, torch.float32, "out_scale", (total_tokens,))
     _check(load().gather_indexer_k(_ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
                                    block_table.stride(0), _ptr(cu_seq_lens), batch, total_tokens,
                                    _ptr(out_k), _ptr(out_scale), _stream()), "gather_indexer_k")
@@ -171,6 +179,9 @@ def paged_mqa_logits(q_fp8, weights, kv_cache, block_table, context_lens, width=
     logits = torch.empty((rows, width), dtype=torch.float32, device=dev) if logits is None else logits
     row_len = torch.empty((rows,), dtype=torch.int32, device=dev) if row_len is None else row_len
     row_req = torch.empty((rows,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    _out(logits, torch.float32, "logits", (rows, width))
+    _out(row_len, torch.int32, "row_len", (rows,))
+    _out(row_req, torch.int32, "row_req", (rows,))
     _check(load().paged_mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(kv_cache), kv_cache.shape[0],
                                    _ptr(block_table), block_table.stride(0), _ptr(context_lens),
                                    B, next_n, _ptr(logits), logits.stride(0), _ptr(row_len),
@@ -195,6 +206,9 @@ def mqa_logits(q_fp8, weights, k_fp8, k_scale, cu_seq_lens, width, logits=None, 
     logits = torch.empty((total, width), dtype=torch.float32, device=dev) if logits is None else logits
     row_len = torch.empty((total,), dtype=torch.int32, device=dev) if row_len is None else row_len
     row_req = torch.empty((total,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    _out(logits, torch.float32, "logits", (total, width))
+    _out(row_len, torch.int32, "row_len", (total,))
+    _out(row_req, torch.int32, "row_req", (total,))
     _check(load().mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(k_fp8), _ptr(k_scale),
                              _ptr(cu_seq_lens), batch, total, _ptr(logits), logits.stride(0),
                              _ptr(row_len), _ptr(row_req), _stream()), "mqa_logits")
@@ -214,7 +228,7 @@ def topk_rows(logits, row_len, k=TOPK_MAX, out=None, workspace=None):
         raise ValueError("row_len needs one entry per row")
     dev = logits.device
     out = torch.empty((rows, k), dtype=torch.int32, device=dev) if out is None else out
-    _need(out, torch.int32, "out")
+    _out(out, torch.int32, "out", (rows, k))
     ws_bytes = topk_workspace_bytes(rows, logits.stride(0), k)
     if ws_bytes and workspace is None:
         workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
@@ -231,7 +245,7 @@ def topk_to_global_slots(topk_idx, row_req, block_table, out=None):
     _need(block_table, torch.int32, "block_table", 2)
     rows, k = topk_idx.shape
     out = torch.empty_like(topk_idx) if out is None else out
-    _need(out, torch.int32, "out")
+    _out(out, torch.int32, "out", (rows, k))
     _check(load().topk_to_global_slots(_ptr(topk_idx), _ptr(row_req), _ptr(block_table),
                                        block_table.stride(0), block_table.shape[0], rows, k,
                                        _ptr(out), _stream()), "topk_to_global_slots")

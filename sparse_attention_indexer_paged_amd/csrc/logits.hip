@@ -36,15 +36,21 @@ using namespace sai;
 #ifndef SAI_DECODE_CAP
 #define SAI_DECODE_CAP 8
 #endif
+#ifndef SAI_DECODE_STAGE
+#define SAI_DECODE_STAGE 2048
+#endif
 
 namespace {
 
 // Decode launch shape: waves of the persistent grid (8 per CU), blocks in
 // the per-wave register ring (DEPTH-1 blocks in flight while one is scored),
-// and units whose results are held in registers before they are stored.
+// the most units scored per straight-line group, and the floats of each
+// wave's LDS result stage.
 constexpr int kDecodeWaves = SAI_DECODE_WAVES;
 constexpr int kDecodeDepth = SAI_DECODE_DEPTH;
 constexpr int kDecodeCap = SAI_DECODE_CAP;
+constexpr int kStageFloats = SAI_DECODE_STAGE;
+constexpr int kFillCols = 256;  // -inf fill piece: one float4 per lane
 
 // Masking by integer select on the bit patterns, so the choice is never an
 // fp operation the no-NaN compile mode may reason about.
@@ -63,6 +69,15 @@ __device__ __forceinline__ void store_logit(float* p, float v) {
   __builtin_nontemporal_store(v, p);
 #else
   *p = v;
+#endif
+}
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store_logit4(float* p, float4 v) {
+  const f32x4 x = {v.x, v.y, v.z, v.w};
+#if SAI_NT_STORE
+  __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+#else
+  *reinterpret_cast<f32x4*>(p) = x;
 #endif
 }
 constexpr uint32_t kNaNBits = 0x7FC00000u;
@@ -100,6 +115,22 @@ __device__ __forceinline__ void load_kfrag_paged(KFrag& f, const uint8_t* __rest
     f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(row + 64);
   }
   f.s = *reinterpret_cast<const float*>(blk + kValueBytes + 4 * lane);
+}
+
+// Loads of one paged block in operand order, or -- when !real -- the same
+// number of loads all aimed at the first 16 bytes of `dummy`, so every path
+// issues an identical instruction stream (the data is then ignored).
+__device__ __forceinline__ void load_kfrag_or_dummy(KFrag& f, const uint8_t* __restrict__ blk,
+                                                    const uint8_t* __restrict__ dummy, bool real) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const uint8_t* base = real ? blk : dummy;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int off = real ? (tile_key(t) + n) * kDim + 16 * g : 0;
+    f.v[2 * t] = *reinterpret_cast<const uint4*>(base + off);
+    f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(base + off + (real ? 64 : 0));
+  }
+  f.s = *reinterpret_cast<const float*>(base + (real ? kValueBytes + 4 * lane : 0));
 }
 
 // Contiguous K: keys [key0, key0+64) of `k` ([*,128] codes) and `ks`; keys at
@@ -189,31 +220,88 @@ __device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], 
 __device__ __forceinline__ int cdiv_i(int a, int b) { return (a + b - 1) / b; }
 
 // ------------------------------------------------------------------ decode
+// Scores NS consecutive key blocks of one request (block ids in lanes
+// 0..NS-1 of myblk) for its NN query rows and writes the masked logits of
+// block i, row r to st[(r * slots + i) * 64 + lane] in LDS.  NS is a
+// compile-time count, so the ring below is straight-line code: every slot
+// issues the same loads on every path (an invalid block id re-reads one
+// 16-byte word of q instead), which lets the in-order vmcnt accounting
+// leave the DEPTH-1 prefetched blocks in flight while one is scored.  No
+// global store sits in the loop, so no K load ever queues behind one.
+template <int NN, int DEPTH, int NS>
+__device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, int64_t num_blocks,
+                                            const uint8_t* __restrict__ dummy, int myblk,
+                                            const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
+                                            int ctx, float* st, int slots) {
+  const int lane = threadIdx.x & 63;
+  KFrag buf[DEPTH];
+  bool okb[DEPTH];
+  auto issue = [&](int i) {
+    const int32_t blk = __builtin_amdgcn_readlane(myblk, i);
+    const bool ok = blk >= 0 && blk < num_blocks;
+    okb[i % DEPTH] = ok;
+    load_kfrag_or_dummy(buf[i % DEPTH], cache + (int64_t)(ok ? blk : 0) * kBlockBytes, dummy, ok);
+    // keep the prefetch where it is: the scheduler would otherwise sink
+    // these loads down to their use
+    __builtin_amdgcn_sched_barrier(0);
+  };
+#pragma unroll
+  for (int i = 0; i < DEPTH - 1 && i < NS; ++i) issue(i);
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    if (i + DEPTH - 1 < NS) issue(i + DEPTH - 1);
+    const KFrag& cur = buf[i % DEPTH];
+    const int col = (c0 + i) * kBlock + lane;
+#pragma unroll
+    for (int r = 0; r < NN; ++r) {
+      const float sc = score_row(cur, qa[r], wf[r]);
+      const float v = select_f(okb[i % DEPTH], sc * cur.s, kNaNBits);
+      st[(r * slots + i) * kBlock + lane] = select_f(col < ctx - NN + r + 1, v, kNegInfBits);
+    }
+  }
+}
+
+// Calls score_group with NS == n (1 <= n <= NS; n is wave-uniform).
+template <int NN, int DEPTH, int NS>
+__device__ __forceinline__ void dispatch_group(int n, const uint8_t* __restrict__ cache, int64_t num_blocks,
+                                               const uint8_t* __restrict__ dummy, int myblk,
+                                               const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
+                                               int ctx, float* st, int slots) {
+  if (n == NS || NS == 1) {
+    score_group<NN, DEPTH, NS>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots);
+  } else if constexpr (NS > 1) {
+    dispatch_group<NN, DEPTH, NS - 1>(n, cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots);
+  }
+}
+
 // Grid of persistent waves, each with an equal share of the work: units
 // (b, c) = key block c of request b are flattened in (b, c) order and wave w
-// of NW scores units [w*U/NW, (w+1)*U/NW); the -inf fill of column blocks
-// past each request's last key block is flattened and split the same way.
-// Each workgroup builds the two prefix sums over the requests' block counts
-// in LDS from the device-side context lengths (no host sync).  A wave first
-// issues its query rows, then keeps DEPTH-1 K blocks in flight while it
-// scores one, and stores results in groups of CAP units after the group's
-// loads have been issued.
+// of NW scores units [w*U/NW, (w+1)*U/NW); the -inf fill of the columns past
+// each request's last key block is cut into pieces of kFillCols columns,
+// flattened and split the same way.  Each workgroup builds the two prefix
+// sums over the requests in LDS from the device-side context lengths (no
+// host sync).  A wave walks its units in groups of at most CAP blocks of one
+// request, stages the logits in its LDS slice and writes them out as
+// contiguous row runs (float4 per lane when rows are 16-byte aligned) once
+// its units are done or the slice is full.
 template <int NN, int DEPTH, int CAP>
 __global__ __launch_bounds__(256) void paged_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ bt, int64_t bt_stride,
     const int32_t* __restrict__ ctx_lens, int32_t batch, float* __restrict__ logits,
-    int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out) {
-  static_assert(CAP % DEPTH == 0, "ring slots must repeat within a store group");
-  extern __shared__ int smem[];
-  int* s_unit = smem;                   // [batch+1] prefix of key blocks
-  int* s_fill = smem + (batch + 1);     // [batch+1] prefix of fill column blocks
-  int* s_ctx = smem + 2 * (batch + 1);  // [batch] clamped context
-  int* s_tot = smem + 3 * (batch + 1);  // [8] per-wave totals
-
+    int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out, bool vec) {
+  constexpr int kSlots = kStageFloats / (kBlock * NN);  // staged units per wave
+  constexpr int kCap = CAP < kSlots ? CAP : kSlots;      // a group fits the stage
+  static_assert(kCap >= 1, "stage too small");
+  extern __shared__ float4 smem4[];
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+  float* stage = reinterpret_cast<float*>(smem4) + wid * kStageFloats;
+  int* s_unit = reinterpret_cast<int*>(reinterpret_cast<float*>(smem4) + 4 * kStageFloats);
+  int* s_fill = s_unit + (batch + 1);     // [batch+1] prefix of fill pieces
+  int* s_ctx = s_unit + 2 * (batch + 1);  // [batch] clamped context
+  int* s_tot = s_unit + 3 * (batch + 1);  // [8] per-wave totals
+
   const int maxc = (int)min64(stride, bt_stride * kBlock);
-  const int wblocks = (int)((stride + kBlock - 1) / kBlock);
 
   int run_u = 0, run_f = 0;
   for (int base = 0; base < batch; base += 256) {
@@ -223,7 +311,7 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       const int c = min(max(ctx_lens[bb], 0), maxc);
       s_ctx[bb] = c;
       nu = cdiv_i(c, kBlock);
-      nf = wblocks - nu;
+      nf = (int)((max(stride - (int64_t)nu * kBlock, (int64_t)0) + kFillCols - 1) / kFillCols);
     }
     const int iu = wave_inclusive_scan(nu), jf = wave_inclusive_scan(nf);
     if (lane == 63) {
@@ -270,92 +358,68 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     return lo;
   };
 
+  // Writes the staged units [sa, sb) (stage slots 0 .. sb-sa-1; unit sa
+  // belongs to request bs) to their rows: per request, each row's run of
+  // columns is contiguous in LDS and in the logits.
+  auto flush = [&](int sa, int sb, int bs) {
+    // the stage was written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    for (int u = sa; u < sb;) {
+      while (s_unit[bs + 1] <= u) ++bs;
+      const int e = min(sb, s_unit[bs + 1]);
+      const int64_t col0 = (int64_t)(u - s_unit[bs]) * kBlock;
+      const int ncol = (int)min64((int64_t)(e - u) * kBlock, stride - col0);
+#pragma unroll
+      for (int r = 0; r < NN; ++r) {
+        const float* src = stage + (r * kSlots + (u - sa)) * kBlock;
+        float* dst = logits + ((int64_t)bs * NN + r) * stride + col0;
+        if (vec) {
+          for (int x = 4 * lane; x < ncol; x += 256)
+            store_logit4(dst + x, *reinterpret_cast<const float4*>(src + x));
+        } else {
+          for (int x = lane; x < ncol; x += 64) store_logit(dst + x, src[x]);
+        }
+      }
+      u = e;
+    }
+  };
+
   const int U = s_unit[batch];
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
-  if (u0 < u1) {
-    int u_ld = u0;                        // load frontier
-    int b_cp = find(s_unit, u0), u_cp = u0;  // scoring position
-    int qb = b_cp;
-    // Block ids of the wave's next 64 units, one per lane, fetched with one
-    // vector load so the ring never waits on a block-table read per unit.
-    int t_blk = -1, win0 = u0;
-    auto fill_table = [&](int first) {
-      const int u = first + lane;
-      int blk = -1;
-      if (u < u1) {
-        const int b = find(s_unit, u);
-        blk = bt[(int64_t)b * bt_stride + (u - s_unit[b])];
-      }
-      t_blk = blk;
-      win0 = first;
-    };
-    fill_table(u0);
-    v8i qa[NN][4];
-    float4 wf[NN][4];
-#pragma unroll
-    for (int r = 0; r < NN; ++r) {
-      load_qfrag(qa[r], q + ((int64_t)qb * NN + r) * (kHeads * kDim));
-      load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
+  // Per group: the block ids come in with one vector load (lane i holds
+  // unit i), the query rows are (re)loaded only when the request changes,
+  // then a ring of exactly n slots scores the group into the stage.
+  int u = u0;
+  int b = u0 < u1 ? find(s_unit, u0) : 0;
+  int sa = u0, bs = b;  // first staged unit and its request
+  int qb = -1;
+  v8i qa[NN][4];
+  float4 wf[NN][4];
+  while (u < u1) {
+    while (s_unit[b + 1] <= u) ++b;
+    const int n = min(kCap, min(u1, s_unit[b + 1]) - u);  // 1..kCap units of request b
+    if (u + n - sa > kSlots) {
+      flush(sa, u, bs);
+      sa = u;
+      bs = b;
     }
-    KFrag buf[DEPTH];
-    bool okb[DEPTH];
-    auto issue = [&](KFrag& f, bool& ok) {
-      if (u_ld - win0 >= 64) fill_table(u_ld);
-      const int32_t blk = __builtin_amdgcn_readlane(t_blk, u_ld - win0);
-      ok = blk >= 0 && blk < num_blocks;
-      if (ok) load_kfrag_paged(f, cache + (int64_t)blk * kBlockBytes); else zero_kfrag(f);
-      ++u_ld;
-    };
+    const int c0 = u - s_unit[b];
+    const int myblk = lane < n ? bt[(int64_t)b * bt_stride + c0 + lane] : -1;
+    if (b != qb) {
+      qb = b;
 #pragma unroll
-    for (int i = 0; i < DEPTH - 1; ++i)
-      if (u_ld < u1) issue(buf[i], okb[i]);
-
-    float res[CAP][NN];
-    int64_t roff[CAP];  // offset of the unit's first row
-    int ccol[CAP];      // first column of the unit's block
-    while (u_cp < u1) {
-      int used = 0;
-#pragma unroll
-      for (int sl = 0; sl < CAP; ++sl) {
-        if (u_cp >= u1) break;
-        if (DEPTH > 1 && u_ld < u1) issue(buf[(sl + DEPTH - 1) % DEPTH], okb[(sl + DEPTH - 1) % DEPTH]);
-        if (DEPTH == 1) issue(buf[0], okb[0]);
-        if (b_cp != qb) {
-          qb = b_cp;
-#pragma unroll
-          for (int r = 0; r < NN; ++r) {
-            load_qfrag(qa[r], q + ((int64_t)qb * NN + r) * (kHeads * kDim));
-            load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
-          }
-        }
-        const KFrag& cur = buf[sl % DEPTH];
-        const int c = u_cp - s_unit[b_cp];
-        const int col = c * kBlock + lane;
-        const int ctx = s_ctx[b_cp];
-#pragma unroll
-        for (int r = 0; r < NN; ++r) {
-          const float sc = score_row(cur, qa[r], wf[r]);
-          const float v = select_f(okb[sl % DEPTH], sc * cur.s, kNaNBits);
-          res[sl][r] = select_f(col < ctx - NN + r + 1, v, kNegInfBits);
-        }
-        roff[sl] = (int64_t)b_cp * NN * stride;
-        ccol[sl] = c * kBlock;
-        used = sl + 1;
-        ++u_cp;
-        if (u_cp < u1) while (s_unit[b_cp + 1] <= u_cp) ++b_cp;
-      }
-#pragma unroll
-      for (int sl = 0; sl < CAP; ++sl) {
-        if (sl >= used) break;
-        const int col = ccol[sl] + lane;
-        if (col < stride) {
-#pragma unroll
-          for (int r = 0; r < NN; ++r) store_logit(logits + roff[sl] + (int64_t)r * stride + col, res[sl][r]);
-        }
+      for (int r = 0; r < NN; ++r) {
+        load_qfrag(qa[r], q + ((int64_t)qb * NN + r) * (kHeads * kDim));
+        load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
       }
     }
+    dispatch_group<NN, DEPTH, kCap>(n, cache, num_blocks, q, myblk, qa, wf, c0, s_ctx[b],
+                                    stage + (u - sa) * kBlock, kSlots);
+    u += n;
   }
+  if (sa < u1) flush(sa, u1, bs);
 
   const int F = s_fill[batch];
   int f = (int)((int64_t)F * w / nw);
@@ -363,31 +427,96 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   if (f < f1) {
     int b = find(s_fill, f);
     const float ninf = __uint_as_float(kNegInfBits);
+    const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
     for (; f < f1; ++f) {
       while (s_fill[b + 1] <= f) ++b;
-      const int cb = (s_unit[b + 1] - s_unit[b]) + (f - s_fill[b]);
-      const int col = cb * kBlock + lane;
-      if (col < stride) {
+      const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
 #pragma unroll
-        for (int r = 0; r < NN; ++r) store_logit(logits + ((int64_t)b * NN + r) * stride + col, ninf);
+      for (int r = 0; r < NN; ++r) {
+        float* row = logits + ((int64_t)b * NN + r) * stride;
+        if (vec) {
+          if (col + 4 * lane < stride) store_logit4(row + col + 4 * lane, ninf4);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kFillCols / 64; ++k)
+            if (col + 64 * k + lane < stride) store_logit(row + col + 64 * k + lane, ninf);
+        }
       }
     }
   }
 }
 
 // ------------------------------------------------------------------ prefill
-// Workgroup = (query tile of 16 consecutive tokens of one request, key chunk
-// of kChunk columns).  Its 4 waves take 4 rows each, hold their Q operands in
-// VGPRs and stream the chunk's K blocks (the 4 waves read the same blocks,
-// so 3 of 4 reads hit the CU's L1); every column of the chunk is written for
-// the tile's rows (-inf past each row's causal limit).  Grid ids are ordered
-// tile-major and remapped so that the chunks of one tile run on one XCD and
-// share its Q in that XCD's L2.
-constexpr int kRowsPerWave = 4;
-constexpr int kTileRows = 16;
-constexpr int kChunk = 1024;
+// Prefill is fp8-MFMA / VALU co-bound (every key is reused by all later
+// tokens), so K is staged once per workgroup in LDS and shared by its waves.
+// Workgroup = 8 consecutive tokens of one request (4 waves x 2 query rows,
+// Q in VGPRs) x a key chunk of 16 blocks (1024 columns).  The chunk's K
+// blocks stream through a double-buffered LDS image: all 256 threads fetch
+// the next block with coalesced 16-byte loads while the current one is
+// scored, then write it to LDS with the 16-byte chunk c of key n at position
+// c ^ (n & 7) of the key's row, so the MFMA operand reads (lanes n = 0..15 of
+// one key tile at a 128-byte stride) spread over all LDS banks.  Every
+// column of the chunk is written for the tile's rows (-inf past each row's
+// causal limit).  Grid ids are ordered tile-major and remapped so the chunks
+// of one tile run on one XCD and share its Q in that XCD's L2.
+#ifndef SAI_PF_ROWS
+#define SAI_PF_ROWS 2
+#endif
+#ifndef SAI_PF_WAVES_PER_EU
+#define SAI_PF_WAVES_PER_EU 0
+#endif
+constexpr int kPfRowsPerWave = SAI_PF_ROWS;
+constexpr int kPfTileRows = 4 * kPfRowsPerWave;
+constexpr int kPfChunkBlocks = 16;
+constexpr int kChunk = kPfChunkBlocks * kBlock;
 
-__global__ __launch_bounds__(256) void prefill_logits_kernel(
+struct PfBlock {
+  uint4 code[kBlock * 8];  // 64 keys x 8 chunks of 16 bytes, swizzled
+  float scale[kBlock];
+};
+
+__device__ __forceinline__ int pf_swz(int n, int c) { return n * 8 + (c ^ (n & 7)); }
+
+// Global -> registers: thread t fetches chunks t and t+256 of the block
+// (key = chunk / 8, 16-byte column = chunk % 8) and, for t < 64, key t's
+// scale.  Keys at or past nvalid read as zero.
+__device__ __forceinline__ void pf_fetch(uint4 (&r)[2], float& sc, const uint8_t* __restrict__ k,
+                                         const float* __restrict__ ks, int64_t key0, int nvalid) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int chunk = t + 256 * e;
+    const int n = chunk >> 3, c = chunk & 7;
+    r[e] = n < nvalid ? *reinterpret_cast<const uint4*>(k + (key0 + n) * kDim + c * 16)
+                      : make_uint4(0, 0, 0, 0);
+  }
+  sc = (t < kBlock && t < nvalid) ? ks[key0 + t] : 0.0f;
+}
+
+__device__ __forceinline__ void pf_store(PfBlock& blk, const uint4 (&r)[2], float sc) {
+  const int t = threadIdx.x;
+#pragma unroll
+  for (int e = 0; e < 2; ++e) {
+    const int chunk = t + 256 * e;
+    blk.code[pf_swz(chunk >> 3, chunk & 7)] = r[e];
+  }
+  if (t < kBlock) blk.scale[t] = sc;
+}
+
+// B operand of key tile t: lane (g, n) takes 16-byte columns g and 4+g of key
+// tile_key(t)+n, the same contraction order as the paged decode loads.
+__device__ __forceinline__ v8i pf_operand(const PfBlock& blk, int t) {
+  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
+  const int key = tile_key(t) + n;
+  return make_v8i(blk.code[pf_swz(key, g)], blk.code[pf_swz(key, 4 + g)]);
+}
+
+#if SAI_PF_WAVES_PER_EU
+#define SAI_PF_ATTR __attribute__((amdgpu_waves_per_eu(SAI_PF_WAVES_PER_EU)))
+#else
+#define SAI_PF_ATTR
+#endif
+__global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
     float* __restrict__ logits, int64_t stride, int32_t* __restrict__ row_len_out,
@@ -395,7 +524,8 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
   extern __shared__ int smem[];
   int* s_tile = smem;                  // [batch+1] prefix of query tiles
   int* scratch = smem + (batch + 1);
-  __shared__ float4 s_w[kTileRows][16];
+  __shared__ PfBlock s_k[2];
+  __shared__ float4 s_w[kPfTileRows][16];
 
   int run = 0;
   for (int base = 0; base < batch; base += 256) {
@@ -403,7 +533,7 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
     int nt = 0;
     if (b < batch) {
       const int len = max(cu[b + 1] - cu[b], 0);
-      nt = cdiv_i(len, kTileRows);
+      nt = cdiv_i(len, kPfTileRows);
     }
     int tot;
     const int e = block_exclusive_scan<256>(nt, scratch, &tot);
@@ -425,22 +555,21 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
   const int b = lo;
   const int64_t base_tok = cu[b];
   const int len = (int)min64(max(cu[b + 1] - cu[b], 0), stride);
-  const int i0 = (tile - s_tile[b]) * kTileRows;
+  const int i0 = (tile - s_tile[b]) * kPfTileRows;
+  if (i0 >= len) return;  // the whole tile lies past a clamped request
 
-  // head weights of the tile's rows, in LDS
-  {
+  if (threadIdx.x < kPfTileRows * 16) {
     const int r = threadIdx.x >> 4, h4 = threadIdx.x & 15;
     float4 w = make_float4(0, 0, 0, 0);
     if (i0 + r < len) w = *reinterpret_cast<const float4*>(wts + (base_tok + i0 + r) * kHeads + 4 * h4);
     s_w[r][h4] = w;
   }
-  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
-  const int ir0 = i0 + wave * kRowsPerWave;  // first request-local row of this wave
-  const int nrows = max(0, min(kRowsPerWave, len - ir0));
-  if (nrows == 0) return;
+  const int ir0 = i0 + wave * kPfRowsPerWave;            // first request-local row of this wave
+  const int nrows = max(0, min(kPfRowsPerWave, len - ir0));
+  const int wlim = ir0 + nrows;                          // keys visible to the wave's last row
 
   if (chunk == 0 && lane < nrows) {
     if (row_len_out) row_len_out[base_tok + ir0 + lane] = ir0 + lane + 1;
@@ -449,13 +578,13 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
 
   const int col0 = chunk * kChunk;
   const int col_end = (int)min64((int64_t)col0 + kChunk, stride);
-  const int maxlim = ir0 + nrows;  // keys visible to the wave's last row
-  const int kend = min(col_end, maxlim);
+  const int kend = min(col_end, min(i0 + kPfTileRows, len));  // keys any row of the tile sees
   const int nblk = kend > col0 ? cdiv_i(kend - col0, kBlock) : 0;
+  const float ninf = __uint_as_float(kNegInfBits);
 
-  v8i qa[kRowsPerWave][4];
+  v8i qa[kPfRowsPerWave][4];
 #pragma unroll
-  for (int r = 0; r < kRowsPerWave; ++r) {
+  for (int r = 0; r < kPfRowsPerWave; ++r) {
     if (r < nrows && nblk > 0) {
       load_qfrag(qa[r], q + (base_tok + ir0 + r) * (kHeads * kDim));
     } else {
@@ -464,36 +593,61 @@ __global__ __launch_bounds__(256) void prefill_logits_kernel(
     }
   }
 
-  KFrag fa, fb;
-  int c = 0;
-  if (nblk > 0) load_kfrag_contig(fa, k, ks, base_tok + col0, len - col0);
-  auto step = [&](KFrag& cur, KFrag& nxt) -> bool {
-    const int key0 = col0 + c * kBlock;
-    if (c + 1 < nblk) load_kfrag_contig(nxt, k, ks, base_tok + key0 + kBlock, len - key0 - kBlock);
-    const int col = key0 + lane;
+  __syncthreads();  // s_w
+  float4 wf[kPfRowsPerWave][4];
 #pragma unroll
-    for (int r = 0; r < kRowsPerWave; ++r) {
-      if (r < nrows) {
-        const int wr = wave * kRowsPerWave + r;
-        const float4 wf[4] = {s_w[wr][4 * 0 + (lane >> 4)], s_w[wr][4 * 1 + (lane >> 4)],
-                              s_w[wr][4 * 2 + (lane >> 4)], s_w[wr][4 * 3 + (lane >> 4)]};
-        const float sc = score_row(cur, qa[r], wf);
-        const int limit = ir0 + r + 1;
-        const float v = select_f(col < limit, sc * cur.s, kNegInfBits);
-        if (col < col_end) logits[(base_tok + ir0 + r) * stride + col] = v;
-      }
-    }
-    ++c;
-    return c < nblk;
-  };
+  for (int r = 0; r < kPfRowsPerWave; ++r)
+#pragma unroll
+    for (int hg = 0; hg < 4; ++hg) wf[r][hg] = s_w[wave * kPfRowsPerWave + r][4 * hg + (lane >> 4)];
+
+  uint4 stage[2];
+  float stage_s;
   if (nblk > 0) {
-    while (step(fa, fb) && step(fb, fa)) {
-    }
+    pf_fetch(stage, stage_s, k, ks, base_tok + col0, len - col0);
+    pf_store(s_k[0], stage, stage_s);
   }
-  // -inf for the chunk's columns past the computed blocks
-  const float ninf = __uint_as_float(kNegInfBits);
+  __syncthreads();
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  for (int j = 0; j < nblk; ++j) {
+    const int key0 = col0 + j * kBlock;
+    if (j + 1 < nblk) pf_fetch(stage, stage_s, k, ks, base_tok + key0 + kBlock, len - key0 - kBlock);
+    const PfBlock& cur = s_k[j & 1];
+    const int col = key0 + lane;
+    if (key0 < wlim) {
+      float p[kPfRowsPerWave][4];
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        const v8i bop = pf_operand(cur, t);
+#pragma unroll
+        for (int r = 0; r < kPfRowsPerWave; ++r) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int hg = 0; hg < 4; ++hg) {
+            const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[r][hg], bop, zero, 0, 0, 0, 0, 0, 0);
+            acc = relu_dot4(wf[r][hg], c, acc);
+          }
+          p[r][t] = acc;
+        }
+      }
+      const float sc = cur.scale[lane];
+#pragma unroll
+      for (int r = 0; r < kPfRowsPerWave; ++r) {
+        if (r < nrows) {
+          const float v = reduce_scatter4(p[r][0], p[r][1], p[r][2], p[r][3]) * sc;
+          if (col < col_end)
+            store_logit(logits + (base_tok + ir0 + r) * stride + col,
+                        select_f(col < ir0 + r + 1, v, kNegInfBits));
+        }
+      }
+    } else if (col < col_end) {
+      for (int r = 0; r < nrows; ++r) store_logit(logits + (base_tok + ir0 + r) * stride + col, ninf);
+    }
+    if (j + 1 < nblk) pf_store(s_k[(j + 1) & 1], stage, stage_s);
+    __syncthreads();
+  }
+  // -inf for the chunk's columns past the staged blocks
   for (int col = col0 + nblk * kBlock + lane; col < col_end; col += 64) {
-    for (int r = 0; r < nrows; ++r) logits[(base_tok + ir0 + r) * stride + col] = ninf;
+    for (int r = 0; r < nrows; ++r) store_logit(logits + (base_tok + ir0 + r) * stride + col, ninf);
   }
 }
 
@@ -507,10 +661,18 @@ int launch_paged(const void* q, const float* w, const void* cache, int64_t num_b
   const int64_t waves = std::min<int64_t>(kDecodeWaves, std::max<int64_t>(units_max, 1));
   int64_t G = (waves + 3) / 4;
   G = (G + 7) / 8 * 8;
-  const size_t lds = (size_t)(3 * (batch + 1) + 8) * sizeof(int);
+  const size_t lds = 4 * kStageFloats * sizeof(float) + (size_t)(3 * (batch + 1) + 8) * sizeof(int);
+  if (lds > 65536) {  // large batches need the device's full per-workgroup LDS
+    int dev = 0, max_lds = 0;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&max_lds, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+      return SAI_ELAUNCH;
+    if (lds > (size_t)max_lds) return SAI_EUNSUPPORTED;
+  }
+  const bool vec = stride % 4 == 0 && aligned16(logits);
   hipLaunchKernelGGL((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap>), dim3((unsigned)G),
                      dim3(256), lds, s, (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt,
-                     bt_stride, ctx, batch, logits, stride, rl, rr);
+                     bt_stride, ctx, batch, logits, stride, rl, rr, vec);
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
 
@@ -549,7 +711,7 @@ extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k
   if (!aligned16(q_fp8) || !aligned16(weights) || !aligned16(k_fp8)) return SAI_EINVAL;
   if (batch > 4096 || logits_stride > 0x7FFFFFFF - kChunk) return SAI_EUNSUPPORTED;
   const int64_t nchunks = (logits_stride + kChunk - 1) / kChunk;
-  const int64_t ntiles = (total_tokens + kTileRows - 1) / kTileRows + batch;
+  const int64_t ntiles = (total_tokens + kPfTileRows - 1) / kPfTileRows + batch;
   int64_t G = nchunks * ntiles;
   G = (G + 7) / 8 * 8;
   if (G > 0x7FFFFFFF) return SAI_EUNSUPPORTED;

@@ -119,6 +119,53 @@ def test_paged_logits_width_not_multiple_of_64_and_empty_request():
     assert row_len.cpu().tolist() == [900, 0, 257]
 
 
+@pytest.mark.parametrize("width,offset", [(1001, 0), (1000, 1)])
+def test_paged_logits_unaligned_rows(width, offset):
+    """Rows that are not 16-byte aligned (an odd row pitch, or a base pointer
+    4 bytes off) are written one float per lane instead of four."""
+    _say(f"paged_mqa_logits: row pitch {width}, base offset {offset} floats")
+    wl = synth.custom(3, 2, [700, 997, 2], num_blocks=40, bt_width=16, seed=11)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    buf = torch.full((6 * width + offset,), 7.0, device=DEV)
+    logits = buf[offset:].view(6, width)
+    sai.paged_mqa_logits(g.q_fp8.view(3, 2, 64, 128), g.w_eff, g.pool, g.block_table, g.ctx,
+                         width=width, logits=logits)
+    ref = O.paged_mqa_logits(o.q_codes.reshape(3, 2, 64, 128), o.w_eff, o.pool, wl.block_table,
+                             wl.ctx, 2, width)
+    assert_logits_close(logits.cpu().numpy(), ref, f"pitch{width}+{offset}")
+    if offset:
+        assert buf[0].item() == 7.0
+
+
+def test_paged_logits_more_units_per_wave_than_stage():
+    """next_n 4 over 16 long requests: each persistent wave scores about 12
+    key blocks but stages at most 8 in LDS, so every wave writes out its
+    results part-way through its share."""
+    ctx = [98304 - 37 * i for i in range(16)]
+    _say("paged_mqa_logits: 16 x ~98K keys, next_n=4")
+    wl = synth.custom(16, 4, ctx, num_blocks=16 * 1536 + 8, bt_width=1536, seed=12)
+    rows = [0, 3, 17, 30, 45, 62, 63]
+    _check_decode(wl, requests=sorted({r // 4 for r in rows}), rows=rows)
+
+
+def test_paged_logits_largest_batch():
+    """4096 requests (the most the decode launch takes): the per-request
+    prefix sums push the workgroup's LDS above 64 KB."""
+    _say("paged_mqa_logits: batch 4096")
+    rng = np.random.default_rng(13)
+    ctx = rng.integers(1, 200, size=4096).tolist()
+    wl = synth.custom(4096, 1, ctx, num_blocks=4096 * 4 + 8, bt_width=4, seed=13)
+    props = torch.cuda.get_device_properties(0)
+    lds = 4 * 2048 * 4 + (3 * 4097 + 8) * 4
+    if getattr(props, "shared_memory_per_block", 1 << 30) < lds:
+        with pytest.raises(RuntimeError, match="unsupported"):
+            _check_decode(wl, requests=[0], rows=[0])
+        return
+    rows = [0, 1, 777, 2048, 4095]
+    _check_decode(wl, requests=rows, rows=rows)
+
+
 def test_paged_logits_deterministic_and_permutation_invariant():
     _say("paged_mqa_logits: determinism + block permutation")
     wl = synth.custom(4, 2, [1000, 333, 64, 2000], num_blocks=80, bt_width=40, seed=9)
