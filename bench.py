@@ -162,6 +162,8 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
              row_req=torch.empty((rows,), dtype=torch.int32, device=dev),
              idx=torch.empty((rows, 2048), dtype=torch.int32, device=dev),
              slots=torch.empty((rows, 2048), dtype=torch.int32, device=dev))
+    ws_bytes = int(lib.topk_workspace_bytes(rows, width, 2048))
+    t["ws"] = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
 
     def launches(s):
@@ -170,7 +172,7 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
                 P(q_fp8), P(w_eff), P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0),
                 P(ctx), wl.batch, nn, P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), s)),
             ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
-                                                  P(t["idx"]), None, 0, s)),
+                                                  P(t["idx"]), P(t["ws"]), ws_bytes, s)),
             ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
                 P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
                 P(t["slots"]), s)),
@@ -197,6 +199,8 @@ def prefill_pipeline(torch, sai, lib, wl, dev, npools):
              row_req=torch.empty((rows,), dtype=torch.int32, device=dev),
              idx=torch.empty((rows, 2048), dtype=torch.int32, device=dev),
              slots=torch.empty((rows, 2048), dtype=torch.int32, device=dev))
+    ws_bytes = int(lib.topk_workspace_bytes(rows, width, 2048))
+    t["ws"] = torch.empty((max(ws_bytes, 1),), dtype=torch.uint8, device=dev)
     P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
 
     def launches(s):
@@ -208,7 +212,7 @@ def prefill_pipeline(torch, sai, lib, wl, dev, npools):
                 P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu), wl.batch, total, P(t["logits"]),
                 width, P(t["row_len"]), P(t["row_req"]), s)),
             ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
-                                                  P(t["idx"]), None, 0, s)),
+                                                  P(t["idx"]), P(t["ws"]), ws_bytes, s)),
             ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
                 P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
                 P(t["slots"]), s)),

@@ -190,7 +190,11 @@ int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
  *   out_idx  [rows, k] int32 (output)
  *   workspace / workspace_bytes: scratch of at least
  *   topk_workspace_bytes(rows, logits_stride, k) bytes (may be NULL if that
- *   is 0); contents need no initialisation.
+ *   is 0); contents need no initialisation.  Rows wider than 16384 columns
+ *   are cut into 16384-column segments whose k winners (key and column) go
+ *   to the workspace, 8 * rows * segments * k bytes, and are then merged;
+ *   rows too wide for the merge (segments * k > 16384) need none.  A
+ *   missing or short workspace returns SAI_EWORKSPACE and launches nothing.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,

@@ -460,7 +460,7 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
 // causal limit).  Grid ids are ordered tile-major and remapped so the chunks
 // of one tile run on one XCD and share its Q in that XCD's L2.
 #ifndef SAI_PF_ROWS
-#define SAI_PF_ROWS 2
+#define SAI_PF_ROWS 1
 #endif
 #ifndef SAI_PF_WAVES_PER_EU
 #define SAI_PF_WAVES_PER_EU 0

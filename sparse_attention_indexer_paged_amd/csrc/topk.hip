@@ -2,25 +2,24 @@
 // Details: the sparse top-k over each query's request-local keys, handed on
 // in a 2-D [rows, k] index buffer).
 //
-// Selection is exact radix select on 32-bit order-preserving keys
-// (f32_order_key: larger logit -> larger key, -0.0 folded onto +0.0):
-//   digit 1 = key bits 31..21 (2048 bins), digit 2 = bits 20..10 (2048),
-//   digit 3 = bits 9..0 (1024).
-// Each round histograms, in LDS, the keys whose higher digits equal the
-// prefix fixed so far, then one pass over the bins (a workgroup scan from
-// the top bin down) picks the bin holding the k-th largest key.  After three
-// rounds the k-th largest key T is known exactly, with `gt` keys above it and
-// need = k - gt of the keys equal to T to be taken, lowest indices first.
-// The output pass walks the row in ascending index order; a workgroup scan
-// of per-thread (above-T, equal-to-T) counts gives every winner its output
-// slot, so indices come out sorted with no sort.
-// Rows whose visible length is at most k skip all of this and emit 0..n-1.
+// Selection is exact, on 32-bit order-preserving keys (f32_order_key:
+// larger logit -> larger key, -0.0 folded onto +0.0): find the k-th largest
+// key T, the count of keys above it, and need = k - that count of the keys
+// equal to T to take, lowest indices first.  The output pass walks the row
+// in ascending index order; a workgroup scan of per-thread (above-T,
+// equal-to-T) counts gives every winner its output slot, so indices come
+// out sorted with no sort.  Rows whose visible length is at most k skip all
+// of this and emit 0..n-1.
 //
-// Rows of up to 16384 columns are read from memory once: thread t of a
-// 1024-thread workgroup keeps the keys of columns [t*VPT, (t+1)*VPT) in
-// registers through all three rounds and the output pass
-// (topk_reg_kernel).  Wider rows take the streaming kernel, which re-reads
-// the row from L2 for every pass.
+// topk_select_kernel (rows up to 16384 columns, and the segments and merge
+// of wider rows) keeps each thread's keys in registers from the single read
+// to the output and finds T from a sample, a histogram over the sampled
+// value range and a brute-force rank of the few keys in the threshold bin,
+// with an exact radix select as the fallback.  Rows too wide for the
+// segment-and-merge plan take topk_row_kernel, which streams the row from
+// L2 for each of three radix rounds (11, 11, 10 key bits).
+#include <type_traits>
+
 #include "sai_device.h"
 
 using namespace sai;
@@ -153,20 +152,42 @@ __device__ __forceinline__ int wave_scan_dpp(int v) {
   return v;
 }
 
+// Wave64 maximum of unsigned values, in lane 63 (same DPP pattern as
+// wave_scan_dpp, with 0 as the identity).
+__device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x111, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x112, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x114, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x118, 0xf, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));
+  return v;
+}
+
 #ifndef SAI_TOPK_THREADS
 #define SAI_TOPK_THREADS 1024
 #endif
+#ifndef SAI_TOPK_SEG_VPT
+#define SAI_TOPK_SEG_VPT 16
+#endif
 constexpr int kRegThreads = SAI_TOPK_THREADS;
+constexpr int kSegVpt = SAI_TOPK_SEG_VPT;  // columns per thread of a row segment
+constexpr int kCandMax = 64;               // threshold-bin keys resolved by brute force
 
-// Wave 0 of the workgroup finds the bin holding the need-th largest count
-// of hist[0..NB): lane l owns the PER = NB/64 bins [NB-PER(l+1), NB-PER*l),
-// read with 16-byte LDS loads into registers; a DPP scan of the lane sums in
-// lane order (= descending bins) finds the lane that holds the need-th
-// element, and that lane walks its registers downwards.  It writes
-// {bin, count above the bin, 1} to sel, or leaves sel untouched if the
-// histogram holds fewer than need elements.
+struct BinPick {
+  int bin, above;
+  bool found;
+};
+
+// Every lane of the calling wave gets the bin of hist[0..NB) that holds the
+// need-th largest element when bins are taken from the top down, and the
+// count above that bin; found is false if the histogram holds fewer than
+// need (with clamp_to_total, need is first lowered to the total).  Lane l reads the PER = NB/64 bins [NB-PER(l+1), NB-PER*l) with
+// 16-byte LDS loads; a DPP scan of the lane sums in lane order (descending
+// bins) finds the lane holding the need-th element, which walks its bins
+// downwards; the result is broadcast from that lane.
 template <int NB>
-__device__ __forceinline__ void select_bin(const int* hist, int need, int* sel) {
+__device__ __forceinline__ BinPick pick_bin(const int* hist, int need, bool clamp_to_total = false) {
   constexpr int PER = NB / 64;
   const int lane = threadIdx.x & 63;
   const int lo = NB - PER * (lane + 1);
@@ -180,133 +201,312 @@ __device__ __forceinline__ void select_bin(const int* hist, int need, int* sel) 
 #pragma unroll
   for (int j = 0; j < PER; ++j) sum += h[j];
   const int inc = wave_scan_dpp(sum);
-  int acc = inc - sum;
-  if (acc < need && need <= inc) {
-    int bin = lo, above = acc;
-    bool done = false;
+  if (clamp_to_total) need = min(need, __builtin_amdgcn_readlane(inc, 63));
+  const int acc = inc - sum;
+  const bool hit = acc < need && need <= inc;
+  // branch-free walk from the lane's top bin down: the bins whose running
+  // total stays below need are the ones above the chosen bin
+  int run = 0, nbelow = 0, sum_above = 0;
 #pragma unroll
-    for (int j = PER - 1; j >= 0; --j) {
-      if (!done) {
-        if (acc + h[j] >= need) {
-          bin = lo + j;
-          above = acc;
-          done = true;
-        } else {
-          acc += h[j];
+  for (int j = PER - 1; j >= 0; --j) {
+    run += h[j];
+    const bool short_of = acc + run < need;
+    nbelow += short_of;
+    sum_above += short_of ? h[j] : 0;
+  }
+  const int bin = lo + PER - 1 - nbelow, above = acc + sum_above;
+  const uint64_t m = __ballot(hit);
+  if (m == 0) return {0, 0, false};
+  const int src = (int)__builtin_ctzll(m);
+  return {__builtin_amdgcn_readlane(bin, src), __builtin_amdgcn_readlane(above, src), true};
+}
+
+// The float whose order key is k (the inverse of f32_order_key; -0 comes
+// back as +0).
+__device__ __forceinline__ float order_key_value(uint32_t k) {
+  return __uint_as_float((k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k);
+}
+
+// Selection key: the order key of the logit, never 0 (0 marks a position
+// that is not part of the row: past its length, or an unused candidate
+// slot).
+__device__ __forceinline__ uint32_t sel_key(float v) {
+  const uint32_t k = f32_order_key(v);
+  return k ? k : 1u;
+}
+
+// Register-resident exact top-k of one row (or one segment of a row, or
+// one row's candidate list): thread t keeps the keys of positions
+// [t*VPT, (t+1)*VPT) in registers from the single read to the output.
+//
+//   CIN  = false: positions are the columns of a logits row (segment);
+//          true:  positions are a candidate list (key, column) of nseg*k
+//                 slots per row, written by the segment pass.
+//   COUT = false: write the winners' columns, ascending, to out_idx[r, k];
+//          true:  write the segment's winners (key, column), ascending, to
+//                 its k-slot candidate list; unused slots get (0, -1).
+//
+// Finding the k-th largest key T:
+//  1. A sample of one key per thread gives, through a 2048-bin histogram of
+//     the top 11 key bits, a lower bound key_lo on T with a 30% margin, and
+//     the largest sampled key key_hi.
+//  2. Keys >= key_lo are counted in 2048 bins spread linearly over
+//     [key_lo, key_hi] (keys above key_hi go to the top bin); the bin
+//     holding the k-th largest key typically holds a few keys.
+//  3. Those keys (at most kCandMax) are copied to LDS and every wave ranks
+//     them by brute force in registers, which gives T exactly.
+// If the bound was too high or the bin too full (heavy ties, odd
+// distributions), an exact 3-round radix select over all keys (11, 11, 10
+// bits) runs instead, so the result is exact either way.
+//
+// Output: a workgroup scan of per-thread (above T, equal to T) counts gives
+// every winner its slot (the `need` lowest-index keys equal to T win), so
+// the winners come out in ascending position order; they are staged in LDS
+// and written with coalesced stores.
+template <int VPT, bool VEC, bool CIN, bool COUT>
+__global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
+    const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
+    int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
+    int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col) {
+  constexpr int NT = kRegThreads, kWaves = NT / 64, SEG = VPT * NT;
+  __shared__ __align__(16) int s_h0[kBins];
+  __shared__ __align__(16) int s_h1[kBins];
+  __shared__ uint32_t s_cand[kCandMax];
+  __shared__ int s_wsum[kWaves];
+  __shared__ uint32_t s_misc[2];  // [0] threshold-bin keys, [1] largest sampled key
+  __shared__ int s_pick[3];       // wave 0's pick_bin result: bin, above, found
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = COUT ? (int)(blockIdx.x / nseg) : (int)blockIdx.x;
+  const int len = (int)min((int64_t)max(row_len[r], 0), stride);
+  if (len <= k) {  // the whole row wins; a segment pass leaves it to the merge
+    if (!COUT)
+      for (int j = tid; j < k; j += NT) out_idx[(int64_t)r * k + j] = j < len ? j : -1;
+    return;
+  }
+  // In the split plan a row that fits one segment is finished by segment 0,
+  // which writes the final indices; the other segments and the merge skip it.
+  constexpr int kSegCols = kSegVpt * NT;
+  if (CIN && len <= kSegCols) return;
+  if (COUT && len <= kSegCols && blockIdx.x != (unsigned)r * nseg) return;
+  const bool final_out = !COUT || len <= kSegCols;
+  int n;             // positions of this workgroup
+  int64_t cbase = 0; // column of position 0 (rows and segments)
+  if (CIN) {
+    n = nseg * k;
+  } else if (COUT) {
+    cbase = (int64_t)(blockIdx.x - (unsigned)r * nseg) * SEG;
+    n = (int)max(min((int64_t)len - cbase, (int64_t)SEG), (int64_t)0);
+  } else {
+    n = len;
+  }
+
+  const int base = tid * VPT;
+  uint32_t key[VPT];
+  int32_t col[CIN ? VPT : 1];
+  // Every load is issued unconditionally from an address clamped into the
+  // row (positions past n are masked afterwards), so all of a thread's
+  // loads are in flight together instead of each waiting behind a branch.
+  if (CIN) {
+    const uint32_t* kp = c_key + (int64_t)r * n;
+    const int32_t* cp = c_col + (int64_t)r * n;
+#pragma unroll
+    for (int e = 0; e < VPT; e += 4) {
+      if (VEC) {  // n is a multiple of 4
+        const int p = min(base + e, n - 4);
+        const uint4 kv = *reinterpret_cast<const uint4*>(kp + p);
+        const int4 cv = *reinterpret_cast<const int4*>(cp + p);
+        key[e] = kv.x; key[e + 1] = kv.y; key[e + 2] = kv.z; key[e + 3] = kv.w;
+        col[e] = cv.x; col[e + 1] = cv.y; col[e + 2] = cv.z; col[e + 3] = cv.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int p = min(base + e + i, n - 1);
+          key[e + i] = kp[p];
+          col[e + i] = cp[p];
         }
       }
     }
-    sel[0] = bin;
-    sel[1] = above;
-    sel[2] = 1;
-  }
-}
-
-// Register-resident radix select: thread t owns the VPT consecutive
-// columns [t*VPT, (t+1)*VPT) of the row (rows up to kRegThreads*VPT columns).
-// Before the first round, a sample of one key per thread (every VPT-th
-// column) locates a lower bound on the first digit of the k-th largest key,
-// with a 30% margin; the first round then counts only keys at or above it,
-// which cuts its LDS atomics several-fold.  If the pruned count holds fewer
-// than k keys, the first round is redone over every key, so the result is
-// exact either way.  Every output write is bounds-guarded by k.
-template <int VPT, bool VEC>
-__global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(
-    const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
-    int32_t k, int32_t* __restrict__ out) {
-  __shared__ __align__(16) int s_hist[kBins];
-  __shared__ int s_wsum[kRegThreads / 64];
-  __shared__ int s_sel[5][3];  // sample, round 1, round 1 again, round 2, round 3
-
-  const int r = blockIdx.x;
-  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
-  constexpr int kWaves = kRegThreads / 64;
-  int32_t* o = out + (int64_t)r * k;
-  const int n = (int)min((int64_t)max(row_len[r], 0), stride);
-  if (n <= k) {
-    for (int j = tid; j < k; j += kRegThreads) o[j] = j < n ? j : -1;
-    return;
-  }
-  const float* x = logits + (int64_t)r * stride;
-  const int base = tid * VPT;
-  uint32_t key[VPT];
-#pragma unroll
-  for (int e = 0; e < VPT; e += 4) {
-    float v[4];
-    load4<VEC>(x, base + e, n, v);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) key[e + i] = f32_order_key(v[i]);
-  }
-
-  auto clear = [&](int slot) {
-    for (int i = tid; i < kBins; i += kRegThreads) s_hist[i] = 0;
-    if (tid < 3) s_sel[slot][tid] = 0;
-    __syncthreads();
-  };
-
-  // sample: one key per thread that owns any column
-  clear(0);
-  if (base < n) atomicAdd(&s_hist[key[0] >> 21], 1);
-  __syncthreads();
-  const int S = (n + VPT - 1) / VPT;
-  const int m = min(S, (int)(((int64_t)k * S * 13 + (int64_t)n * 10 - 1) / ((int64_t)n * 10)) + 8);
-  if (wid == 0) select_bin<kBins>(s_hist, m, s_sel[0]);
-  __syncthreads();
-  const uint32_t lo_digit = (uint32_t)s_sel[0][0];
-
-  // round 1 on keys whose first digit is at least lo_digit
-  clear(1);
-#pragma unroll
-  for (int e = 0; e < VPT; ++e)
-    if (base + e < n && (key[e] >> 21) >= lo_digit) atomicAdd(&s_hist[key[e] >> 21], 1);
-  __syncthreads();
-  if (wid == 0) select_bin<kBins>(s_hist, k, s_sel[1]);
-  __syncthreads();
-  int slot = 1;
-  if (!s_sel[1][2]) {  // pruned too much: count every key
-    clear(2);
 #pragma unroll
     for (int e = 0; e < VPT; ++e)
-      if (base + e < n) atomicAdd(&s_hist[key[e] >> 21], 1);
-    __syncthreads();
-    if (wid == 0) select_bin<kBins>(s_hist, k, s_sel[2]);
-    __syncthreads();
-    slot = 2;
+      if (base + e >= n) {
+        key[e] = 0u;
+        col[e] = -1;
+      }
+  } else {
+    // the row holds `stride` floats from x0; cbase + n <= stride
+    const float* x0 = logits + (int64_t)r * stride;
+    float v[VPT];
+#pragma unroll
+    for (int e = 0; e < VPT; e += 4) {
+      if (VEC) {  // stride is a multiple of 4
+        const int64_t p = min(cbase + base + e, stride - 4);
+        const float4 f = *reinterpret_cast<const float4*>(x0 + p);
+        v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[e + i] = x0[min(cbase + base + e + i, cbase + n - 1)];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) key[e] = base + e < n ? sel_key(v[e]) : 0u;
   }
-  uint32_t prefix = (uint32_t)s_sel[slot][0] << 21;
-  uint32_t pmask = 0x7FFu << 21;
-  int need = k - s_sel[slot][1];
+  auto column = [&](int e) -> int32_t {
+    if constexpr (CIN) return col[e];
+    else return (int32_t)(cbase + base + e);
+  };
 
-  // round 2: bits 20..10 of keys matching the first digit
-  clear(3);
+  // pick_bin by wave 0, broadcast to the workgroup through LDS
+  auto pick = [&](const int* h, int nd, auto nb_tag, bool clamp = false) {
+    constexpr int NB = decltype(nb_tag)::value;
+    if (wid == 0) {
+      const BinPick p = pick_bin<NB>(h, nd, clamp);
+      if (lane == 0) {
+        s_pick[0] = p.bin;
+        s_pick[1] = p.above;
+        s_pick[2] = p.found;
+      }
+    }
+    __syncthreads();
+    return BinPick{s_pick[0], s_pick[1], s_pick[2] != 0};
+  };
+  using B11 = std::integral_constant<int, 2048>;
+  using B10 = std::integral_constant<int, 1024>;
+
+  if (COUT && !final_out && n <= k) {  // at most k columns: all are candidates
+    uint32_t* ok = o_key + (int64_t)blockIdx.x * k;
+    int32_t* oc = o_col + (int64_t)blockIdx.x * k;
 #pragma unroll
-  for (int e = 0; e < VPT; ++e)
-    if (base + e < n && (key[e] & pmask) == prefix) atomicAdd(&s_hist[(key[e] >> 10) & 0x7FF], 1);
-  __syncthreads();
-  if (wid == 0) select_bin<kBins>(s_hist, need, s_sel[3]);
-  __syncthreads();
-  prefix |= (uint32_t)s_sel[3][0] << 10;
-  pmask |= 0x7FFu << 10;
-  need -= s_sel[3][1];
+    for (int e = 0; e < VPT; ++e)
+      if (base + e < n) {
+        ok[base + e] = key[e];
+        oc[base + e] = column(e);
+      }
+    for (int j = n + tid; j < k; j += NT) {
+      ok[j] = 0u;
+      oc[j] = -1;
+    }
+    return;
+  }
 
-  // round 3: bits 9..0
-  clear(4);
+  // 1. sample
+  for (int i = tid; i < kBins; i += NT) {
+    s_h0[i] = 0;
+    s_h1[i] = 0;
+  }
+  if (tid < 2) s_misc[tid] = 0u;
+  __syncthreads();
+  if (key[0] != 0u) atomicAdd(&s_h0[key[0] >> 21], 1);
+  const uint32_t wmax = wave_max_dpp(key[0]);
+  if (lane == 63) atomicMax(&s_misc[1], wmax);
+  __syncthreads();
+  const int S = (n + VPT - 1) / VPT;
+  // k*S*13 < 2^25 and n*10 < 2^19: 32-bit arithmetic
+  const int m = min(S, (int)(((uint32_t)k * S * 13u + (uint32_t)n * 10u - 1u) / ((uint32_t)n * 10u)) + 8);
+  const BinPick ps = pick(s_h0, m, B11{}, true);
+  const uint32_t lo_digit = (uint32_t)ps.bin;
+  const uint32_t key_lo = lo_digit << 21;
+  const float v_lo = order_key_value(key_lo);
+  const float range = order_key_value(max(s_misc[1], key_lo)) - v_lo;
+  const float scale = 2048.0f / range;
+  auto fbin = [&](uint32_t kk) {
+    return (int)fminf((order_key_value(kk) - v_lo) * scale, (float)(kBins - 1));
+  };
+
+  // 2. linear bins over the logit values [v_lo, v_hi] (a finite, non-empty
+  // range: anything else goes straight to the radix select)
+  bool fast = isfinite(v_lo) && isfinite(range) && range > 0.0f && isfinite(scale);
+  BinPick p1 = {0, 0, false};
+  if (fast) {
 #pragma unroll
-  for (int e = 0; e < VPT; ++e)
-    if (base + e < n && (key[e] & pmask) == prefix) atomicAdd(&s_hist[key[e] & 0x3FF], 1);
-  __syncthreads();
-  if (wid == 0) select_bin<1024>(s_hist, need, s_sel[4]);
-  __syncthreads();
-  prefix |= (uint32_t)s_sel[4][0];
-  need -= s_sel[4][1];
-  const uint32_t T = prefix;
+    for (int e = 0; e < VPT; ++e)
+      if (key[e] != 0u && key[e] >= key_lo) atomicAdd(&s_h1[fbin(key[e])], 1);
+    __syncthreads();
+    p1 = pick(s_h1, k, B11{});
+    fast = p1.found;
+  }
+  if (fast) {
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
+      if (key[e] != 0u && key[e] >= key_lo && fbin(key[e]) == p1.bin) {
+        const uint32_t sl = atomicAdd(&s_misc[0], 1u);
+        if (sl < (uint32_t)kCandMax) s_cand[sl] = key[e];
+      }
+    }
+    __syncthreads();
+    fast = s_misc[0] <= (uint32_t)kCandMax;
+  }
 
-  // ordered output over the whole row: counts packed as (equal << 12) | above
-  // (above-T totals stay below k <= 2048; equal totals below 2^20)
+  uint32_t T = 0;
+  int need = 0;  // keys equal to T that win (lowest positions first)
+  if (fast) {
+    // 3. rank the threshold bin's keys: T is the need1-th largest of them
+    // (every wave computes the same from the same LDS contents)
+    const int nc = (int)s_misc[0];
+    const int need1 = k - p1.above;
+    const uint32_t c = lane < nc ? s_cand[lane] : 0u;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < nc; ++j) {
+      const uint32_t cj = __builtin_amdgcn_readlane(c, j);
+      gt += cj > c;
+      ge += cj >= c;
+    }
+    const uint64_t hm = __ballot(lane < nc && gt < need1 && need1 <= ge);
+    if (hm != 0) {
+      const int src = (int)__builtin_ctzll(hm);
+      T = __builtin_amdgcn_readlane(c, src);
+      need = need1 - __builtin_amdgcn_readlane(gt, src);
+    } else {
+      fast = false;
+    }
+  }
+  if (!fast) {
+    // exact radix select; the first digit counts only digits >= lo_digit
+    // unless that holds fewer than k keys
+    uint32_t prefix = 0, pmask = 0;
+    int nd = k;
+    auto round = [&](int* h, int shift, uint32_t dm, uint32_t min_digit, auto nb_tag) {
+      for (int i = tid; i < kBins; i += NT) h[i] = 0;
+      __syncthreads();
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) {
+        const uint32_t d = (key[e] >> shift) & dm;
+        if (key[e] != 0u && (key[e] & pmask) == prefix && d >= min_digit) atomicAdd(&h[d], 1);
+      }
+      __syncthreads();
+      const BinPick p = pick(h, nd, nb_tag);
+      if (p.found) {
+        prefix |= (uint32_t)p.bin << shift;
+        pmask |= dm << shift;
+        nd -= p.above;
+      }
+      return p.found;
+    };
+    // every wave is done reading both histograms; from here consecutive
+    // rounds alternate buffers, so a clear never overlaps a slower wave's
+    // pick of the round before
+    __syncthreads();
+    int* hb = s_h0;
+    auto flip = [&]() { hb = hb == s_h0 ? s_h1 : s_h0; };
+    const bool pruned = round(hb, 21, 0x7FFu, lo_digit, B11{});
+    flip();
+    if (!pruned) {
+      round(hb, 21, 0x7FFu, 0u, B11{});
+      flip();
+    }
+    round(hb, 10, 0x7FFu, 0u, B11{});
+    flip();
+    round(hb, 0, 0x3FFu, 0u, B10{});
+    T = prefix;
+    need = nd;
+  }
+
+  // ordered output; counts packed as (equal << 12) | above (above-T totals
+  // stay below k <= 2048, equal totals below 2^19)
   int ngt = 0, neq = 0;
 #pragma unroll
   for (int e = 0; e < VPT; ++e) {
-    const bool in = base + e < n;
+    const bool in = key[e] != 0u;
     ngt += (in && key[e] > T);
     neq += (in && key[e] == T);
   }
@@ -318,64 +518,127 @@ __global__ __launch_bounds__(kRegThreads) void topk_reg_kernel(
 #pragma unroll
   for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
   int gt_b = ex & 0xFFF, eq_b = ex >> 12;
+  int tot = 0;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) tot += s_wsum[w];
+  const int nwin = min(k, (tot & 0xFFF) + min(tot >> 12, need));  // k unless the row is short
 #pragma unroll
   for (int e = 0; e < VPT; ++e) {
-    if (base + e < n) {
+    if (key[e] != 0u) {
+      int pos = -1;
       if (key[e] > T) {
-        const int pos = gt_b + min(eq_b, need);
-        if ((unsigned)pos < (unsigned)k) o[pos] = base + e;
+        pos = gt_b + min(eq_b, need);
         ++gt_b;
       } else if (key[e] == T) {
-        const int pos = gt_b + eq_b;
-        if (eq_b < need && (unsigned)pos < (unsigned)k) o[pos] = base + e;
+        if (eq_b < need) pos = gt_b + eq_b;
         ++eq_b;
+      }
+      if ((unsigned)pos < (unsigned)k) {
+        s_h0[pos] = column(e);
+        if (COUT) s_h1[pos] = (int)key[e];
       }
     }
   }
+  __syncthreads();
+  if (COUT && !final_out) {
+    uint32_t* ok = o_key + (int64_t)blockIdx.x * k;
+    int32_t* oc = o_col + (int64_t)blockIdx.x * k;
+    for (int j = tid; j < k; j += NT) {
+      ok[j] = j < nwin ? (uint32_t)s_h1[j] : 0u;
+      oc[j] = j < nwin ? s_h0[j] : -1;
+    }
+  } else {
+    int32_t* o = out_idx + (int64_t)r * k;
+    for (int j = tid; j < k; j += NT) o[j] = j < nwin ? s_h0[j] : -1;
+  }
 }
 
-template <int VPT>
-void launch_reg(bool vec, const float* logits, int64_t stride, const int32_t* row_len, int32_t rows,
-                int32_t k, int32_t* out, hipStream_t s) {
-  if (vec)
-    hipLaunchKernelGGL((topk_reg_kernel<VPT, true>), dim3(rows), dim3(kRegThreads), 0, s, logits,
-                       stride, row_len, k, out);
-  else
-    hipLaunchKernelGGL((topk_reg_kernel<VPT, false>), dim3(rows), dim3(kRegThreads), 0, s, logits,
-                       stride, row_len, k, out);
+// How topk_rows handles a row pitch: rows up to 16 columns per thread are
+// selected in one pass; wider rows are cut into segments of kSegVpt columns
+// per thread whose winners are merged by a second pass, as long as the
+// candidate lists fit 16 per thread; wider still take the streaming kernel.
+struct TopkPlan {
+  int vpt;   // one-pass columns per thread (0 = not one-pass)
+  int nseg;  // segments per row (split plan)
+  int mvpt;  // merge candidates per thread (split plan)
+  bool stream;
+};
+
+TopkPlan plan_for(int64_t stride, int k) {
+  const int64_t nt = kRegThreads;
+  if (stride <= 4 * nt) return {4, 0, 0, false};
+  if (stride <= 8 * nt) return {8, 0, 0, false};
+  if (stride <= 16 * nt) return {16, 0, 0, false};
+  const int64_t nseg = (stride + kSegVpt * nt - 1) / (kSegVpt * nt);
+  const int64_t cand = nseg * k;
+  const int mvpt = cand <= 4 * nt ? 4 : cand <= 8 * nt ? 8 : cand <= 16 * nt ? 16 : 0;
+  if (mvpt == 0) return {0, 0, 0, true};
+  return {0, (int)nseg, mvpt, false};
 }
+
+template <int VPT, bool CIN, bool COUT>
+void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, const int32_t* row_len,
+                int32_t k, int32_t nseg, const uint32_t* c_key, const int32_t* c_col, int32_t* out,
+                uint32_t* o_key, int32_t* o_col, hipStream_t s) {
+  if (vec)
+    hipLaunchKernelGGL((topk_select_kernel<VPT, true, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
+                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col);
+  else
+    hipLaunchKernelGGL((topk_select_kernel<VPT, false, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
+                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col);
+}
+
+bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 }  // namespace
 
 extern "C" size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
-  (void)rows;
-  (void)logits_stride;
-  (void)k;
-  return 0;
+  if (rows <= 0 || logits_stride <= 0 || k < 1 || k > SAI_TOPK_MAX) return 0;
+  const TopkPlan p = plan_for(logits_stride, k);
+  if (p.nseg == 0) return 0;
+  // candidate keys then candidate columns, [rows][nseg][k] each
+  return (size_t)rows * (size_t)p.nseg * (size_t)k * 8u;
 }
 
 extern "C" int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,
                          int32_t rows, int32_t k, int32_t* out_idx, void* workspace,
                          size_t workspace_bytes, hipStream_t stream) {
-  (void)workspace;
-  (void)workspace_bytes;
   if (rows < 0 || logits_stride < 0) return SAI_EINVAL;
   if (k < 1 || k > SAI_TOPK_MAX) return SAI_EUNSUPPORTED;
   if (rows == 0) return SAI_OK;
   if (!logits || !row_len || !out_idx || logits_stride == 0) return SAI_EINVAL;
   if (logits_stride > 0x7FFFFFFF - 4 * kThreads) return SAI_EUNSUPPORTED;
-  const bool vec = (logits_stride % 4 == 0) && ((reinterpret_cast<uintptr_t>(logits) & 15u) == 0);
-  if (logits_stride <= 4 * kRegThreads)
-    launch_reg<4>(vec, logits, logits_stride, row_len, rows, k, out_idx, stream);
-  else if (logits_stride <= 8 * kRegThreads)
-    launch_reg<8>(vec, logits, logits_stride, row_len, rows, k, out_idx, stream);
-  else if (logits_stride <= 16 * kRegThreads)
-    launch_reg<16>(vec, logits, logits_stride, row_len, rows, k, out_idx, stream);
-  else if (vec)
+  const bool vec = (logits_stride % 4 == 0) && aligned16p(logits);
+  const TopkPlan p = plan_for(logits_stride, k);
+  const unsigned ur = (unsigned)rows;
+  if (p.vpt == 4) {
+    launch_sel<4, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
+  } else if (p.vpt == 8) {
+    launch_sel<8, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
+  } else if (p.vpt == 16) {
+    launch_sel<16, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
+  } else if (p.nseg > 0) {
+    const size_t need = topk_workspace_bytes(rows, logits_stride, k);
+    if (!workspace || workspace_bytes < need) return SAI_EWORKSPACE;
+    if ((int64_t)rows * p.nseg > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+    uint32_t* ck = static_cast<uint32_t*>(workspace);
+    int32_t* cc = reinterpret_cast<int32_t*>(ck + (size_t)rows * p.nseg * k);
+    const bool cvec = (k % 4 == 0) && aligned16p(workspace);
+    // the segment pass also writes out_idx for rows that fit one segment
+    launch_sel<kSegVpt, false, true>(vec, ur * (unsigned)p.nseg, logits, logits_stride, row_len, k, p.nseg,
+                                     nullptr, nullptr, out_idx, ck, cc, stream);
+    if (p.mvpt == 4)
+      launch_sel<4, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
+    else if (p.mvpt == 8)
+      launch_sel<8, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
+    else
+      launch_sel<16, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
+  } else if (vec) {
     hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kThreads), 0, stream, logits,
                        logits_stride, row_len, k, out_idx);
-  else
+  } else {
     hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kThreads), 0, stream, logits,
                        logits_stride, row_len, k, out_idx);
+  }
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }

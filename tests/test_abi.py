@@ -12,7 +12,7 @@ from sparse_attention_indexer_paged_amd import binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sai.h")
 
-SAI_OK, SAI_EINVAL, SAI_EUNSUPPORTED = 0, -1, -2
+SAI_OK, SAI_EINVAL, SAI_EUNSUPPORTED, SAI_EWORKSPACE = 0, -1, -2, -3
 
 
 def declared_functions():
@@ -77,4 +77,17 @@ def test_validation_needs_no_gpu(lib):
 
 
 def test_topk_workspace_query(lib):
-    assert binding.topk_workspace_bytes(64, 16384, 2048) >= 0
+    # rows up to 16384 wide need none; wider rows keep k (key, column)
+    # candidates per 16384-column segment; past 8 segments none again
+    assert binding.topk_workspace_bytes(64, 16384, 2048) == 0
+    assert binding.topk_workspace_bytes(256, 65536, 2048) == 256 * 4 * 2048 * 8
+    assert binding.topk_workspace_bytes(32, 131072, 2048) == 32 * 8 * 2048 * 8
+    assert binding.topk_workspace_bytes(32, 131073, 2048) == 0
+    assert binding.topk_workspace_bytes(4, 300000, 100) == 4 * 19 * 100 * 8
+
+
+def test_topk_missing_workspace_is_rejected(lib):
+    fake = ctypes.c_void_p(4096)
+    nul = ctypes.c_void_p(0)
+    assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, nul, 0, nul) == SAI_EWORKSPACE
+    assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, fake, 100, nul) == SAI_EWORKSPACE

@@ -196,9 +196,8 @@ def test_decode_topk_and_slots_bit_exact_tiny():
     assert np.array_equal(slots.cpu().numpy(), want_s)
 
 
-def _adversarial_rows():
+def _adversarial_rows(W=9000):
     rng = np.random.default_rng(3)
-    W = 9000
     rows = []
     rows.append(rng.standard_normal(W))
     rows.append(np.zeros(W))                                   # all equal
@@ -211,7 +210,7 @@ def _adversarial_rows():
     r = rng.standard_normal(W) * 1e-38; rows.append(r)         # subnormals
     r = np.full(W, 1.0); r[5000:] = 2.0; rows.append(r)        # threshold inside a tie block
     L = np.stack(rows).astype(np.float32)
-    lens = np.array([W, W, W, W, W, W, W, W, W, W, 2048, 2047, 1, 0, 5000, 8999], np.int32)
+    lens = np.array([W, W, W, W, W, W, W, W, W, W, 2048, 2047, 1, 0, 5000, W - 1], np.int32)
     L = np.concatenate([L, L[:6]])
     return L, lens
 
@@ -223,6 +222,30 @@ def test_topk_adversarial_rows(k):
     got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
     want = O.topk_rows(L, lens, k)
     assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("k", [2048, 37])
+def test_topk_adversarial_wide_rows(k):
+    """The same rows 40000 wide: three segments per row whose winners are
+    merged, ties and fallbacks in both passes."""
+    _say(f"topk_rows: adversarial rows 40000 wide, k={k}")
+    L, lens = _adversarial_rows(40000)
+    got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
+    want = O.topk_rows(L, lens, k)
+    assert np.array_equal(got.cpu().numpy(), want)
+
+
+@pytest.mark.parametrize("width,k", [(140000, 2048), (300000, 100)])
+def test_topk_widest_rows(width, k):
+    """Rows past the two-pass limit (streaming kernel) and a small k whose
+    candidate lists still fit the merge."""
+    _say(f"topk_rows: width {width}, k={k}")
+    rng = np.random.default_rng(width + k)
+    L = rng.standard_normal((4, width)).astype(np.float32)
+    L[1, ::3] = 0.5
+    lens = np.array([width, width - 7, k + 1, width // 2], np.int32)
+    got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
+    assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, k))
 
 
 def test_topk_unaligned_stride():
