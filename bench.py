@@ -2,8 +2,9 @@
 """Throughput of the paged lightning-indexer hot path on one MI355X.
 
 One step = one pass of the whole hot path over one batch of synthetic input:
-  decode:  paged_mqa_logits -> topk_rows (top-2048) -> topk_to_global_slots
-  prefill: gather_indexer_k -> mqa_logits -> topk_rows -> topk_to_global_slots
+  decode:  paged_mqa_logits -> topk_rows_slots (top-2048 indices and their
+           global slot ids, i.e. topk_rows + topk_to_global_slots fused)
+  prefill: gather_indexer_k -> mqa_logits -> topk_rows_slots
 The default workload is the decode batch the headline metric is quoted on:
 batch 64, next_n 1, contexts uniform in [4096, 16384], a 20000-block paged
 fp8 K cache (169 MB) with a random block table.
@@ -151,7 +152,7 @@ def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
 
 
 def decode_pipeline(torch, sai, lib, wl, dev, npools):
-    """Decode step: paged_mqa_logits -> topk_rows -> topk_to_global_slots."""
+    """Decode step: paged_mqa_logits -> topk_rows_slots."""
     nn, rows, width = wl.next_n, wl.rows, wl.width
     pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
     bt = torch.from_numpy(wl.block_table).to(dev)
@@ -171,11 +172,9 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
             ("paged_mqa_logits", lambda i: lib.paged_mqa_logits(
                 P(q_fp8), P(w_eff), P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0),
                 P(ctx), wl.batch, nn, P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), s)),
-            ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
-                                                  P(t["idx"]), P(t["ws"]), ws_bytes, s)),
-            ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
-                P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
-                P(t["slots"]), s)),
+            ("topk_rows_slots", lambda i: lib.topk_rows_slots(
+                P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), P(bt), bt.stride(0),
+                wl.batch, rows, 2048, P(t["idx"]), P(t["slots"]), P(t["ws"]), ws_bytes, s)),
         ]
     ctx_np = wl.ctx.astype(np.int64)
     k_bytes = int(ctx_np.sum()) * K_BYTES_PER_TOKEN
@@ -186,7 +185,7 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
 
 
 def prefill_pipeline(torch, sai, lib, wl, dev, npools):
-    """Prefill step: gather_indexer_k -> mqa_logits -> topk_rows -> topk_to_global_slots."""
+    """Prefill step: gather_indexer_k -> mqa_logits -> topk_rows_slots."""
     rows, width, total = wl.rows, wl.width, wl.total_tokens
     pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
     bt = torch.from_numpy(wl.block_table).to(dev)
@@ -211,11 +210,9 @@ def prefill_pipeline(torch, sai, lib, wl, dev, npools):
             ("mqa_logits", lambda i: lib.mqa_logits(
                 P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu), wl.batch, total, P(t["logits"]),
                 width, P(t["row_len"]), P(t["row_req"]), s)),
-            ("topk_rows", lambda i: lib.topk_rows(P(t["logits"]), width, P(t["row_len"]), rows, 2048,
-                                                  P(t["idx"]), P(t["ws"]), ws_bytes, s)),
-            ("topk_to_global_slots", lambda i: lib.topk_to_global_slots(
-                P(t["idx"]), P(t["row_req"]), P(bt), bt.stride(0), wl.batch, rows, 2048,
-                P(t["slots"]), s)),
+            ("topk_rows_slots", lambda i: lib.topk_rows_slots(
+                P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), P(bt), bt.stride(0),
+                wl.batch, rows, 2048, P(t["idx"]), P(t["slots"]), P(t["ws"]), ws_bytes, s)),
         ]
     lim = np.concatenate([np.arange(1, int(c) + 1) for c in wl.ctx]).astype(np.float64)
     flops = float(lim.sum()) * 64 * 128 * 2

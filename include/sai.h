@@ -213,6 +213,25 @@ int topk_to_global_slots(const int32_t* topk_idx, const int32_t* row_req,
                          const int32_t* block_table, int64_t bt_stride, int32_t batch,
                          int32_t rows, int32_t k, int32_t* out_slots, hipStream_t stream);
 
+/*
+ * topk_rows_slots -- topk_rows and topk_to_global_slots in one call (ROCm/ATOM
+ * PR #1094, Technical Details: the selected request-local indices and the
+ * global slot ids of the sparse-attention cache they address).
+ *
+ * out_idx is what topk_rows writes and out_slots what topk_to_global_slots
+ * writes for that out_idx; the slot ids are produced by the selection
+ * kernels as they write each index, so the decode step needs no separate
+ * slot pass.  Arguments as for those two calls: logits [rows, logits_stride],
+ * row_len and row_req [rows], block_table [batch, bt_stride], out_idx and
+ * out_slots [rows, k], workspace of topk_workspace_bytes(rows,
+ * logits_stride, k) bytes.  Errors as for topk_rows, plus SAI_EINVAL for a
+ * null row_req, block_table or out_slots when rows > 0.
+ */
+int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* row_len,
+                    const int32_t* row_req, const int32_t* block_table, int64_t bt_stride,
+                    int32_t batch, int32_t rows, int32_t k, int32_t* out_idx, int32_t* out_slots,
+                    void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -41,6 +41,8 @@ SIGNATURES = {
                   _c_void_p],
     "topk_to_global_slots": [_c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32, _c_void_p,
                              _c_void_p],
+    "topk_rows_slots": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
+                        _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
 }
 _RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t}
 
@@ -252,10 +254,35 @@ def topk_to_global_slots(topk_idx, row_req, block_table, out=None):
     return out
 
 
+def topk_rows_slots(logits, row_len, row_req, block_table, k=TOPK_MAX, out=None, slots=None,
+                    workspace=None):
+    """topk_rows and topk_to_global_slots in one call: (idx, slots), int32 [rows, k] each."""
+    _need(logits, torch.float32, "logits", 2)
+    _need(row_len, torch.int32, "row_len", 1)
+    _need(row_req, torch.int32, "row_req", 1)
+    _need(block_table, torch.int32, "block_table", 2)
+    rows = logits.shape[0]
+    if row_len.shape[0] != rows or row_req.shape[0] != rows:
+        raise ValueError("row_len and row_req need one entry per row")
+    dev = logits.device
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev) if out is None else out
+    slots = torch.empty((rows, k), dtype=torch.int32, device=dev) if slots is None else slots
+    _out(out, torch.int32, "out", (rows, k))
+    _out(slots, torch.int32, "slots", (rows, k))
+    ws_bytes = topk_workspace_bytes(rows, logits.stride(0), k)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    _check(load().topk_rows_slots(_ptr(logits), logits.stride(0), _ptr(row_len), _ptr(row_req),
+                                  _ptr(block_table), block_table.stride(0), block_table.shape[0],
+                                  rows, k, _ptr(out), _ptr(slots), _ptr(workspace),
+                                  workspace.numel() if workspace is not None else 0, _stream()),
+           "topk_rows_slots")
+    return out, slots
+
+
 def decode_indexer(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None):
     """The decode hot path: logits -> top-k -> global slot ids, one stream, no host sync."""
     logits, row_len, row_req = paged_mqa_logits(q_fp8, weights, kv_cache, block_table,
                                                 context_lens, width)
-    idx = topk_rows(logits, row_len, k)
-    slots = topk_to_global_slots(idx, row_req, block_table)
+    idx, slots = topk_rows_slots(logits, row_len, row_req, block_table, k)
     return logits, idx, slots

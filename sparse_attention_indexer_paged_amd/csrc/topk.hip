@@ -235,6 +235,24 @@ __device__ __forceinline__ uint32_t sel_key(float v) {
   return k ? k : 1u;
 }
 
+// Optional fused slot map: with out != nullptr every final index i of row r
+// is also written as its global paged-cache slot,
+// bt[row_req[r] * bt_stride + i / 64] * 64 + i % 64, or -1 (for i = -1, a
+// request outside [0, batch), a block past bt_stride or a negative entry).
+struct SlotMap {
+  const int32_t* row_req;
+  const int32_t* bt;
+  int64_t bt_stride;
+  int32_t batch;
+  int32_t* out;
+};
+
+__device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t i) {
+  if (i < 0 || b < 0 || b >= sm.batch || (int64_t)(i / 64) >= sm.bt_stride) return -1;
+  const int32_t blk = sm.bt[(int64_t)b * sm.bt_stride + i / 64];
+  return blk >= 0 ? blk * 64 + i % 64 : -1;
+}
+
 // Register-resident exact top-k of one row (or one segment of a row, or
 // one row's candidate list): thread t keeps the keys of positions
 // [t*VPT, (t+1)*VPT) in registers from the single read to the output.
@@ -267,7 +285,8 @@ template <int VPT, bool VEC, bool CIN, bool COUT>
 __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
     int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
-    int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col) {
+    int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col,
+    SlotMap sm) {
   constexpr int NT = kRegThreads, kWaves = NT / 64, SEG = VPT * NT;
   __shared__ __align__(16) int s_h0[kBins];
   __shared__ __align__(16) int s_h1[kBins];
@@ -279,9 +298,14 @@ __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = COUT ? (int)(blockIdx.x / nseg) : (int)blockIdx.x;
   const int len = (int)min((int64_t)max(row_len[r], 0), stride);
+  const int32_t req = sm.out ? sm.row_req[r] : 0;
+  auto emit = [&](int j, int32_t i) {  // final index j of row r
+    out_idx[(int64_t)r * k + j] = i;
+    if (sm.out) sm.out[(int64_t)r * k + j] = slot_of(sm, req, i);
+  };
   if (len <= k) {  // the whole row wins; a segment pass leaves it to the merge
     if (!COUT)
-      for (int j = tid; j < k; j += NT) out_idx[(int64_t)r * k + j] = j < len ? j : -1;
+      for (int j = tid; j < k; j += NT) emit(j, j < len ? j : -1);
     return;
   }
   // In the split plan a row that fits one segment is finished by segment 0,
@@ -548,8 +572,7 @@ __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
       oc[j] = j < nwin ? s_h0[j] : -1;
     }
   } else {
-    int32_t* o = out_idx + (int64_t)r * k;
-    for (int j = tid; j < k; j += NT) o[j] = j < nwin ? s_h0[j] : -1;
+    for (int j = tid; j < k; j += NT) emit(j, j < nwin ? s_h0[j] : -1);
   }
 }
 
@@ -579,13 +602,13 @@ TopkPlan plan_for(int64_t stride, int k) {
 template <int VPT, bool CIN, bool COUT>
 void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, const int32_t* row_len,
                 int32_t k, int32_t nseg, const uint32_t* c_key, const int32_t* c_col, int32_t* out,
-                uint32_t* o_key, int32_t* o_col, hipStream_t s) {
+                uint32_t* o_key, int32_t* o_col, const SlotMap& sm, hipStream_t s) {
   if (vec)
     hipLaunchKernelGGL((topk_select_kernel<VPT, true, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
-                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col);
+                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
   else
     hipLaunchKernelGGL((topk_select_kernel<VPT, false, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
-                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col);
+                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
 }
 
 bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -600,9 +623,12 @@ extern "C" size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int3
   return (size_t)rows * (size_t)p.nseg * (size_t)k * 8u;
 }
 
-extern "C" int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,
-                         int32_t rows, int32_t k, int32_t* out_idx, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
+namespace {
+
+int topk_impl(const float* logits, int64_t logits_stride, const int32_t* row_len, int32_t rows,
+              int32_t k, int32_t* out_idx, void* workspace, size_t workspace_bytes,
+              const SlotMap& sm, bool* streamed, hipStream_t stream) {
+  *streamed = false;
   if (rows < 0 || logits_stride < 0) return SAI_EINVAL;
   if (k < 1 || k > SAI_TOPK_MAX) return SAI_EUNSUPPORTED;
   if (rows == 0) return SAI_OK;
@@ -611,34 +637,65 @@ extern "C" int topk_rows(const float* logits, int64_t logits_stride, const int32
   const bool vec = (logits_stride % 4 == 0) && aligned16p(logits);
   const TopkPlan p = plan_for(logits_stride, k);
   const unsigned ur = (unsigned)rows;
-  if (p.vpt == 4) {
-    launch_sel<4, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
-  } else if (p.vpt == 8) {
-    launch_sel<8, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
-  } else if (p.vpt == 16) {
-    launch_sel<16, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, stream);
-  } else if (p.nseg > 0) {
+  if (p.nseg > 0) {  // checked before anything is launched
     const size_t need = topk_workspace_bytes(rows, logits_stride, k);
     if (!workspace || workspace_bytes < need) return SAI_EWORKSPACE;
     if ((int64_t)rows * p.nseg > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  }
+  if (p.vpt == 4) {
+    launch_sel<4, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
+  } else if (p.vpt == 8) {
+    launch_sel<8, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
+  } else if (p.vpt == 16) {
+    launch_sel<16, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
+  } else if (p.nseg > 0) {
     uint32_t* ck = static_cast<uint32_t*>(workspace);
     int32_t* cc = reinterpret_cast<int32_t*>(ck + (size_t)rows * p.nseg * k);
     const bool cvec = (k % 4 == 0) && aligned16p(workspace);
-    // the segment pass also writes out_idx for rows that fit one segment
+    // the segment pass also writes the final output of rows that fit one segment
     launch_sel<kSegVpt, false, true>(vec, ur * (unsigned)p.nseg, logits, logits_stride, row_len, k, p.nseg,
-                                     nullptr, nullptr, out_idx, ck, cc, stream);
+                                     nullptr, nullptr, out_idx, ck, cc, sm, stream);
     if (p.mvpt == 4)
-      launch_sel<4, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
+      launch_sel<4, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
     else if (p.mvpt == 8)
-      launch_sel<8, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
+      launch_sel<8, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
     else
-      launch_sel<16, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, stream);
-  } else if (vec) {
-    hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kThreads), 0, stream, logits,
-                       logits_stride, row_len, k, out_idx);
+      launch_sel<16, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
   } else {
-    hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kThreads), 0, stream, logits,
-                       logits_stride, row_len, k, out_idx);
+    *streamed = true;
+    if (vec)
+      hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kThreads), 0, stream, logits,
+                         logits_stride, row_len, k, out_idx);
+    else
+      hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kThreads), 0, stream, logits,
+                         logits_stride, row_len, k, out_idx);
   }
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
+}
+
+}  // namespace
+
+extern "C" int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,
+                         int32_t rows, int32_t k, int32_t* out_idx, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  bool streamed;
+  return topk_impl(logits, logits_stride, row_len, rows, k, out_idx, workspace, workspace_bytes,
+                   SlotMap{nullptr, nullptr, 0, 0, nullptr}, &streamed, stream);
+}
+
+extern "C" int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* row_len,
+                               const int32_t* row_req, const int32_t* block_table, int64_t bt_stride,
+                               int32_t batch, int32_t rows, int32_t k, int32_t* out_idx,
+                               int32_t* out_slots, void* workspace, size_t workspace_bytes,
+                               hipStream_t stream) {
+  if (rows < 0 || batch < 0 || bt_stride < 0) return SAI_EINVAL;
+  if (rows > 0 && (!row_req || !block_table || !out_slots)) return SAI_EINVAL;
+  bool streamed;
+  const int st = topk_impl(logits, logits_stride, row_len, rows, k, out_idx, workspace,
+                           workspace_bytes, SlotMap{row_req, block_table, bt_stride, batch, out_slots},
+                           &streamed, stream);
+  if (st != SAI_OK || !streamed) return st;
+  // rows too wide for the fused kernels: map the indices afterwards
+  return topk_to_global_slots(out_idx, row_req, block_table, bt_stride, batch, rows, k, out_slots,
+                              stream);
 }

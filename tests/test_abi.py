@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "sai_status_string", "indexer_k_cache_write", "indexer_q_quant", "gather_indexer_k",
         "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
-        "topk_to_global_slots"])
+        "topk_to_global_slots", "topk_rows_slots"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -84,6 +84,19 @@ def test_topk_workspace_query(lib):
     assert binding.topk_workspace_bytes(32, 131072, 2048) == 32 * 8 * 2048 * 8
     assert binding.topk_workspace_bytes(32, 131073, 2048) == 0
     assert binding.topk_workspace_bytes(4, 300000, 100) == 4 * 19 * 100 * 8
+
+
+def test_topk_rows_slots_host_validation(lib):
+    fake = ctypes.c_void_p(4096)
+    nul = ctypes.c_void_p(0)
+    # null row_req / block_table / out_slots, negative sizes, bad k, no workspace
+    assert lib.topk_rows_slots(fake, 256, fake, nul, fake, 4, 2, 3, 8, fake, fake, nul, 0, nul) == SAI_EINVAL
+    assert lib.topk_rows_slots(fake, 256, fake, fake, nul, 4, 2, 3, 8, fake, fake, nul, 0, nul) == SAI_EINVAL
+    assert lib.topk_rows_slots(fake, 256, fake, fake, fake, 4, 2, 3, 8, fake, nul, nul, 0, nul) == SAI_EINVAL
+    assert lib.topk_rows_slots(fake, 256, fake, fake, fake, -1, 2, 3, 8, fake, fake, nul, 0, nul) == SAI_EINVAL
+    assert lib.topk_rows_slots(fake, 256, fake, fake, fake, 4, 2, 3, 0, fake, fake, nul, 0, nul) == SAI_EUNSUPPORTED
+    assert lib.topk_rows_slots(fake, 65536, fake, fake, fake, 4, 2, 3, 2048, fake, fake, nul, 0, nul) == SAI_EWORKSPACE
+    assert lib.topk_rows_slots(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul, 0, nul) == SAI_OK
 
 
 def test_topk_missing_workspace_is_rejected(lib):

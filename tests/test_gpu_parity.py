@@ -272,6 +272,36 @@ def test_slots_edge_cases():
     assert got[2].tolist() == [-1] * 8
 
 
+@pytest.mark.parametrize("width", [1000, 16384, 40000, 140000])
+def test_topk_rows_slots_matches_the_two_calls(width):
+    """The fused call on every selection path (one pass, one-segment rows,
+    segments + merge, streaming): indices and slot ids against the oracle's
+    top-k and slot map; then, with a request outside the batch and negative
+    table entries, slot ids against the standalone topk_to_global_slots."""
+    _say(f"topk_rows_slots: width {width}")
+    rng = np.random.default_rng(width)
+    rows, k = 7, 2048
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    L[3, ::5] = 1.5                                          # ties at the threshold
+    lens = np.array([width, width - 1, 2048, min(width, 3000), 5, 0, width // 2], np.int32)
+    nblk = -(-width // 64)
+    bt = rng.permutation(4 * nblk)[: 3 * nblk].reshape(3, nblk).astype(np.int32)
+    req = np.array([0, 1, 2, 1, 0, 2, 1], np.int32)
+    T = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    idx, slots = sai.topk_rows_slots(T(L), T(lens), T(req), T(bt), k)
+    want = O.topk_rows(L, lens, k)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, req, bt))
+    # entries the library maps to -1: an unused table tail and a bad request
+    bt[1, nblk // 2:] = -1
+    req[6] = 7
+    idx, slots = sai.topk_rows_slots(T(L), T(lens), T(req), T(bt), k)
+    sep = sai.topk_to_global_slots(idx, T(req), T(bt))
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert torch.equal(slots, sep)
+    assert (slots[6] == -1).all()
+
+
 # ---------------------------------------------------------------- prefill
 def test_gather_bit_exact():
     _say("gather_indexer_k: ragged requests incl. empty")
