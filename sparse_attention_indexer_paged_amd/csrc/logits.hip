@@ -478,29 +478,38 @@ struct PfBlock {
 __device__ __forceinline__ int pf_swz(int n, int c) { return n * 8 + (c ^ (n & 7)); }
 
 // Global -> registers: thread t fetches chunks t and t+256 of the block
-// (key = chunk / 8, 16-byte column = chunk % 8) and, for t < 64, key t's
-// scale.  Keys at or past nvalid read as zero.
-__device__ __forceinline__ void pf_fetch(uint4 (&r)[2], float& sc, const uint8_t* __restrict__ k,
-                                         const float* __restrict__ ks, int64_t key0, int nvalid) {
+// (key = chunk / 8, 16-byte column = chunk % 8; chunk t+256 is key
+// 32 + t/8) and key (t % 64)'s scale.
+// Every load is issued unconditionally from a token index clamped into
+// [0, total) so that all of them are in flight together; keys past the
+// request are zeroed when the block is written to LDS.
+struct PfStage {
+  uint4 c0, c1;  // chunks t and t+256
+  float s;       // scale of key t % 64
+};
+
+__device__ __forceinline__ PfStage pf_fetch(const uint8_t* __restrict__ k, const float* __restrict__ ks,
+                                            int64_t key0, int64_t total) {
   const int t = threadIdx.x;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int chunk = t + 256 * e;
-    const int n = chunk >> 3, c = chunk & 7;
-    r[e] = n < nvalid ? *reinterpret_cast<const uint4*>(k + (key0 + n) * kDim + c * 16)
-                      : make_uint4(0, 0, 0, 0);
-  }
-  sc = (t < kBlock && t < nvalid) ? ks[key0 + t] : 0.0f;
+  PfStage st;
+  st.c0 = *reinterpret_cast<const uint4*>(k + min64(key0 + (t >> 3), total - 1) * kDim + (t & 7) * 16);
+  st.c1 = *reinterpret_cast<const uint4*>(k + min64(key0 + 32 + (t >> 3), total - 1) * kDim + (t & 7) * 16);
+  st.s = ks[min64(key0 + (t & 63), total - 1)];
+  return st;
 }
 
-__device__ __forceinline__ void pf_store(PfBlock& blk, const uint4 (&r)[2], float sc) {
+// Registers -> LDS image (swizzled), keys at or past nvalid as zero.
+// (Masks rather than selects of whole values: a select between a stage
+// member and a zero constant can become a select of addresses, which puts
+// the stages in scratch memory.)
+__device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m); }
+
+__device__ __forceinline__ void pf_store(PfBlock& blk, const PfStage& st, int nvalid) {
   const int t = threadIdx.x;
-#pragma unroll
-  for (int e = 0; e < 2; ++e) {
-    const int chunk = t + 256 * e;
-    blk.code[pf_swz(chunk >> 3, chunk & 7)] = r[e];
-  }
-  if (t < kBlock) blk.scale[t] = sc;
+  const uint32_t m0 = (t >> 3) < nvalid ? ~0u : 0u, m1 = 32 + (t >> 3) < nvalid ? ~0u : 0u;
+  blk.code[pf_swz(t >> 3, t & 7)] = and4(st.c0, m0);
+  blk.code[pf_swz(32 + (t >> 3), t & 7)] = and4(st.c1, m1);
+  if (t < kBlock) blk.scale[t] = __uint_as_float(__float_as_uint(st.s) & (t < nvalid ? ~0u : 0u));
 }
 
 // B operand of key tile t: lane (g, n) takes 16-byte columns g and 4+g of key
@@ -520,12 +529,13 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
     float* __restrict__ logits, int64_t stride, int32_t* __restrict__ row_len_out,
-    int32_t* __restrict__ row_req_out, int32_t nchunks, int32_t ntiles_max) {
+    int32_t* __restrict__ row_req_out, int32_t nchunks, int32_t ntiles_max, bool vec) {
   extern __shared__ int smem[];
   int* s_tile = smem;                  // [batch+1] prefix of query tiles
   int* scratch = smem + (batch + 1);
   __shared__ PfBlock s_k[2];
   __shared__ float4 s_w[kPfTileRows][16];
+  __shared__ __align__(16) float s_res[kPfTileRows][kChunk];  // the chunk's logits per row
 
   int run = 0;
   for (int base = 0; base < batch; base += 256) {
@@ -600,54 +610,79 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) wf[r][hg] = s_w[wave * kPfRowsPerWave + r][4 * hg + (lane >> 4)];
 
-  uint4 stage[2];
-  float stage_s;
+  // Software pipeline over the chunk's blocks: block j is scored from LDS
+  // buffer j%2 while block j+2 is fetched into registers and block j+1
+  // (fetched one step earlier) is written to the other buffer.  The loop is
+  // unrolled by two so the register stages alternate statically, and no
+  // global store sits in it (results go to s_res), so the in-order vmcnt
+  // accounting only ever waits for the older of the two fetches.
+  const int64_t kbase = base_tok + col0;
+  PfStage sa, sb;
   if (nblk > 0) {
-    pf_fetch(stage, stage_s, k, ks, base_tok + col0, len - col0);
-    pf_store(s_k[0], stage, stage_s);
+    sa = pf_fetch(k, ks, kbase, total);
+    pf_store(s_k[0], sa, len - col0);  // waits for Q and w as well
+    sa = pf_fetch(k, ks, kbase + kBlock, total);
   }
   __syncthreads();
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  for (int j = 0; j < nblk; ++j) {
-    const int key0 = col0 + j * kBlock;
-    if (j + 1 < nblk) pf_fetch(stage, stage_s, k, ks, base_tok + key0 + kBlock, len - key0 - kBlock);
-    const PfBlock& cur = s_k[j & 1];
-    const int col = key0 + lane;
-    if (key0 < wlim) {
-      float p[kPfRowsPerWave][4];
-#pragma unroll
-      for (int t = 0; t < 4; ++t) {
-        const v8i bop = pf_operand(cur, t);
-#pragma unroll
-        for (int r = 0; r < kPfRowsPerWave; ++r) {
-          float acc = 0.0f;
-#pragma unroll
-          for (int hg = 0; hg < 4; ++hg) {
-            const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[r][hg], bop, zero, 0, 0, 0, 0, 0, 0);
-            acc = relu_dot4(wf[r][hg], c, acc);
-          }
-          p[r][t] = acc;
-        }
-      }
-      const float sc = cur.scale[lane];
-#pragma unroll
-      for (int r = 0; r < kPfRowsPerWave; ++r) {
-        if (r < nrows) {
-          const float v = reduce_scatter4(p[r][0], p[r][1], p[r][2], p[r][3]) * sc;
-          if (col < col_end)
-            store_logit(logits + (base_tok + ir0 + r) * stride + col,
-                        select_f(col < ir0 + r + 1, v, kNegInfBits));
-        }
-      }
-    } else if (col < col_end) {
-      for (int r = 0; r < nrows; ++r) store_logit(logits + (base_tok + ir0 + r) * stride + col, ninf);
-    }
-    if (j + 1 < nblk) pf_store(s_k[(j + 1) & 1], stage, stage_s);
-    __syncthreads();
+  float* res = s_res[wave * kPfRowsPerWave];
+  // Scores block J (from LDS) while CUR (block J+1) is written to the other
+  // buffer and NXT receives block J+2; a macro rather than a lambda so the
+  // two register stages stay plain locals (by-reference stages end up in
+  // scratch memory).
+#define SAI_PF_STEP(J, CUR, NXT)                                                              \
+  {                                                                                           \
+    const int j_ = (J);                                                                       \
+    NXT = pf_fetch(k, ks, kbase + (int64_t)(j_ + 2) * kBlock, total);                         \
+    const int key0 = col0 + j_ * kBlock;                                                      \
+    const int col = key0 + lane;                                                              \
+    if (j_ < nblk && key0 < wlim) {                                                           \
+      const PfBlock& blk = s_k[j_ & 1];                                                       \
+      float p[kPfRowsPerWave][4];                                                             \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
+        const v8i bop = pf_operand(blk, t);                                                   \
+        _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                          \
+          float acc = 0.0f;                                                                   \
+          _Pragma("unroll") for (int hg = 0; hg < 4; ++hg) {                                  \
+            const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[r][hg], bop, zero, \
+                                                                           0, 0, 0, 0, 0, 0);  \
+            acc = relu_dot4(wf[r][hg], c, acc);                                               \
+          }                                                                                   \
+          p[r][t] = acc;                                                                      \
+        }                                                                                     \
+      }                                                                                       \
+      const float sc = blk.scale[lane];                                                       \
+      _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                            \
+        const float v = reduce_scatter4(p[r][0], p[r][1], p[r][2], p[r][3]) * sc;             \
+        res[r * kChunk + j_ * kBlock + lane] = select_f(col < ir0 + r + 1, v, kNegInfBits);   \
+      }                                                                                       \
+    } else {                                                                                  \
+      _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                              \
+        res[r * kChunk + j_ * kBlock + lane] = ninf;                                          \
+    }                                                                                         \
+    pf_store(s_k[(j_ + 1) & 1], CUR, len - (key0 + kBlock));                                   \
+    __syncthreads();                                                                          \
   }
-  // -inf for the chunk's columns past the staged blocks
-  for (int col = col0 + nblk * kBlock + lane; col < col_end; col += 64) {
-    for (int r = 0; r < nrows; ++r) store_logit(logits + (base_tok + ir0 + r) * stride + col, ninf);
+  for (int j = 0; j < nblk; j += 2) {
+    SAI_PF_STEP(j, sa, sb)
+    SAI_PF_STEP(j + 1, sb, sa)
+  }
+#undef SAI_PF_STEP
+
+  // write the wave's rows for the whole chunk: staged blocks, then -inf
+  const int nstaged = min(nblk * kBlock, col_end - col0);
+  for (int r = 0; r < nrows; ++r) {
+    float* dst = logits + (base_tok + ir0 + r) * stride + col0;
+    const float* src = res + r * kChunk;
+    if (vec) {
+      for (int x = 4 * lane; x < col_end - col0; x += 256) {
+        const float4 v = x < nstaged ? *reinterpret_cast<const float4*>(src + x)
+                                     : make_float4(ninf, ninf, ninf, ninf);
+        store_logit4(dst + x, v);
+      }
+    } else {
+      for (int x = lane; x < col_end - col0; x += 64) store_logit(dst + x, x < nstaged ? src[x] : ninf);
+    }
   }
 }
 
@@ -719,6 +754,6 @@ extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k
   hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)G), dim3(256), lds, stream,
                      (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_seq_lens,
                      batch, total_tokens, logits, logits_stride, row_len_out, row_req_out,
-                     (int32_t)nchunks, (int32_t)ntiles);
+                     (int32_t)nchunks, (int32_t)ntiles, logits_stride % 4 == 0 && aligned16(logits));
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }

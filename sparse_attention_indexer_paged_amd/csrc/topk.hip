@@ -182,24 +182,24 @@ struct BinPick {
 // Every lane of the calling wave gets the bin of hist[0..NB) that holds the
 // need-th largest element when bins are taken from the top down, and the
 // count above that bin; found is false if the histogram holds fewer than
-// need (with clamp_to_total, need is first lowered to the total).  Lane l reads the PER = NB/64 bins [NB-PER(l+1), NB-PER*l) with
-// 16-byte LDS loads; a DPP scan of the lane sums in lane order (descending
-// bins) finds the lane holding the need-th element, which walks its bins
-// downwards; the result is broadcast from that lane.
+// need (with clamp_to_total, need is first lowered to the total).  Lane l
+// owns the PER = NB/64 bins [NB-PER(l+1), NB-PER*l), read with 16-byte LDS
+// loads; a DPP scan of the lane sums in lane order (descending bins) finds
+// the lane holding the need-th element, which walks its bins downwards; the
+// result is broadcast from that lane.
 template <int NB>
 __device__ __forceinline__ BinPick pick_bin(const int* hist, int need, bool clamp_to_total = false) {
   constexpr int PER = NB / 64;
   const int lane = threadIdx.x & 63;
   const int lo = NB - PER * (lane + 1);
-  int h[PER];
+  // two passes over the lane's bins, 4 at a time, so the bins never occupy
+  // PER registers at once: the sum, then the walk
+  int sum = 0;
 #pragma unroll
   for (int j = 0; j < PER; j += 4) {
     const int4 v = *reinterpret_cast<const int4*>(hist + lo + j);
-    h[j] = v.x; h[j + 1] = v.y; h[j + 2] = v.z; h[j + 3] = v.w;
+    sum += v.x + v.y + v.z + v.w;
   }
-  int sum = 0;
-#pragma unroll
-  for (int j = 0; j < PER; ++j) sum += h[j];
   const int inc = wave_scan_dpp(sum);
   if (clamp_to_total) need = min(need, __builtin_amdgcn_readlane(inc, 63));
   const int acc = inc - sum;
@@ -208,11 +208,16 @@ __device__ __forceinline__ BinPick pick_bin(const int* hist, int need, bool clam
   // total stays below need are the ones above the chosen bin
   int run = 0, nbelow = 0, sum_above = 0;
 #pragma unroll
-  for (int j = PER - 1; j >= 0; --j) {
-    run += h[j];
-    const bool short_of = acc + run < need;
-    nbelow += short_of;
-    sum_above += short_of ? h[j] : 0;
+  for (int j = PER - 4; j >= 0; j -= 4) {
+    const int4 v = *reinterpret_cast<const int4*>(hist + lo + j);
+    const int h4[4] = {v.w, v.z, v.y, v.x};  // bins lo+j+3 .. lo+j
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      run += h4[q];
+      const bool short_of = acc + run < need;
+      nbelow += short_of;
+      sum_above += short_of ? h4[q] : 0;
+    }
   }
   const int bin = lo + PER - 1 - nbelow, above = acc + sum_above;
   const uint64_t m = __ballot(hit);
