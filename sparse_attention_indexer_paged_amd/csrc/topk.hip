@@ -164,14 +164,11 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
   return v;
 }
 
-#ifndef SAI_TOPK_THREADS
-#define SAI_TOPK_THREADS 1024
+#ifndef SAI_TOPK_MANY_WGS
+#define SAI_TOPK_MANY_WGS 512
 #endif
-#ifndef SAI_TOPK_SEG_VPT
-#define SAI_TOPK_SEG_VPT 16
-#endif
-constexpr int kRegThreads = SAI_TOPK_THREADS;
-constexpr int kSegVpt = SAI_TOPK_SEG_VPT;  // columns per thread of a row segment
+constexpr int kSegCols = 16384;              // columns per segment of a wide row
+constexpr int kManyWgs = SAI_TOPK_MANY_WGS;  // from this many workgroups on, use small ones
 constexpr int kCandMax = 64;               // threshold-bin keys resolved by brute force
 
 struct BinPick {
@@ -252,6 +249,11 @@ struct SlotMap {
   int32_t* out;
 };
 
+// Block-table rows of up to kBtLds entries are staged in LDS (dynamic
+// shared memory) at the start of the kernel, so the slot of every output
+// index is one LDS read instead of a dependent global load at the end.
+constexpr int kBtLds = 4096;
+
 __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t i) {
   if (i < 0 || b < 0 || b >= sm.batch || (int64_t)(i / 64) >= sm.bt_stride) return -1;
   const int32_t blk = sm.bt[(int64_t)b * sm.bt_stride + i / 64];
@@ -286,13 +288,14 @@ __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t
 // every winner its slot (the `need` lowest-index keys equal to T win), so
 // the winners come out in ascending position order; they are staged in LDS
 // and written with coalesced stores.
-template <int VPT, bool VEC, bool CIN, bool COUT>
-__global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
+template <int NT, int VPT, bool VEC, bool CIN, bool COUT>
+__global__ __launch_bounds__(NT) void topk_select_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
     int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
     int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col,
     SlotMap sm) {
-  constexpr int NT = kRegThreads, kWaves = NT / 64, SEG = VPT * NT;
+  constexpr int kWaves = NT / 64, SEG = VPT * NT;
+  static_assert(!COUT || SEG == kSegCols, "a segment pass covers exactly one segment");
   __shared__ __align__(16) int s_h0[kBins];
   __shared__ __align__(16) int s_h1[kBins];
   __shared__ uint32_t s_cand[kCandMax];
@@ -304,9 +307,30 @@ __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
   const int r = COUT ? (int)(blockIdx.x / nseg) : (int)blockIdx.x;
   const int len = (int)min((int64_t)max(row_len[r], 0), stride);
   const int32_t req = sm.out ? sm.row_req[r] : 0;
+  extern __shared__ int32_t s_bt[];  // [bt_stride] when bt_lds
+  const bool bt_lds = sm.out && sm.bt_stride <= kBtLds;
+  // whether this workgroup writes final indices (see the early returns below)
+  const bool emits = COUT ? (len > k && len <= kSegCols && blockIdx.x == (unsigned)r * nseg)
+                          : (!CIN || len <= k || len > kSegCols);
+  if (bt_lds && emits) {
+    const bool okr = req >= 0 && req < sm.batch;
+    for (int c = tid; c < (int)sm.bt_stride; c += NT) s_bt[c] = okr ? sm.bt[(int64_t)req * sm.bt_stride + c] : -1;
+    __syncthreads();
+  }
   auto emit = [&](int j, int32_t i) {  // final index j of row r
     out_idx[(int64_t)r * k + j] = i;
-    if (sm.out) sm.out[(int64_t)r * k + j] = slot_of(sm, req, i);
+    if (sm.out) {
+      int32_t slot = -1;
+      if (bt_lds) {
+        if (i >= 0 && i / 64 < (int)sm.bt_stride) {
+          const int32_t blk = s_bt[i / 64];
+          slot = blk >= 0 ? blk * 64 + i % 64 : -1;
+        }
+      } else {
+        slot = slot_of(sm, req, i);
+      }
+      sm.out[(int64_t)r * k + j] = slot;
+    }
   };
   if (len <= k) {  // the whole row wins; a segment pass leaves it to the merge
     if (!COUT)
@@ -315,7 +339,6 @@ __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
   }
   // In the split plan a row that fits one segment is finished by segment 0,
   // which writes the final indices; the other segments and the merge skip it.
-  constexpr int kSegCols = kSegVpt * NT;
   if (CIN && len <= kSegCols) return;
   if (COUT && len <= kSegCols && blockIdx.x != (unsigned)r * nseg) return;
   const bool final_out = !COUT || len <= kSegCols;
@@ -581,39 +604,85 @@ __global__ __launch_bounds__(kRegThreads) void topk_select_kernel(
   }
 }
 
-// How topk_rows handles a row pitch: rows up to 16 columns per thread are
-// selected in one pass; wider rows are cut into segments of kSegVpt columns
-// per thread whose winners are merged by a second pass, as long as the
-// candidate lists fit 16 per thread; wider still take the streaming kernel.
-struct TopkPlan {
-  int vpt;   // one-pass columns per thread (0 = not one-pass)
-  int nseg;  // segments per row (split plan)
-  int mvpt;  // merge candidates per thread (split plan)
-  bool stream;
+// How topk_rows handles a row pitch: rows up to kSegCols columns are
+// selected in one pass; wider rows are cut into kSegCols-column segments
+// whose winners are merged by a second pass, as long as a row's candidate
+// lists fit one workgroup (16384 slots); wider still take the streaming
+// kernel.  Workgroup shape: with at least kManyWgs workgroups the smallest
+// of 256 or 512 threads x 4..32 positions that holds the work, so several
+// workgroups share a CU; with fewer, 1024 threads x 4..16 positions, which
+// shortens each workgroup's chain.
+struct Shape {
+  int nt, vpt;  // nt == 0: no register-resident shape holds the work
 };
 
-TopkPlan plan_for(int64_t stride, int k) {
-  const int64_t nt = kRegThreads;
-  if (stride <= 4 * nt) return {4, 0, 0, false};
-  if (stride <= 8 * nt) return {8, 0, 0, false};
-  if (stride <= 16 * nt) return {16, 0, 0, false};
-  const int64_t nseg = (stride + kSegVpt * nt - 1) / (kSegVpt * nt);
-  const int64_t cand = nseg * k;
-  const int mvpt = cand <= 4 * nt ? 4 : cand <= 8 * nt ? 8 : cand <= 16 * nt ? 16 : 0;
-  if (mvpt == 0) return {0, 0, 0, true};
-  return {0, (int)nseg, mvpt, false};
+Shape shape_for(int64_t n, int64_t wgs) {
+  if (wgs >= kManyWgs) {
+    for (int nt : {256, 512})
+      for (int vpt : {4, 8, 16, 32})
+        if (n <= (int64_t)nt * vpt) return {nt, vpt};
+  }
+  for (int vpt : {4, 8, 16})
+    if (n <= 1024LL * vpt) return {1024, vpt};
+  return {0, 0};
 }
 
-template <int VPT, bool CIN, bool COUT>
+struct TopkPlan {
+  Shape one;    // one-pass shape (nt == 0: not one-pass)
+  int nseg;     // segments per row (split plan)
+  Shape seg;    // segment pass
+  Shape merge;  // merge pass
+  bool stream;  // neither: the streaming kernel
+};
+
+TopkPlan plan_for(int64_t stride, int k, int64_t rows) {
+  if (stride <= kSegCols) return {shape_for(stride, rows), 0, {0, 0}, {0, 0}, false};
+  const int64_t nseg = (stride + kSegCols - 1) / kSegCols;
+  const Shape merge = shape_for(nseg * k, rows);
+  if (merge.nt == 0) return {{0, 0}, 0, {0, 0}, {0, 0}, true};
+  return {{0, 0}, (int)nseg, shape_for(kSegCols, rows * nseg), merge, false};
+}
+
+template <int NT, int VPT, bool CIN, bool COUT>
 void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, const int32_t* row_len,
                 int32_t k, int32_t nseg, const uint32_t* c_key, const int32_t* c_col, int32_t* out,
                 uint32_t* o_key, int32_t* o_col, const SlotMap& sm, hipStream_t s) {
+  const size_t dyn = sm.out && sm.bt_stride <= kBtLds ? (size_t)sm.bt_stride * sizeof(int32_t) : 0;
   if (vec)
-    hipLaunchKernelGGL((topk_select_kernel<VPT, true, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
+    hipLaunchKernelGGL((topk_select_kernel<NT, VPT, true, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
                        logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
   else
-    hipLaunchKernelGGL((topk_select_kernel<VPT, false, CIN, COUT>), dim3(grid), dim3(kRegThreads), 0, s,
+    hipLaunchKernelGGL((topk_select_kernel<NT, VPT, false, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
                        logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+}
+
+// Launches the shape's instantiation (segment passes exist only for the
+// shapes that cover exactly one segment).
+template <bool CIN, bool COUT>
+void launch_shape(Shape sh, bool vec, unsigned grid, const float* logits, int64_t stride,
+                  const int32_t* row_len, int32_t k, int32_t nseg, const uint32_t* c_key,
+                  const int32_t* c_col, int32_t* out, uint32_t* o_key, int32_t* o_col,
+                  const SlotMap& sm, hipStream_t s) {
+#define SAI_SEL_CASE(NT_, VPT_)                                                                  \
+  if constexpr (!COUT || NT_ * VPT_ == kSegCols) {                                              \
+    if (sh.nt == NT_ && sh.vpt == VPT_) {                                                       \
+      launch_sel<NT_, VPT_, CIN, COUT>(vec, grid, logits, stride, row_len, k, nseg, c_key, c_col, \
+                                       out, o_key, o_col, sm, s);                               \
+      return;                                                                                   \
+    }                                                                                           \
+  }
+  SAI_SEL_CASE(256, 4)
+  SAI_SEL_CASE(256, 8)
+  SAI_SEL_CASE(256, 16)
+  SAI_SEL_CASE(256, 32)
+  SAI_SEL_CASE(512, 4)
+  SAI_SEL_CASE(512, 8)
+  SAI_SEL_CASE(512, 16)
+  SAI_SEL_CASE(512, 32)
+  SAI_SEL_CASE(1024, 4)
+  SAI_SEL_CASE(1024, 8)
+  SAI_SEL_CASE(1024, 16)
+#undef SAI_SEL_CASE
 }
 
 bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
@@ -622,7 +691,7 @@ bool aligned16p(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) =
 
 extern "C" size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k) {
   if (rows <= 0 || logits_stride <= 0 || k < 1 || k > SAI_TOPK_MAX) return 0;
-  const TopkPlan p = plan_for(logits_stride, k);
+  const TopkPlan p = plan_for(logits_stride, k, rows);
   if (p.nseg == 0) return 0;
   // candidate keys then candidate columns, [rows][nseg][k] each
   return (size_t)rows * (size_t)p.nseg * (size_t)k * 8u;
@@ -640,32 +709,25 @@ int topk_impl(const float* logits, int64_t logits_stride, const int32_t* row_len
   if (!logits || !row_len || !out_idx || logits_stride == 0) return SAI_EINVAL;
   if (logits_stride > 0x7FFFFFFF - 4 * kThreads) return SAI_EUNSUPPORTED;
   const bool vec = (logits_stride % 4 == 0) && aligned16p(logits);
-  const TopkPlan p = plan_for(logits_stride, k);
+  const TopkPlan p = plan_for(logits_stride, k, rows);
   const unsigned ur = (unsigned)rows;
   if (p.nseg > 0) {  // checked before anything is launched
     const size_t need = topk_workspace_bytes(rows, logits_stride, k);
     if (!workspace || workspace_bytes < need) return SAI_EWORKSPACE;
     if ((int64_t)rows * p.nseg > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   }
-  if (p.vpt == 4) {
-    launch_sel<4, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
-  } else if (p.vpt == 8) {
-    launch_sel<8, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
-  } else if (p.vpt == 16) {
-    launch_sel<16, false, false>(vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr, out_idx, nullptr, nullptr, sm, stream);
+  if (p.one.nt) {
+    launch_shape<false, false>(p.one, vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr,
+                               out_idx, nullptr, nullptr, sm, stream);
   } else if (p.nseg > 0) {
     uint32_t* ck = static_cast<uint32_t*>(workspace);
     int32_t* cc = reinterpret_cast<int32_t*>(ck + (size_t)rows * p.nseg * k);
     const bool cvec = (k % 4 == 0) && aligned16p(workspace);
     // the segment pass also writes the final output of rows that fit one segment
-    launch_sel<kSegVpt, false, true>(vec, ur * (unsigned)p.nseg, logits, logits_stride, row_len, k, p.nseg,
-                                     nullptr, nullptr, out_idx, ck, cc, sm, stream);
-    if (p.mvpt == 4)
-      launch_sel<4, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
-    else if (p.mvpt == 8)
-      launch_sel<8, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
-    else
-      launch_sel<16, true, false>(cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc, out_idx, nullptr, nullptr, sm, stream);
+    launch_shape<false, true>(p.seg, vec, ur * (unsigned)p.nseg, logits, logits_stride, row_len, k,
+                              p.nseg, nullptr, nullptr, out_idx, ck, cc, sm, stream);
+    launch_shape<true, false>(p.merge, cvec, ur, logits, logits_stride, row_len, k, p.nseg, ck, cc,
+                              out_idx, nullptr, nullptr, sm, stream);
   } else {
     *streamed = true;
     if (vec)

@@ -248,6 +248,27 @@ def test_topk_widest_rows(width, k):
     assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, k))
 
 
+@pytest.mark.parametrize("rows,width", [(520, 1000), (600, 9000), (600, 40000)])
+def test_topk_many_rows_small_workgroups(rows, width):
+    """At least 512 workgroups switch to 256/512-thread shapes (one pass,
+    segment pass and merge), with ties, short rows and tied thresholds."""
+    _say(f"topk_rows_slots: {rows} rows x {width}")
+    rng = np.random.default_rng(rows + width)
+    L = rng.standard_normal((rows, width)).astype(np.float32)
+    L[::7, ::3] = 0.25
+    L[5] = 1.0
+    lens = rng.integers(0, width + 1, size=rows).astype(np.int32)
+    lens[:4] = [width, 2048, 2049, 0]
+    nblk = -(-width // 64)
+    bt = rng.permutation(2 * nblk)[:nblk].reshape(1, nblk).astype(np.int32)
+    req = np.zeros(rows, np.int32)
+    T = lambda a: torch.from_numpy(a).to(DEV)  # noqa: E731
+    idx, slots = sai.topk_rows_slots(T(L), T(lens), T(req), T(bt), 2048)
+    want = O.topk_rows(L, lens, 2048)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, req, bt))
+
+
 def test_topk_unaligned_stride():
     _say("topk_rows: odd stride")
     rng = np.random.default_rng(4)
