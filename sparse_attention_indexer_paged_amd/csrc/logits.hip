@@ -449,24 +449,37 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
 // ------------------------------------------------------------------ prefill
 // Prefill is fp8-MFMA / VALU co-bound (every key is reused by all later
 // tokens), so K is staged once per workgroup in LDS and shared by its waves.
-// Workgroup = 8 consecutive tokens of one request (4 waves x 2 query rows,
-// Q in VGPRs) x a key chunk of 16 blocks (1024 columns).  The chunk's K
-// blocks stream through a double-buffered LDS image: all 256 threads fetch
-// the next block with coalesced 16-byte loads while the current one is
-// scored, then write it to LDS with the 16-byte chunk c of key n at position
-// c ^ (n & 7) of the key's row, so the MFMA operand reads (lanes n = 0..15 of
-// one key tile at a 128-byte stride) spread over all LDS banks.  Every
-// column of the chunk is written for the tile's rows (-inf past each row's
-// causal limit).  Grid ids are ordered tile-major and remapped so the chunks
-// of one tile run on one XCD and share its Q in that XCD's L2.
+// Workgroup = kPfTileRows consecutive tokens of one request (kPfWaves waves
+// x kPfRowsPerWave query rows, Q in VGPRs, head weights read from LDS) x a
+// key chunk of 16 blocks (1024 columns).  The chunk's K blocks stream
+// through a double-buffered LDS image: all threads fetch a later block with
+// coalesced 16-byte loads while the current one is scored, then write it to
+// LDS with the 16-byte chunk c of key n at position c ^ (n & 7) of the key's
+// row, so the MFMA operand reads (lanes n = 0..15 of one key tile at a
+// 128-byte stride) spread over all LDS banks.  Every column of the chunk is
+// written for the tile's rows (-inf past each row's causal limit).  Tiles
+// are dealt to XCDs by tile % 8, heaviest first.
 #ifndef SAI_PF_ROWS
 #define SAI_PF_ROWS 1
+#endif
+#ifndef SAI_PF_WAVES
+#define SAI_PF_WAVES 4
+#endif
+#ifndef SAI_PF_WF_LDS
+#define SAI_PF_WF_LDS 0
+#endif
+#ifndef SAI_PF_DEPTH
+#define SAI_PF_DEPTH 2
 #endif
 #ifndef SAI_PF_WAVES_PER_EU
 #define SAI_PF_WAVES_PER_EU 0
 #endif
 constexpr int kPfRowsPerWave = SAI_PF_ROWS;
-constexpr int kPfTileRows = 4 * kPfRowsPerWave;
+constexpr int kPfWaves = SAI_PF_WAVES;
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfTileRows = kPfWaves * kPfRowsPerWave;
+constexpr int kPfChunksPerThread = 512 / kPfThreads;  // 16-byte chunks of a K block per thread
+static_assert(kPfChunksPerThread * kPfThreads == 512, "a K block is 512 chunks of 16 bytes");
 constexpr int kPfChunkBlocks = 16;
 constexpr int kChunk = kPfChunkBlocks * kBlock;
 
@@ -484,16 +497,19 @@ __device__ __forceinline__ int pf_swz(int n, int c) { return n * 8 + (c ^ (n & 7
 // [0, total) so that all of them are in flight together; keys past the
 // request are zeroed when the block is written to LDS.
 struct PfStage {
-  uint4 c0, c1;  // chunks t and t+256
-  float s;       // scale of key t % 64
+  uint4 c[kPfChunksPerThread];  // chunks t + kPfThreads * e
+  float s;                      // scale of key t % 64
 };
 
 __device__ __forceinline__ PfStage pf_fetch(const uint8_t* __restrict__ k, const float* __restrict__ ks,
                                             int64_t key0, int64_t total) {
   const int t = threadIdx.x;
   PfStage st;
-  st.c0 = *reinterpret_cast<const uint4*>(k + min64(key0 + (t >> 3), total - 1) * kDim + (t & 7) * 16);
-  st.c1 = *reinterpret_cast<const uint4*>(k + min64(key0 + 32 + (t >> 3), total - 1) * kDim + (t & 7) * 16);
+#pragma unroll
+  for (int e = 0; e < kPfChunksPerThread; ++e) {
+    const int chunk = t + kPfThreads * e;
+    st.c[e] = *reinterpret_cast<const uint4*>(k + min64(key0 + (chunk >> 3), total - 1) * kDim + (chunk & 7) * 16);
+  }
   st.s = ks[min64(key0 + (t & 63), total - 1)];
   return st;
 }
@@ -506,9 +522,11 @@ __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v
 
 __device__ __forceinline__ void pf_store(PfBlock& blk, const PfStage& st, int nvalid) {
   const int t = threadIdx.x;
-  const uint32_t m0 = (t >> 3) < nvalid ? ~0u : 0u, m1 = 32 + (t >> 3) < nvalid ? ~0u : 0u;
-  blk.code[pf_swz(t >> 3, t & 7)] = and4(st.c0, m0);
-  blk.code[pf_swz(32 + (t >> 3), t & 7)] = and4(st.c1, m1);
+#pragma unroll
+  for (int e = 0; e < kPfChunksPerThread; ++e) {
+    const int chunk = t + kPfThreads * e;
+    blk.code[pf_swz(chunk >> 3, chunk & 7)] = and4(st.c[e], (chunk >> 3) < nvalid ? ~0u : 0u);
+  }
   if (t < kBlock) blk.scale[t] = __uint_as_float(__float_as_uint(st.s) & (t < nvalid ? ~0u : 0u));
 }
 
@@ -525,7 +543,7 @@ __device__ __forceinline__ v8i pf_operand(const PfBlock& blk, int t) {
 #else
 #define SAI_PF_ATTR
 #endif
-__global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
+__global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ k,
     const float* __restrict__ ks, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
     float* __restrict__ logits, int64_t stride, int32_t* __restrict__ row_len_out,
@@ -538,7 +556,7 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
   __shared__ __align__(16) float s_res[kPfTileRows][kChunk];  // the chunk's logits per row
 
   int run = 0;
-  for (int base = 0; base < batch; base += 256) {
+  for (int base = 0; base < batch; base += kPfThreads) {
     const int b = base + threadIdx.x;
     int nt = 0;
     if (b < batch) {
@@ -546,17 +564,22 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
       nt = cdiv_i(len, kPfTileRows);
     }
     int tot;
-    const int e = block_exclusive_scan<256>(nt, scratch, &tot);
+    const int e = block_exclusive_scan<kPfThreads>(nt, scratch, &tot);
     if (b < batch) s_tile[b] = run + e;
     run += tot;
   }
   if (threadIdx.x == 0) s_tile[batch] = run;
   __syncthreads();
 
-  const int G = gridDim.x;
-  const int lg = (blockIdx.x & 7) * (G >> 3) + (blockIdx.x >> 3);
-  const int tile = lg / nchunks, chunk = lg - tile * nchunks;
-  if (tile >= s_tile[batch] || tile >= ntiles_max) return;
+  // Workgroup g runs on XCD g % 8.  Tiles are dealt to XCDs by tile % 8, so
+  // the causal work (later tiles see more keys) is spread evenly over the
+  // XCDs, and each XCD takes its tiles from the last (heaviest) down; the
+  // chunks of one tile are consecutive on one XCD and share its Q in L2.
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int t8 = (ntiles_max + 7) / 8;
+  const int tj = jx / nchunks, chunk = jx - tj * nchunks;
+  const int tile = (t8 - 1 - tj) * 8 + xcd;
+  if (tj >= t8 || tile >= s_tile[batch] || tile >= ntiles_max) return;
   int lo = 0, hi = batch;
   while (hi - lo > 1) {
     const int mid = (lo + hi) >> 1;
@@ -604,24 +627,32 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
   }
 
   __syncthreads();  // s_w
+  // head weights of lane (g, n): heads 16hg + 4g .. +3, read from LDS in
+  // the loop (SAI_PF_WF_LDS, saves 16 VGPRs per row) or kept in registers
+#if SAI_PF_WF_LDS
+  auto wfr = [&](int r, int hg) { return s_w[wave * kPfRowsPerWave + r][4 * hg + (lane >> 4)]; };
+#else
   float4 wf[kPfRowsPerWave][4];
 #pragma unroll
   for (int r = 0; r < kPfRowsPerWave; ++r)
 #pragma unroll
     for (int hg = 0; hg < 4; ++hg) wf[r][hg] = s_w[wave * kPfRowsPerWave + r][4 * hg + (lane >> 4)];
+  auto wfr = [&](int r, int hg) { return wf[r][hg]; };
+#endif
 
   // Software pipeline over the chunk's blocks: block j is scored from LDS
-  // buffer j%2 while block j+2 is fetched into registers and block j+1
-  // (fetched one step earlier) is written to the other buffer.  The loop is
-  // unrolled by two so the register stages alternate statically, and no
-  // global store sits in it (results go to s_res), so the in-order vmcnt
-  // accounting only ever waits for the older of the two fetches.
+  // buffer j%2 while block j+DEPTH is fetched into registers and block j+1
+  // (fetched DEPTH-1 steps earlier) is written to the other buffer.  The
+  // loop is unrolled by DEPTH so the register stages rotate statically, and
+  // no global store sits in it (results go to s_res), so the in-order vmcnt
+  // accounting only ever waits for the oldest fetch.
   const int64_t kbase = base_tok + col0;
-  PfStage sa, sb;
+  PfStage sa, sb, sc;
   if (nblk > 0) {
-    sa = pf_fetch(k, ks, kbase, total);
-    pf_store(s_k[0], sa, len - col0);  // waits for Q and w as well
+    sc = pf_fetch(k, ks, kbase, total);
+    pf_store(s_k[0], sc, len - col0);  // waits for Q and w as well
     sa = pf_fetch(k, ks, kbase + kBlock, total);
+    if (SAI_PF_DEPTH > 2) sb = pf_fetch(k, ks, kbase + 2 * kBlock, total);
   }
   __syncthreads();
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -633,40 +664,70 @@ __global__ __launch_bounds__(256) SAI_PF_ATTR void prefill_logits_kernel(
 #define SAI_PF_STEP(J, CUR, NXT)                                                              \
   {                                                                                           \
     const int j_ = (J);                                                                       \
-    NXT = pf_fetch(k, ks, kbase + (int64_t)(j_ + 2) * kBlock, total);                         \
+    NXT = pf_fetch(k, ks, kbase + (int64_t)(j_ + SAI_PF_DEPTH) * kBlock, total);              \
     const int key0 = col0 + j_ * kBlock;                                                      \
     const int col = key0 + lane;                                                              \
     if (j_ < nblk && key0 < wlim) {                                                           \
       const PfBlock& blk = s_k[j_ & 1];                                                       \
       float p[kPfRowsPerWave][4];                                                             \
-      _Pragma("unroll") for (int t = 0; t < 4; ++t) {                                         \
-        const v8i bop = pf_operand(blk, t);                                                   \
-        _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                          \
-          float acc = 0.0f;                                                                   \
-          _Pragma("unroll") for (int hg = 0; hg < 4; ++hg) {                                  \
-            const v4f c = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[r][hg], bop, zero, \
-                                                                           0, 0, 0, 0, 0, 0);  \
-            acc = relu_dot4(wf[r][hg], c, acc);                                               \
-          }                                                                                   \
-          p[r][t] = acc;                                                                      \
+      /* software pipeline over the 4 key tiles: tile t's MFMAs are issued  */                \
+      /* before tile t-1's ReLU-weighted sums, which never wait on them     */                \
+      v4f cprev[kPfRowsPerWave][4];                                                           \
+      _Pragma("unroll") for (int t = 0; t <= 4; ++t) {                                        \
+        v4f ccur[kPfRowsPerWave][4];                                                          \
+        if (t < 4) {                                                                          \
+          const v8i bop = pf_operand(blk, t);                                                 \
+          _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                          \
+            _Pragma("unroll") for (int hg = 0; hg < 4; ++hg)                                  \
+              ccur[r][hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                 \
+                  qa[r][hg], bop, zero, 0, 0, 0, 0, 0, 0);                                    \
         }                                                                                     \
+        if (t > 0) {                                                                          \
+          _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                        \
+            float acc = 0.0f;                                                                 \
+            _Pragma("unroll") for (int hg = 0; hg < 4; ++hg)                                  \
+              acc = relu_dot4(wfr(r, hg), cprev[r][hg], acc);                                 \
+            p[r][t - 1] = acc;                                                                \
+          }                                                                                   \
+        }                                                                                     \
+        if (t < 4)                                                                            \
+          _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                          \
+            _Pragma("unroll") for (int hg = 0; hg < 4; ++hg) cprev[r][hg] = ccur[r][hg];      \
+      }                                                                                       \
+      /* keep that order in the schedule: per tile its 2 operand reads, its  */               \
+      /* MFMAs, then the previous tile's 32 VALU ops per row                 */               \
+      _Pragma("unroll") for (int t = 0; t <= 4; ++t) {                                        \
+        if (t < 4) {                                                                          \
+          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                  \
+          __builtin_amdgcn_sched_group_barrier(0x008, 4 * kPfRowsPerWave, 0);                 \
+        }                                                                                     \
+        if (t > 0) __builtin_amdgcn_sched_group_barrier(0x002, 32 * kPfRowsPerWave, 0);       \
       }                                                                                       \
       const float sc = blk.scale[lane];                                                       \
       _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                            \
         const float v = reduce_scatter4(p[r][0], p[r][1], p[r][2], p[r][3]) * sc;             \
         res[r * kChunk + j_ * kBlock + lane] = select_f(col < ir0 + r + 1, v, kNegInfBits);   \
       }                                                                                       \
-    } else {                                                                                  \
+    } else if (j_ < nblk) { /* steps past the last block write nothing */                   \
       _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                              \
         res[r * kChunk + j_ * kBlock + lane] = ninf;                                          \
     }                                                                                         \
     pf_store(s_k[(j_ + 1) & 1], CUR, len - (key0 + kBlock));                                   \
     __syncthreads();                                                                          \
   }
+#if SAI_PF_DEPTH > 2
+  // stages rotate: CUR holds block j+1 (fetched two steps ago), NXT gets j+3
+  for (int j = 0; j < nblk; j += 3) {
+    SAI_PF_STEP(j, sa, sc)
+    SAI_PF_STEP(j + 1, sb, sa)
+    SAI_PF_STEP(j + 2, sc, sb)
+  }
+#else
   for (int j = 0; j < nblk; j += 2) {
     SAI_PF_STEP(j, sa, sb)
     SAI_PF_STEP(j + 1, sb, sa)
   }
+#endif
 #undef SAI_PF_STEP
 
   // write the wave's rows for the whole chunk: staged blocks, then -inf
@@ -747,11 +808,11 @@ extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k
   if (batch > 4096 || logits_stride > 0x7FFFFFFF - kChunk) return SAI_EUNSUPPORTED;
   const int64_t nchunks = (logits_stride + kChunk - 1) / kChunk;
   const int64_t ntiles = (total_tokens + kPfTileRows - 1) / kPfTileRows + batch;
-  int64_t G = nchunks * ntiles;
-  G = (G + 7) / 8 * 8;
+  const int64_t G = 8 * ((ntiles + 7) / 8) * nchunks;
   if (G > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  const size_t lds = (size_t)((batch + 1) + 8) * sizeof(int);
-  hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)G), dim3(256), lds, stream,
+  // prefix of query tiles [batch+1] + the block scan's scratch [waves+1]
+  const size_t lds = (size_t)((batch + 1) + kPfWaves + 1) * sizeof(int);
+  hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)G), dim3(kPfThreads), lds, stream,
                      (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_seq_lens,
                      batch, total_tokens, logits, logits_stride, row_len_out, row_req_out,
                      (int32_t)nchunks, (int32_t)ntiles, logits_stride % 4 == 0 && aligned16(logits));
