@@ -505,12 +505,20 @@ __device__ __forceinline__ PfStage pf_fetch(const uint8_t* __restrict__ k, const
                                             int64_t key0, int64_t total) {
   const int t = threadIdx.x;
   PfStage st;
+  if (key0 + kBlock <= total) {  // wave-uniform: the block lies inside the buffer, no clamp
+    const uint8_t* kb = k + key0 * kDim;
 #pragma unroll
-  for (int e = 0; e < kPfChunksPerThread; ++e) {
-    const int chunk = t + kPfThreads * e;
-    st.c[e] = *reinterpret_cast<const uint4*>(k + min64(key0 + (chunk >> 3), total - 1) * kDim + (chunk & 7) * 16);
+    for (int e = 0; e < kPfChunksPerThread; ++e)
+      st.c[e] = *reinterpret_cast<const uint4*>(kb + (t + kPfThreads * e) * 16);
+    st.s = ks[key0 + (t & 63)];
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPfChunksPerThread; ++e) {
+      const int chunk = t + kPfThreads * e;
+      st.c[e] = *reinterpret_cast<const uint4*>(k + min64(key0 + (chunk >> 3), total - 1) * kDim + (chunk & 7) * 16);
+    }
+    st.s = ks[min64(key0 + (t & 63), total - 1)];
   }
-  st.s = ks[min64(key0 + (t & 63), total - 1)];
   return st;
 }
 
@@ -522,12 +530,21 @@ __device__ __forceinline__ uint4 and4(uint4 v, uint32_t m) { return make_uint4(v
 
 __device__ __forceinline__ void pf_store(PfBlock& blk, const PfStage& st, int nvalid) {
   const int t = threadIdx.x;
+  if (nvalid >= kBlock) {  // wave-uniform: every key of the block belongs to the request
 #pragma unroll
-  for (int e = 0; e < kPfChunksPerThread; ++e) {
-    const int chunk = t + kPfThreads * e;
-    blk.code[pf_swz(chunk >> 3, chunk & 7)] = and4(st.c[e], (chunk >> 3) < nvalid ? ~0u : 0u);
+    for (int e = 0; e < kPfChunksPerThread; ++e) {
+      const int chunk = t + kPfThreads * e;
+      blk.code[pf_swz(chunk >> 3, chunk & 7)] = st.c[e];
+    }
+    if (t < kBlock) blk.scale[t] = st.s;
+  } else {
+#pragma unroll
+    for (int e = 0; e < kPfChunksPerThread; ++e) {
+      const int chunk = t + kPfThreads * e;
+      blk.code[pf_swz(chunk >> 3, chunk & 7)] = and4(st.c[e], (chunk >> 3) < nvalid ? ~0u : 0u);
+    }
+    if (t < kBlock) blk.scale[t] = __uint_as_float(__float_as_uint(st.s) & (t < nvalid ? ~0u : 0u));
   }
-  if (t < kBlock) blk.scale[t] = __uint_as_float(__float_as_uint(st.s) & (t < nvalid ? ~0u : 0u));
 }
 
 // B operand of key tile t: lane (g, n) takes 16-byte columns g and 4+g of key
@@ -673,10 +690,12 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
       /* software pipeline over the 4 key tiles: tile t's MFMAs are issued  */                \
       /* before tile t-1's ReLU-weighted sums, which never wait on them     */                \
       v4f cprev[kPfRowsPerWave][4];                                                           \
+      v8i bops[4]; /* all 4 key tiles' operands are read up front */                          \
+      _Pragma("unroll") for (int t = 0; t < 4; ++t) bops[t] = pf_operand(blk, t);             \
       _Pragma("unroll") for (int t = 0; t <= 4; ++t) {                                        \
         v4f ccur[kPfRowsPerWave][4];                                                          \
         if (t < 4) {                                                                          \
-          const v8i bop = pf_operand(blk, t);                                                 \
+          const v8i bop = bops[t];                                                            \
           _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                          \
             _Pragma("unroll") for (int hg = 0; hg < 4; ++hg)                                  \
               ccur[r][hg] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(                 \
@@ -694,13 +713,11 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
           _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                          \
             _Pragma("unroll") for (int hg = 0; hg < 4; ++hg) cprev[r][hg] = ccur[r][hg];      \
       }                                                                                       \
-      /* keep that order in the schedule: per tile its 2 operand reads, its  */               \
-      /* MFMAs, then the previous tile's 32 VALU ops per row                 */               \
+      /* keep that order in the schedule: the 8 operand reads, then per tile */               \
+      /* its MFMAs followed by the previous tile's 32 VALU ops per row      */               \
+      __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);                                      \
       _Pragma("unroll") for (int t = 0; t <= 4; ++t) {                                        \
-        if (t < 4) {                                                                          \
-          __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                                  \
-          __builtin_amdgcn_sched_group_barrier(0x008, 4 * kPfRowsPerWave, 0);                 \
-        }                                                                                     \
+        if (t < 4) __builtin_amdgcn_sched_group_barrier(0x008, 4 * kPfRowsPerWave, 0);        \
         if (t > 0) __builtin_amdgcn_sched_group_barrier(0x002, 32 * kPfRowsPerWave, 0);       \
       }                                                                                       \
       const float sc = blk.scale[lane];                                                       \
