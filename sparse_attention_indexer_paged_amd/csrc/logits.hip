@@ -349,13 +349,16 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     if (row_req_out) row_req_out[r] = b;
   }
 
-  auto find = [&](const int* pre, int u) {  // last b with pre[b] <= u
-    int lo = 0, hi = batch;
-    while (hi - lo > 1) {
-      const int mid = (lo + hi) >> 1;
-      if (pre[mid] <= u) lo = mid; else hi = mid;
-    }
-    return lo;
+  // last b in [0, batch) with pre[b] <= u (pre non-decreasing, pre[0] = 0
+  // <= u; called wave-uniformly): a coarse ballot over every cs-th entry,
+  // then a fine one inside the chosen stretch of cs <= 64 entries
+  auto find = [&](const int* pre, int u) {
+    const int cs = (batch + 63) >> 6;
+    const uint64_t mc = __ballot(pre[min(lane * cs, batch - 1)] <= u);
+    const int c = min(63 - (int)__builtin_clzll(mc), (batch - 1) / cs);
+    const int j = c * cs + lane;
+    const uint64_t mf = __ballot(lane < cs && j < batch && pre[min(j, batch - 1)] <= u);
+    return c * cs + (63 - (int)__builtin_clzll(mf));
   };
 
   // Writes the staged units [sa, sb) (stage slots 0 .. sb-sa-1; unit sa
