@@ -105,21 +105,11 @@ __device__ __forceinline__ v8i make_v8i(uint4 a, uint4 b) {
   return r;
 }
 
-// Paged block: values at `blk`, scales at blk + 8192.
-__device__ __forceinline__ void load_kfrag_paged(KFrag& f, const uint8_t* __restrict__ blk) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const uint8_t* row = blk + (tile_key(t) + n) * kDim + 16 * g;
-    f.v[2 * t] = *reinterpret_cast<const uint4*>(row);
-    f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(row + 64);
-  }
-  f.s = *reinterpret_cast<const float*>(blk + kValueBytes + 4 * lane);
-}
-
-// Loads of one paged block in operand order, or -- when !real -- the same
-// number of loads all aimed at the first 16 bytes of `dummy`, so every path
-// issues an identical instruction stream (the data is then ignored).
+// Loads of one paged block (values, then scales at blk + 8192) in operand
+// order: lane (g, n) of key tile t takes bytes [16g, 16g+16) and
+// [64+16g, 64+16g+16) of key tile_key(t)+n.  When !real, the same number of
+// loads all aim at the first 16 bytes of `dummy`, so every path issues an
+// identical instruction stream (the data is then ignored).
 __device__ __forceinline__ void load_kfrag_or_dummy(KFrag& f, const uint8_t* __restrict__ blk,
                                                     const uint8_t* __restrict__ dummy, bool real) {
   const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
@@ -131,33 +121,6 @@ __device__ __forceinline__ void load_kfrag_or_dummy(KFrag& f, const uint8_t* __r
     f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(base + off + (real ? 64 : 0));
   }
   f.s = *reinterpret_cast<const float*>(base + (real ? kValueBytes + 4 * lane : 0));
-}
-
-// Contiguous K: keys [key0, key0+64) of `k` ([*,128] codes) and `ks`; keys at
-// or past `nvalid` (relative to key0) are not read and contribute zeros.
-__device__ __forceinline__ void load_kfrag_contig(KFrag& f, const uint8_t* __restrict__ k,
-                                                  const float* __restrict__ ks, int64_t key0,
-                                                  int nvalid) {
-  const int lane = threadIdx.x & 63, g = lane >> 4, n = lane & 15;
-#pragma unroll
-  for (int t = 0; t < 4; ++t) {
-    const int key = tile_key(t) + n;
-    if (key < nvalid) {
-      const uint8_t* row = k + (key0 + key) * kDim + 16 * g;
-      f.v[2 * t] = *reinterpret_cast<const uint4*>(row);
-      f.v[2 * t + 1] = *reinterpret_cast<const uint4*>(row + 64);
-    } else {
-      f.v[2 * t] = make_uint4(0, 0, 0, 0);
-      f.v[2 * t + 1] = make_uint4(0, 0, 0, 0);
-    }
-  }
-  f.s = lane < nvalid ? ks[key0 + lane] : 0.0f;
-}
-
-__device__ __forceinline__ void zero_kfrag(KFrag& f) {
-#pragma unroll
-  for (int i = 0; i < 8; ++i) f.v[i] = make_uint4(0, 0, 0, 0);
-  f.s = 0.0f;
 }
 
 // A operands of one query row ([64 heads][128] codes): head group hg holds
