@@ -39,6 +39,9 @@ using namespace sai;
 #ifndef SAI_DECODE_STAGE
 #define SAI_DECODE_STAGE 2048
 #endif
+#ifndef SAI_DECODE_FILL_FIRST
+#define SAI_DECODE_FILL_FIRST 1
+#endif
 
 namespace {
 
@@ -351,6 +354,33 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     }
   };
 
+#if SAI_DECODE_FILL_FIRST
+  // The -inf fill needs only the context lengths, so its stores go out
+  // before the K stream starts and complete while the first loads wait.
+  const int F = s_fill[batch];
+  int f = (int)((int64_t)F * w / nw);
+  const int f1 = (int)((int64_t)F * (w + 1) / nw);
+  if (f < f1) {
+    int b = find(s_fill, f);
+    const float ninf = __uint_as_float(kNegInfBits);
+    const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
+    for (; f < f1; ++f) {
+      while (s_fill[b + 1] <= f) ++b;
+      const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
+#pragma unroll
+      for (int r = 0; r < NN; ++r) {
+        float* row = logits + ((int64_t)b * NN + r) * stride;
+        if (vec) {
+          if (col + 4 * lane < stride) store_logit4(row + col + 4 * lane, ninf4);
+        } else {
+#pragma unroll
+          for (int k = 0; k < kFillCols / 64; ++k)
+            if (col + 64 * k + lane < stride) store_logit(row + col + 64 * k + lane, ninf);
+        }
+      }
+    }
+  }
+#endif
   const int U = s_unit[batch];
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
@@ -386,7 +416,7 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     u += n;
   }
   if (sa < u1) flush(sa, u1, bs);
-
+#if !SAI_DECODE_FILL_FIRST
   const int F = s_fill[batch];
   int f = (int)((int64_t)F * w / nw);
   const int f1 = (int)((int64_t)F * (w + 1) / nw);
@@ -410,6 +440,8 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       }
     }
   }
+#endif
+
 }
 
 // ------------------------------------------------------------------ prefill
