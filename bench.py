@@ -14,10 +14,9 @@ several pools (4 x 169 MB > the 256 MB Infinity Cache) and steps rotate over
 them, so every step streams its K from HBM rather than from the MALL.
 
 Printed: one JSON line with the metric, per-step time, the roofline of the
-dominant kernel (paged_mqa_logits; its average duration from HIP events on
-its stream, placed around it on every 5th step of the timed region because
-each event record adds a stream packet between the kernels), a parity check
-of the run's own outputs
+dominant kernel (paged_mqa_logits; its average duration from a HIP event
+pair carried in its own dispatch on every 5th step of the timed region,
+armed with sai_time_next_launch), a parity check of the run's own outputs
 against the CPU oracle on sampled rows, and the oracle's own throughput on
 the host cores (cpu_baseline).
 """
@@ -274,8 +273,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-graph", action="store_true", help="skip the hipGraph replay figure")
     ap.add_argument("--event-every", type=int, default=5,
-                    help="bracket the dominant kernel with HIP events on every N-th timed step "
-                         "(each event pair adds a stream packet, ~3 us per step)")
+                    help="time the dominant kernel with dispatch-carried HIP events on every N-th "
+                         "timed step (arming adds ~1 us to a step)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device once (a known-size "
                          "transfer that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -321,7 +320,8 @@ def main():
     every = max(1, args.event_every)
     timed = [i for i in range(K) if i % every == 0]
     e0, e1 = ev.create(len(timed)), ev.create(len(timed))
-    rec = ev.hip.hipEventRecord
+    # the events ride in the dominant kernel's own dispatch (no marker packets)
+    arm = lib.sai_time_next_launch
     before = [fn for _, fn in calls[:dom]]
     dom_fn = calls[dom][1]
     after = [fn for _, fn in calls[dom + 1:]]
@@ -331,9 +331,8 @@ def main():
         for fn in before:
             fn(i)
         if i % every == 0:
-            rec(e0[i // every], s_ptr)
+            arm(e0[i // every], e1[i // every])
             dom_fn(i)
-            rec(e1[i // every], s_ptr)
         else:
             dom_fn(i)
         for fn in after:

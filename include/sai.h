@@ -59,6 +59,19 @@ extern "C" {
 const char* sai_status_string(int status);
 
 /*
+ * sai_time_next_launch -- profiling aid (not an operation of the pages).
+ * Arms a pair of events (created by the caller with hipEventCreate*) for the
+ * next kernel that the calling thread launches through any entry point
+ * below: that launch carries them in its own dispatch, so
+ * hipEventElapsedTime(start, stop) is the kernel's execution time without
+ * the marker packets a separate hipEventRecord adds to the stream.  The pair
+ * is used once; entry points that launch several kernels time the first.
+ * Both NULL disarms.  SAI_EINVAL if exactly one is NULL.  Per thread; no
+ * device work.
+ */
+int sai_time_next_launch(hipEvent_t start, hipEvent_t stop);
+
+/*
  * indexer_k_cache_write -- quantise K rows to fp8 and scatter them into the
  * paged indexer K cache.
  *

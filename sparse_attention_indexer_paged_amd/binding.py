@@ -28,6 +28,7 @@ _i64 = ctypes.c_int64
 # name -> argtypes (restype int unless listed in _RESTYPE)
 SIGNATURES = {
     "sai_status_string": [ctypes.c_int],
+    "sai_time_next_launch": [_c_void_p, _c_void_p],
     "indexer_k_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
     "indexer_q_quant": [_c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "gather_indexer_k": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32, _i64, _c_void_p,

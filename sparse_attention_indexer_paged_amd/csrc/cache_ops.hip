@@ -18,6 +18,12 @@ extern "C" const char* sai_status_string(int status) {
   }
 }
 
+extern "C" int sai_time_next_launch(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return SAI_EINVAL;
+  g_launch_timing = LaunchTiming{start, stop};
+  return SAI_OK;
+}
+
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 static inline int launch_status() {
@@ -74,7 +80,7 @@ extern "C" int indexer_k_cache_write(const void* k_bf16, int64_t k_row_stride,
     return SAI_EINVAL;
   const int64_t grid = (n + 15) / 16;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  hipLaunchKernelGGL(k_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+  launch(k_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                      (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n,
                      (uint8_t*)kv_cache, num_blocks);
   return launch_status();
@@ -131,7 +137,7 @@ extern "C" int indexer_q_quant(const void* q_bf16, const float* weights, int64_t
   if (!q_bf16 || !weights || !q_fp8 || !w_eff || !aligned16(q_bf16) || !aligned16(q_fp8))
     return SAI_EINVAL;
   if (rows > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  hipLaunchKernelGGL(q_quant_kernel, dim3((unsigned)rows), dim3(256), 0, stream,
+  launch(q_quant_kernel, dim3((unsigned)rows), dim3(256), 0, stream,
                      (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale);
   return launch_status();
 }
@@ -180,7 +186,7 @@ extern "C" int gather_indexer_k(const void* kv_cache, int64_t num_blocks, const 
   if (!aligned16(kv_cache) || !aligned16(out_k_fp8)) return SAI_EINVAL;
   const int64_t grid = (total_tokens + 31) / 32;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  hipLaunchKernelGGL(gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
+  launch(gather_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
                      (const uint8_t*)kv_cache, num_blocks, block_table, bt_stride, cu_seq_lens,
                      batch, total_tokens, (uint8_t*)out_k_fp8, out_scale);
   return launch_status();
@@ -254,14 +260,14 @@ extern "C" int topk_to_global_slots(const int32_t* topk_idx, const int32_t* row_
   if (rows == 0 || k == 0) return SAI_OK;
   if (!topk_idx || !row_req || !block_table || !out_slots) return SAI_EINVAL;
   if (k <= 256 * kSlotPerThread && bt_stride <= kSlotLdsEntries) {
-    hipLaunchKernelGGL(slots_row_kernel, dim3(rows), dim3(256), 0, stream, topk_idx, row_req,
+    launch(slots_row_kernel, dim3(rows), dim3(256), 0, stream, topk_idx, row_req,
                        block_table, bt_stride, batch, k, out_slots);
     return launch_status();
   }
   const int64_t total = (int64_t)rows * k;
   const int64_t grid = (total + 255) / 256;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  hipLaunchKernelGGL(slots_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, row_req,
+  launch(slots_kernel, dim3(grid), dim3(256), 0, stream, topk_idx, row_req,
                      block_table, bt_stride, batch, total, k, out_slots);
   return launch_status();
 }

@@ -39,9 +39,6 @@ using namespace sai;
 #ifndef SAI_DECODE_STAGE
 #define SAI_DECODE_STAGE 2048
 #endif
-#ifndef SAI_DECODE_FILL_FIRST
-#define SAI_DECODE_FILL_FIRST 1
-#endif
 
 namespace {
 
@@ -354,7 +351,6 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     }
   };
 
-#if SAI_DECODE_FILL_FIRST
   // The -inf fill needs only the context lengths, so its stores go out
   // before the K stream starts and complete while the first loads wait.
   const int F = s_fill[batch];
@@ -380,7 +376,6 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       }
     }
   }
-#endif
   const int U = s_unit[batch];
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
@@ -416,32 +411,6 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     u += n;
   }
   if (sa < u1) flush(sa, u1, bs);
-#if !SAI_DECODE_FILL_FIRST
-  const int F = s_fill[batch];
-  int f = (int)((int64_t)F * w / nw);
-  const int f1 = (int)((int64_t)F * (w + 1) / nw);
-  if (f < f1) {
-    int b = find(s_fill, f);
-    const float ninf = __uint_as_float(kNegInfBits);
-    const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
-    for (; f < f1; ++f) {
-      while (s_fill[b + 1] <= f) ++b;
-      const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
-#pragma unroll
-      for (int r = 0; r < NN; ++r) {
-        float* row = logits + ((int64_t)b * NN + r) * stride;
-        if (vec) {
-          if (col + 4 * lane < stride) store_logit4(row + col + 4 * lane, ninf4);
-        } else {
-#pragma unroll
-          for (int k = 0; k < kFillCols / 64; ++k)
-            if (col + 64 * k + lane < stride) store_logit(row + col + 64 * k + lane, ninf);
-        }
-      }
-    }
-  }
-#endif
-
 }
 
 // ------------------------------------------------------------------ prefill
@@ -781,7 +750,7 @@ int launch_paged(const void* q, const float* w, const void* cache, int64_t num_b
     if (lds > (size_t)max_lds) return SAI_EUNSUPPORTED;
   }
   const bool vec = stride % 4 == 0 && aligned16(logits);
-  hipLaunchKernelGGL((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap>), dim3((unsigned)G),
+  launch((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap>), dim3((unsigned)G),
                      dim3(256), lds, s, (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt,
                      bt_stride, ctx, batch, logits, stride, rl, rr, vec);
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
@@ -827,7 +796,7 @@ extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k
   if (G > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   // prefix of query tiles [batch+1] + the block scan's scratch [waves+1]
   const size_t lds = (size_t)((batch + 1) + kPfWaves + 1) * sizeof(int);
-  hipLaunchKernelGGL(prefill_logits_kernel, dim3((unsigned)G), dim3(kPfThreads), lds, stream,
+  launch(prefill_logits_kernel, dim3((unsigned)G), dim3(kPfThreads), lds, stream,
                      (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_seq_lens,
                      batch, total_tokens, logits, logits_stride, row_len_out, row_req_out,
                      (int32_t)nchunks, (int32_t)ntiles, logits_stride % 4 == 0 && aligned16(logits));

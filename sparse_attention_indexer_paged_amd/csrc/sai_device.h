@@ -1,6 +1,7 @@
 // Device-side building blocks shared by the gfx950 indexer kernels.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -93,6 +94,24 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
   *total = scratch[NW];
   __syncthreads();
   return res;
+}
+
+// ---------------------------------------------------------------- launches
+// Every kernel goes through launch().  When the calling thread has armed a
+// start/stop event pair (sai_time_next_launch), its next launch carries the
+// pair in its own dispatch, so their elapsed time is that kernel's execution
+// alone; a separate hipEventRecord would add marker packets to the stream.
+struct LaunchTiming {
+  hipEvent_t start = nullptr;
+  hipEvent_t stop = nullptr;
+};
+inline thread_local LaunchTiming g_launch_timing;
+
+template <typename F, typename... Args>
+inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
+  const LaunchTiming t = g_launch_timing;
+  g_launch_timing = LaunchTiming{};
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t.start, t.stop, 0u, args...);
 }
 
 }  // namespace sai

@@ -649,10 +649,10 @@ void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, co
                 uint32_t* o_key, int32_t* o_col, const SlotMap& sm, hipStream_t s) {
   const size_t dyn = sm.out && sm.bt_stride <= kBtLds ? (size_t)sm.bt_stride * sizeof(int32_t) : 0;
   if (vec)
-    hipLaunchKernelGGL((topk_select_kernel<NT, VPT, true, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
+    launch((topk_select_kernel<NT, VPT, true, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
                        logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
   else
-    hipLaunchKernelGGL((topk_select_kernel<NT, VPT, false, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
+    launch((topk_select_kernel<NT, VPT, false, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
                        logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
 }
 
@@ -731,10 +731,10 @@ int topk_impl(const float* logits, int64_t logits_stride, const int32_t* row_len
   } else {
     *streamed = true;
     if (vec)
-      hipLaunchKernelGGL(topk_row_kernel<true>, dim3(rows), dim3(kThreads), 0, stream, logits,
+      launch(topk_row_kernel<true>, dim3(rows), dim3(kThreads), 0, stream, logits,
                          logits_stride, row_len, k, out_idx);
     else
-      hipLaunchKernelGGL(topk_row_kernel<false>, dim3(rows), dim3(kThreads), 0, stream, logits,
+      launch(topk_row_kernel<false>, dim3(rows), dim3(kThreads), 0, stream, logits,
                          logits_stride, row_len, k, out_idx);
   }
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;

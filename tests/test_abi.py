@@ -31,7 +31,8 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted([
-        "sai_status_string", "indexer_k_cache_write", "indexer_q_quant", "gather_indexer_k",
+        "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
+        "gather_indexer_k",
         "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
         "topk_to_global_slots", "topk_rows_slots"])
 
@@ -104,3 +105,11 @@ def test_topk_missing_workspace_is_rejected(lib):
     nul = ctypes.c_void_p(0)
     assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, nul, 0, nul) == SAI_EWORKSPACE
     assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, fake, 100, nul) == SAI_EWORKSPACE
+
+
+def test_time_next_launch_host_checks(lib):
+    """Arming needs both events or neither; no device work happens here."""
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    assert lib.sai_time_next_launch(fake, nul) == SAI_EINVAL
+    assert lib.sai_time_next_launch(nul, fake) == SAI_EINVAL
+    assert lib.sai_time_next_launch(nul, nul) == SAI_OK
