@@ -17,8 +17,11 @@ Printed: one JSON line with the metric, per-step time, the roofline of the
 dominant kernel (paged_mqa_logits; its average duration from a HIP event
 pair carried in its own dispatch on every 5th step of the timed region,
 armed with sai_time_next_launch), a parity check of the run's own outputs
-against the CPU oracle on sampled rows, and the oracle's own throughput on
-the host cores (cpu_baseline).
+against the CPU oracle on sampled rows, the oracle's own throughput on
+the host cores (cpu_baseline), and two reference points taken after the
+timed region: the bandwidth of a plain 1 GiB device copy on the same box and
+the dominant kernel's time when it re-reads one pool (hot_dominant_us, much
+of its K then comes from the memory-side cache).
 """
 import argparse
 import ctypes
@@ -275,6 +278,8 @@ def main():
     ap.add_argument("--event-every", type=int, default=5,
                     help="time the dominant kernel with dispatch-carried HIP events on every N-th "
                          "timed step (arming adds ~1 us to a step)")
+    ap.add_argument("--no-refs", action="store_true",
+                    help="skip the 1 GiB copy and hot-cache reference timings")
     ap.add_argument("--profile-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device once (a known-size "
                          "transfer that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -367,6 +372,37 @@ def main():
     except Exception as exc:  # noqa: BLE001
         print(f"graph replay skipped: {exc}", file=sys.stderr)
 
+    # Reference points on the same box, outside the timed region: a plain
+    # 1 GiB device-to-device copy (what the HBM sustains for a simple
+    # stream), and the dominant kernel "hot", launched on one cache pool
+    # every time so that much of its K is served by the 256 MB memory-side
+    # cache (labelled as such; not the headline).
+    copy_gbps, hot_us = None, None
+    if not args.no_refs:
+        n = 1 << 30
+        a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+        b = torch.empty_like(a)
+        b.copy_(a)
+        torch.cuda.synchronize()
+        ca, cb = ev.create(1), ev.create(1)
+        ev.hip.hipEventRecord(ca[0], s_ptr)
+        for _ in range(5):
+            b.copy_(a)
+        ev.hip.hipEventRecord(cb[0], s_ptr)
+        copy_gbps = 2 * n * 5 / (ev.elapsed_ms(ca[0], cb[0]) * 1e-3) / 1e9
+        ev.destroy(ca + cb)
+        del a, b
+        if not prefill:
+            for _ in range(5):
+                dom_fn(0)
+            h0, h1 = ev.create(20), ev.create(20)
+            for j in range(20):
+                arm(h0[j], h1[j])
+                dom_fn(0)
+            torch.cuda.synchronize()
+            hot_us = float(np.median([ev.elapsed_ms(h0[j], h1[j]) for j in range(20)])) * 1e3
+            ev.destroy(h0 + h1)
+
     if args.profile_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -432,6 +468,10 @@ def main():
         "fp8_mfma_frac": round(work["flops"] / t_dom_s / 1e12 / FP8_PEAK_TFLOPS, 4),
         "dominant_us_p10_p50_p90": [round(float(np.percentile(t_dom, p)) * 1e3, 3) for p in (10, 50, 90)],
         "dominant_event_steps": len(timed),
+        "copy_gbps": None if copy_gbps is None else round(copy_gbps, 1),
+        "alg_bytes_frac_of_copy": (None if copy_gbps is None or work["bound"] != "hbm"
+                                   else round(work["alg_bytes"] / t_dom_s / 1e9 / copy_gbps, 4)),
+        "hot_dominant_us": None if hot_us is None else round(hot_us, 3),
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "parity_sampled_rows": parity_ok,
         "cpu_baseline": cpu,
