@@ -170,6 +170,10 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 constexpr int kSegCols = 16384;              // columns per segment of a wide row
 constexpr int kManyWgs = SAI_TOPK_MANY_WGS;  // from this many workgroups on, use small ones
 constexpr int kCandMax = 64;               // threshold-bin keys resolved by brute force
+// Launches of at most this many workgroups are latency-bound: their rows'
+// loads go out before the row lengths are known (a few wasted reads of rows
+// that need no selection are cheaper than the extra round trip).
+constexpr unsigned kEarlyLoadWgs = 1024;
 
 struct BinPick {
   int bin, above;
@@ -288,7 +292,7 @@ __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t
 // every winner its slot (the `need` lowest-index keys equal to T win), so
 // the winners come out in ascending position order; they are staged in LDS
 // and written with coalesced stores.
-template <int NT, int VPT, bool VEC, bool CIN, bool COUT>
+template <int NT, int VPT, bool VEC, bool CIN, bool COUT, bool EARLY>
 __global__ __launch_bounds__(NT) void topk_select_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
     int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
@@ -305,6 +309,60 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
 
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = COUT ? (int)(blockIdx.x / nseg) : (int)blockIdx.x;
+  const int base = tid * VPT;
+  // column of position 0 (rows and segments)
+  const int64_t cbase = COUT ? (int64_t)(blockIdx.x - (unsigned)r * nseg) * SEG : 0;
+  uint32_t key[VPT];
+  int32_t col[CIN ? VPT : 1];
+  float v[CIN ? 1 : VPT];
+  // Every load is issued unconditionally from an address clamped into the
+  // row's stride (or, for the merge, into the row's candidate block), not
+  // into its length, so all of a thread's loads are in flight together and
+  // positions past the length are masked afterwards.  With EARLY (few
+  // workgroups, so latency-bound) they go out before the row length has
+  // arrived; otherwise after it, so that rows which need no selection
+  // (length <= k) skip them.  (A runtime choice would join the two orders,
+  // and the wait-count pass drains all loads at such a join.)
+  auto load_row = [&]() {
+    if (CIN) {
+      const int nc = nseg * k;
+      const uint32_t* kp = c_key + (int64_t)r * nc;
+      const int32_t* cp = c_col + (int64_t)r * nc;
+  #pragma unroll
+      for (int e = 0; e < VPT; e += 4) {
+        if (VEC) {  // nc is a multiple of 4
+          const int p = min(base + e, nc - 4);
+          const uint4 kv = *reinterpret_cast<const uint4*>(kp + p);
+          const int4 cv = *reinterpret_cast<const int4*>(cp + p);
+          key[e] = kv.x; key[e + 1] = kv.y; key[e + 2] = kv.z; key[e + 3] = kv.w;
+          col[e] = cv.x; col[e + 1] = cv.y; col[e + 2] = cv.z; col[e + 3] = cv.w;
+        } else {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int p = min(base + e + i, nc - 1);
+            key[e + i] = kp[p];
+            col[e + i] = cp[p];
+          }
+        }
+      }
+    } else {
+      const float* x0 = logits + (int64_t)r * stride;  // stride floats
+  #pragma unroll
+      for (int e = 0; e < VPT; e += 4) {
+        if (VEC) {  // stride is a multiple of 4
+          const int64_t p = min(cbase + base + e, stride - 4);
+          const float4 f = *reinterpret_cast<const float4*>(x0 + p);
+          v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
+        } else {
+  #pragma unroll
+          for (int i = 0; i < 4; ++i) v[e + i] = x0[min(cbase + base + e + i, stride - 1)];
+        }
+      }
+    }
+  };
+  if constexpr (EARLY) load_row();
+  // read after the row's loads are issued: a scalar load ahead of them
+  // would make their address computation wait for it
   const int len = (int)min((int64_t)max(row_len[r], 0), stride);
   const int32_t req = sm.out ? sm.row_req[r] : 0;
   extern __shared__ int32_t s_bt[];  // [bt_stride] when bt_lds
@@ -312,11 +370,51 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   // whether this workgroup writes final indices (see the early returns below)
   const bool emits = COUT ? (len > k && len <= kSegCols && blockIdx.x == (unsigned)r * nseg)
                           : (!CIN || len <= k || len > kSegCols);
-  if (bt_lds && emits) {
-    const bool okr = req >= 0 && req < sm.batch;
-    for (int c = tid; c < (int)sm.bt_stride; c += NT) s_bt[c] = okr ? sm.bt[(int64_t)req * sm.bt_stride + c] : -1;
+  // The request's block-table row goes to LDS for the slot ids.  With EARLY
+  // it is loaded into registers while the row's loads (above) are in flight
+  // and stored just before the barrier ahead of the output, which publishes
+  // it; otherwise it is staged right after the row's loads are issued.
+  constexpr int kBtPer = EARLY ? (kBtLds + NT - 1) / NT : 1;
+  int32_t btv[kBtPer];
+  auto load_bt = [&]() {
+    if (bt_lds && emits) {
+      const bool okr = req >= 0 && req < sm.batch;
+      const int32_t* rowp = sm.bt + (int64_t)(okr ? req : 0) * sm.bt_stride;
+#pragma unroll
+      for (int i = 0; i < kBtPer; ++i) {
+        const int c = tid + i * NT;
+        btv[i] = okr && c < (int)sm.bt_stride ? rowp[c] : -1;
+      }
+    }
+  };
+  auto store_bt = [&]() {
+    if (bt_lds && emits) {
+#pragma unroll
+      for (int i = 0; i < kBtPer; ++i)
+        if (tid + i * NT < (int)sm.bt_stride) s_bt[tid + i * NT] = btv[i];
+    }
+  };
+  // without EARLY: load and store in one pass, right after the row's loads
+  auto stage_bt = [&]() {
+    if constexpr (EARLY) {
+      load_bt();
+      store_bt();
+    } else if (bt_lds && emits) {
+      const bool okr = req >= 0 && req < sm.batch;
+      for (int c = tid; c < (int)sm.bt_stride; c += NT)
+        s_bt[c] = okr ? sm.bt[(int64_t)req * sm.bt_stride + c] : -1;
+    }
+  };
+  // Clears the histograms; done while the row's loads are in flight, so
+  // this barrier overlaps their latency.
+  auto clear_hist = [&]() {
+    for (int i = tid; i < kBins; i += NT) {
+      s_h0[i] = 0;
+      s_h1[i] = 0;
+    }
+    if (tid < 2) s_misc[tid] = 0u;
     __syncthreads();
-  }
+  };
   auto emit = [&](int j, int32_t i) {  // final index j of row r
     out_idx[(int64_t)r * k + j] = i;
     if (sm.out) {
@@ -332,53 +430,38 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
       sm.out[(int64_t)r * k + j] = slot;
     }
   };
-  if (len <= k) {  // the whole row wins; a segment pass leaves it to the merge
-    if (!COUT)
-      for (int j = tid; j < k; j += NT) emit(j, j < len ? j : -1);
-    return;
+  // A workgroup with no selection to do stops here: rows of at most k
+  // columns (all win), and in the split plan the segments and merge of a
+  // row that fits one segment (segment 0 finishes it).
+  auto done_early = [&]() {
+    if (len <= k) {
+      if (!COUT) {
+        stage_bt();
+        __syncthreads();  // publishes s_bt
+        for (int j = tid; j < k; j += NT) emit(j, j < len ? j : -1);
+      }
+      return true;
+    }
+    return (CIN && len <= kSegCols) || (COUT && len <= kSegCols && blockIdx.x != (unsigned)r * nseg);
+  };
+  if constexpr (!EARLY) {
+    if (done_early()) return;
+    load_row();
   }
-  // In the split plan a row that fits one segment is finished by segment 0,
-  // which writes the final indices; the other segments and the merge skip it.
-  if (CIN && len <= kSegCols) return;
-  if (COUT && len <= kSegCols && blockIdx.x != (unsigned)r * nseg) return;
-  const bool final_out = !COUT || len <= kSegCols;
-  int n;             // positions of this workgroup
-  int64_t cbase = 0; // column of position 0 (rows and segments)
+  int n;  // positions of this workgroup
   if (CIN) {
     n = nseg * k;
   } else if (COUT) {
-    cbase = (int64_t)(blockIdx.x - (unsigned)r * nseg) * SEG;
     n = (int)max(min((int64_t)len - cbase, (int64_t)SEG), (int64_t)0);
   } else {
     n = len;
   }
-
-  const int base = tid * VPT;
-  uint32_t key[VPT];
-  int32_t col[CIN ? VPT : 1];
-  // Every load is issued unconditionally from an address clamped into the
-  // row (positions past n are masked afterwards), so all of a thread's
-  // loads are in flight together instead of each waiting behind a branch.
+  // With early loads nothing that depends on the row length branches before
+  // the keys are converted: a branch there would let the compiler sink the
+  // loads below it, i.e. wait for the length before issuing them.
+  if constexpr (EARLY) load_bt(); else stage_bt();
+  clear_hist();
   if (CIN) {
-    const uint32_t* kp = c_key + (int64_t)r * n;
-    const int32_t* cp = c_col + (int64_t)r * n;
-#pragma unroll
-    for (int e = 0; e < VPT; e += 4) {
-      if (VEC) {  // n is a multiple of 4
-        const int p = min(base + e, n - 4);
-        const uint4 kv = *reinterpret_cast<const uint4*>(kp + p);
-        const int4 cv = *reinterpret_cast<const int4*>(cp + p);
-        key[e] = kv.x; key[e + 1] = kv.y; key[e + 2] = kv.z; key[e + 3] = kv.w;
-        col[e] = cv.x; col[e + 1] = cv.y; col[e + 2] = cv.z; col[e + 3] = cv.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int p = min(base + e + i, n - 1);
-          key[e + i] = kp[p];
-          col[e + i] = cp[p];
-        }
-      }
-    }
 #pragma unroll
     for (int e = 0; e < VPT; ++e)
       if (base + e >= n) {
@@ -386,23 +469,13 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
         col[e] = -1;
       }
   } else {
-    // the row holds `stride` floats from x0; cbase + n <= stride
-    const float* x0 = logits + (int64_t)r * stride;
-    float v[VPT];
-#pragma unroll
-    for (int e = 0; e < VPT; e += 4) {
-      if (VEC) {  // stride is a multiple of 4
-        const int64_t p = min(cbase + base + e, stride - 4);
-        const float4 f = *reinterpret_cast<const float4*>(x0 + p);
-        v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) v[e + i] = x0[min(cbase + base + e + i, cbase + n - 1)];
-      }
-    }
 #pragma unroll
     for (int e = 0; e < VPT; ++e) key[e] = base + e < n ? sel_key(v[e]) : 0u;
   }
+  if constexpr (EARLY) {
+    if (done_early()) return;
+  }
+  const bool final_out = !COUT || len <= kSegCols;
   auto column = [&](int e) -> int32_t {
     if constexpr (CIN) return col[e];
     else return (int32_t)(cbase + base + e);
@@ -441,13 +514,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     return;
   }
 
-  // 1. sample
-  for (int i = tid; i < kBins; i += NT) {
-    s_h0[i] = 0;
-    s_h1[i] = 0;
-  }
-  if (tid < 2) s_misc[tid] = 0u;
-  __syncthreads();
+  // 1. sample (the histograms were cleared while the row was loading)
   if (key[0] != 0u) atomicAdd(&s_h0[key[0] >> 21], 1);
   const uint32_t wmax = wave_max_dpp(key[0]);
   if (lane == 63) atomicMax(&s_misc[1], wmax);
@@ -591,6 +658,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
       }
     }
   }
+  if constexpr (EARLY) store_bt();
   __syncthreads();
   if (COUT && !final_out) {
     uint32_t* ok = o_key + (int64_t)blockIdx.x * k;
@@ -648,12 +716,25 @@ void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, co
                 int32_t k, int32_t nseg, const uint32_t* c_key, const int32_t* c_col, int32_t* out,
                 uint32_t* o_key, int32_t* o_col, const SlotMap& sm, hipStream_t s) {
   const size_t dyn = sm.out && sm.bt_stride <= kBtLds ? (size_t)sm.bt_stride * sizeof(int32_t) : 0;
+  // early loads only for the 1024-thread shapes, which serve launches of
+  // fewer than kManyWgs workgroups
+  if constexpr (NT == 1024) {
+    if (grid <= kEarlyLoadWgs) {
+      if (vec)
+        launch((topk_select_kernel<NT, VPT, true, CIN, COUT, true>), dim3(grid), dim3(NT), dyn, s,
+               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+      else
+        launch((topk_select_kernel<NT, VPT, false, CIN, COUT, true>), dim3(grid), dim3(NT), dyn, s,
+               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+      return;
+    }
+  }
   if (vec)
-    launch((topk_select_kernel<NT, VPT, true, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
-                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+    launch((topk_select_kernel<NT, VPT, true, CIN, COUT, false>), dim3(grid), dim3(NT), dyn, s,
+           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
   else
-    launch((topk_select_kernel<NT, VPT, false, CIN, COUT>), dim3(grid), dim3(NT), dyn, s,
-                       logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+    launch((topk_select_kernel<NT, VPT, false, CIN, COUT, false>), dim3(grid), dim3(NT), dyn, s,
+           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
 }
 
 // Launches the shape's instantiation (segment passes exist only for the
