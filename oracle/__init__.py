@@ -28,3 +28,4 @@ from .indexer import (  # noqa: F401
     k_cache_write, gather_indexer_k, paged_mqa_logits, mqa_logits,
     topk_rows, topk_to_global_slots, decode_limits,
 )
+from . import mla  # noqa: F401,E402  (fp8 MLA cache and sparse MLA decode)
