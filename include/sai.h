@@ -245,6 +245,33 @@ int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* r
                     int32_t batch, int32_t rows, int32_t k, int32_t* out_idx, int32_t* out_slots,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
+/*
+ * mla_cache_write -- write tokens into the fp8 MLA cache that sparse MLA
+ * decode reads ("fp8_ds_mla" layout; prhub summary of vLLM PR #47090, key
+ * source excerpt of _fused_norm_rope_kernel, MLA_CACHE_DS_MLA branch).
+ *
+ * Entry of 656 bytes per token: bytes [0, 512) the latent values as fp8
+ * e4m3fn codes, quantised per 128-value tile with the indexer's rule
+ * (amax = max |tile|, scale = max(amax * fl32(1/448), 1.1754944e-38),
+ * code = fp8(value / scale), round to nearest even, saturating, float32);
+ * bytes [512, 528) the 4 tile scales (fp32); bytes [528, 656) the 64 RoPE
+ * values, copied as bf16.  Token slot s is entry s % block_size of block
+ * s / block_size; entries are 656 bytes apart, blocks block_size*656 bytes.
+ * The RMS norm and the rotation that produce these values are the caller's.
+ *
+ *   kv_bf16        [n, kv_row_stride] bf16, first 512 values of a row used
+ *                  (kv_row_stride >= 512, multiple of 8; 16-byte aligned base)
+ *   kpe_bf16       [n, kpe_row_stride] bf16, first 64 values of a row used
+ *                  (kpe_row_stride >= 64 and even; 4-byte aligned base)
+ *   slot_mapping   [n] int64; a negative slot, or one at or past
+ *                  num_blocks*block_size, is skipped
+ *   cache          [num_blocks, block_size, 656] uint8 (16-byte aligned),
+ *                  written only at the entries of the written slots
+ */
+int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const void* kpe_bf16,
+                    int64_t kpe_row_stride, const int64_t* slot_mapping, int64_t n, void* cache,
+                    int64_t num_blocks, int32_t block_size, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,6 +44,8 @@ SIGNATURES = {
                              _c_void_p],
     "topk_rows_slots": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
                         _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
+    "mla_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _i32,
+                        _c_void_p],
 }
 _RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t}
 
@@ -97,6 +99,19 @@ def _need(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must be contiguous")
 
 
+def _need_rows(t, dtype, name):
+    """A 2-D GPU tensor whose rows may be strided but whose elements within a
+    row are contiguous (the C ABI takes the row stride)."""
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+        raise ValueError(f"{name} must be 2-D with contiguous rows")
+
+
 def _out(t, dtype, name, shape):
     """Caller-provided outputs: the kernels write every element of ``shape``
     (row pitch = the row length), so the tensor must be exactly that."""
@@ -121,6 +136,29 @@ def indexer_k_cache_write(k_bf16, slot_mapping, kv_cache):
                                         k_bf16.shape[0], _ptr(kv_cache), kv_cache.shape[0],
                                         _stream()), "indexer_k_cache_write")
     return kv_cache
+
+
+MLA_ENTRY_BYTES = 656
+
+
+def mla_cache_write(kv_bf16, kpe_bf16, slot_mapping, cache):
+    """Write latent rows kv [n, 512] bf16 and RoPE rows kpe [n, 64] bf16 into the
+    fp8 MLA cache [num_blocks, block_size, 656] u8 in place."""
+    _need_rows(kv_bf16, torch.bfloat16, "kv_bf16")
+    _need_rows(kpe_bf16, torch.bfloat16, "kpe_bf16")
+    _need(slot_mapping, torch.int64, "slot_mapping", 1)
+    _need(cache, torch.uint8, "cache", 3)
+    n = kv_bf16.shape[0]
+    if kv_bf16.shape[1] < 512 or kpe_bf16.shape[1] < 64 or cache.shape[2] != MLA_ENTRY_BYTES:
+        raise ValueError("kv_bf16 must be [n,>=512], kpe_bf16 [n,>=64], cache [blocks, block_size, 656]")
+    if kpe_bf16.shape[0] != n or slot_mapping.shape[0] != n:
+        raise ValueError("kpe_bf16 and slot_mapping need one row per kv row")
+    if n == 0:
+        return cache
+    _check(load().mla_cache_write(_ptr(kv_bf16), kv_bf16.stride(0), _ptr(kpe_bf16), kpe_bf16.stride(0),
+                                  _ptr(slot_mapping), n, _ptr(cache), cache.shape[0], cache.shape[1],
+                                  _stream()), "mla_cache_write")
+    return cache
 
 
 def indexer_q_quant(q_bf16, weights, q_fp8=None, w_eff=None, q_scale=None):

@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsai.so")
 
-SOURCES = ["cache_ops.hip", "logits.hip", "topk.hip"]
+SOURCES = ["cache_ops.hip", "logits.hip", "topk.hip", "mla.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [

@@ -34,7 +34,7 @@ def test_header_declares_the_boundary():
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
         "gather_indexer_k",
         "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
-        "topk_to_global_slots", "topk_rows_slots"])
+        "topk_to_global_slots", "topk_rows_slots", "mla_cache_write"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -113,3 +113,17 @@ def test_time_next_launch_host_checks(lib):
     assert lib.sai_time_next_launch(fake, nul) == SAI_EINVAL
     assert lib.sai_time_next_launch(nul, fake) == SAI_EINVAL
     assert lib.sai_time_next_launch(nul, nul) == SAI_OK
+
+
+def test_mla_cache_write_host_checks(lib):
+    """Validation of host arguments; no device work."""
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    f = lib.mla_cache_write
+    assert f(fake, 512, fake, 64, fake, 0, fake, 4, 64, nul) == SAI_OK           # n == 0
+    assert f(fake, 512, fake, 64, fake, -1, fake, 4, 64, nul) == SAI_EINVAL      # n < 0
+    assert f(fake, 511, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL       # kv stride
+    assert f(fake, 516, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL       # kv stride % 8
+    assert f(fake, 512, fake, 63, fake, 3, fake, 4, 64, nul) == SAI_EINVAL       # kpe stride
+    assert f(fake, 512, fake, 64, fake, 3, fake, 4, 0, nul) == SAI_EINVAL        # block size
+    assert f(nul, 512, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL        # null kv
+    assert f(ctypes.c_void_p(4104), 512, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL  # unaligned
