@@ -272,6 +272,50 @@ int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const void* kpe_
                     int64_t kpe_row_stride, const int64_t* slot_mapping, int64_t n, void* cache,
                     int64_t num_blocks, int32_t block_size, hipStream_t stream);
 
+/*
+ * sparse_mla_workspace_bytes -- bytes of device workspace sparse_mla_decode
+ * needs for (rows, heads, k); 0 when it runs in one pass (or for arguments it
+ * would reject).  The value depends only on the three arguments.
+ */
+size_t sparse_mla_workspace_bytes(int32_t rows, int32_t heads, int32_t k);
+
+/*
+ * sparse_mla_decode -- sparse MLA decode over the fp8 MLA cache: the
+ * attention that consumes the global slot ids the indexer selects (ROCm/ATOM
+ * PR #1094, Technical Details; cache layout as for mla_cache_write).  The
+ * pages name this step without printing its arithmetic; this is the plain
+ * absorbed-MLA reading.  For query row t, head h and the row's valid slots j
+ * (0 <= id < num_blocks*block_size; -1 padding and out-of-range ids are
+ * skipped, a repeated id counts each time it appears):
+ *   s_j = sm_scale * (q_nope[t,h] . kv_j + q_pe[t,h] . kpe_j)
+ *   out[t,h] = sum_j softmax(s)_j * kv_j,   lse[t,h] = ln sum_j exp(s_j)
+ * with kv_j = code * tile scale (the 512 latent values) and kpe_j the stored
+ * 64 RoPE values.  A row with no valid slot gives out = 0, lse = -inf.
+ * Scores are accumulated in fp32 from exactly converted bf16 operands;
+ * softmax weights times the tile scale are rounded to bf16 for the P.V
+ * product (fp32 accumulation).
+ *
+ *   q_nope     [rows, heads, 512] bf16, contiguous, 16-byte aligned
+ *   q_pe       [rows, heads, 64] bf16, contiguous, 16-byte aligned
+ *   heads      a multiple of 16, at most 128
+ *   cache      [num_blocks, block_size, 656] uint8, 16-byte aligned,
+ *              num_blocks >= 1
+ *   slots      [rows, k] int32 global slot ids (k >= 0; k = 0 gives empty rows)
+ *   out        [rows, heads, 512] fp32, 16-byte aligned, fully written
+ *   lse        [rows, heads] fp32 or NULL, fully written when given
+ *   workspace  sparse_mla_workspace_bytes(rows, heads, k) bytes of device
+ *              memory (16-byte aligned), NULL when that is 0; owned by the
+ *              caller, contents need no initialisation and are scratch
+ *              afterwards; calls sharing one workspace must not overlap
+ * SAI_EUNSUPPORTED for heads outside the supported set; SAI_EWORKSPACE for a
+ * missing or short workspace.  Two kernels when the workspace is used, one
+ * otherwise, on `stream`.
+ */
+int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t rows, int32_t heads,
+                      const void* cache, int64_t num_blocks, int32_t block_size,
+                      const int32_t* slots, int32_t k, float sm_scale, float* out, float* lse,
+                      void* workspace, size_t workspace_bytes, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -93,16 +93,19 @@ def mla_entry(cache, slot):
     return kv.reshape(KV_DIM), kpe
 
 
-def sparse_mla_decode(q_nope, q_pe, cache, slots, sm_scale):
+def sparse_mla_decode(q_nope, q_pe, cache, slots, sm_scale, with_abs=False):
     """q_nope float [T, H, 512], q_pe float [T, H, 64], slots int [T, K]
     (global slot ids, -1 padded; ids outside the cache are skipped like -1).
-    Returns (out float64 [T, H, 512], lse float64 [T, H])."""
+    Returns (out float64 [T, H, 512], lse float64 [T, H]); with ``with_abs``
+    also sum_j softmax(score)_j |kv_j| [T, H, 512], the magnitude that bounds
+    how far rounding the softmax weights can move ``out``."""
     q_nope = np.asarray(q_nope, dtype=np.float64)
     q_pe = np.asarray(q_pe, dtype=np.float64)
     slots = np.asarray(slots, dtype=np.int64)
     T, H = q_nope.shape[:2]
     n_slots = cache.shape[0] * cache.shape[1]
     out = np.zeros((T, H, KV_DIM))
+    out_abs = np.zeros((T, H, KV_DIM))
     lse = np.full((T, H), -np.inf)
     for t in range(T):
         valid = [s for s in slots[t] if 0 <= s < n_slots]
@@ -116,5 +119,6 @@ def sparse_mla_decode(q_nope, q_pe, cache, slots, sm_scale):
         p = np.exp(score - m)
         z = p.sum(axis=1, keepdims=True)
         out[t] = (p / z) @ kv
+        out_abs[t] = (p / z) @ np.abs(kv)
         lse[t] = (m + np.log(z))[:, 0]
-    return out, lse
+    return (out, lse, out_abs) if with_abs else (out, lse)

@@ -46,8 +46,12 @@ SIGNATURES = {
                         _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
     "mla_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _i32,
                         _c_void_p],
+    "sparse_mla_workspace_bytes": [_i32, _i32, _i32],
+    "sparse_mla_decode": [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _i64, _i32, _c_void_p, _i32,
+                          ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
 }
-_RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t}
+_RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t,
+            "sparse_mla_workspace_bytes": ctypes.c_size_t}
 
 _lib = None
 
@@ -159,6 +163,42 @@ def mla_cache_write(kv_bf16, kpe_bf16, slot_mapping, cache):
                                   _ptr(slot_mapping), n, _ptr(cache), cache.shape[0], cache.shape[1],
                                   _stream()), "mla_cache_write")
     return cache
+
+
+def sparse_mla_workspace_bytes(rows, heads, k):
+    return int(load().sparse_mla_workspace_bytes(rows, heads, k))
+
+
+def sparse_mla_decode(q_nope, q_pe, cache, slots, sm_scale, out=None, lse=None, workspace=None):
+    """Sparse MLA decode: q_nope [T,H,512] bf16, q_pe [T,H,64] bf16, cache
+    [num_blocks, block_size, 656] u8, slots [T,K] int32 global slot ids (-1 or
+    out-of-range ids skipped) -> (out [T,H,512] fp32, lse [T,H] fp32)."""
+    _need(q_nope, torch.bfloat16, "q_nope", 3)
+    _need(q_pe, torch.bfloat16, "q_pe", 3)
+    _need(cache, torch.uint8, "cache", 3)
+    _need(slots, torch.int32, "slots", 2)
+    T, H = q_nope.shape[:2]
+    K = slots.shape[1]
+    if q_nope.shape[2] != 512 or tuple(q_pe.shape) != (T, H, 64) or cache.shape[2] != MLA_ENTRY_BYTES:
+        raise ValueError("q_nope must be [T,H,512], q_pe [T,H,64], cache [blocks, block_size, 656]")
+    if slots.shape[0] != T:
+        raise ValueError("slots needs one row per query row")
+    dev = q_nope.device
+    out = torch.empty((T, H, 512), dtype=torch.float32, device=dev) if out is None else out
+    lse = torch.empty((T, H), dtype=torch.float32, device=dev) if lse is None else lse
+    _out(out, torch.float32, "out", (T, H, 512))
+    _out(lse, torch.float32, "lse", (T, H))
+    if T == 0:
+        return out, lse
+    ws_bytes = sparse_mla_workspace_bytes(T, H, K)
+    if workspace is None and ws_bytes:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    ws_len = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(load().sparse_mla_decode(_ptr(q_nope), _ptr(q_pe), T, H, _ptr(cache), cache.shape[0],
+                                    cache.shape[1], _ptr(slots), K, float(sm_scale), _ptr(out),
+                                    _ptr(lse), _ptr(workspace), ws_len, _stream()),
+           "sparse_mla_decode")
+    return out, lse
 
 
 def indexer_q_quant(q_bf16, weights, q_fp8=None, w_eff=None, q_scale=None):

@@ -83,3 +83,374 @@ extern "C" int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const
          (int64_t)block_size * kMlaEntry);
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
+
+// ------------------------------------------------------------ sparse decode
+// Sparse MLA decode over the fp8 cache (the consumer of the global slot ids;
+// ROCm/ATOM PR #1094, Technical Details).  For query row t and head h, over
+// the row's valid slots j:
+//   s_j = sm_scale * (q_nope[t,h] . kv_j + q_pe[t,h] . kpe_j),
+//   out[t,h] = sum_j softmax(s)_j kv_j,  lse[t,h] = log sum_j exp(s_j),
+// kv_j the dequantised latent (code * tile scale), kpe_j the stored RoPE part.
+//
+// Workgroup = one query row x 16 heads x one split of the slot list, 4 waves.
+// Slots go through in chunks of 32: the chunk's entries are gathered one
+// chunk ahead into registers, then written to LDS twice -- codes
+// token-major (the B operand of Q.K^T: 8 consecutive dims of one token per
+// lane) and dim-major (the B operand of P.V: 8 consecutive tokens of one dim
+// per lane), the latter through 4x4 byte transposes in registers.  Wave w
+// owns latent tile w (128 dims): it scores the chunk against its tile with
+// bf16 MFMAs on exactly converted fp8 codes, scales each token's partial by
+// its tile scale, and adds one of the four RoPE MFMAs; the four partials are
+// summed through LDS.  Every wave then runs the same online softmax and
+// multiplies P (times its tile's scales, in bf16) by its tile of V.  With
+// several splits the partial (m, l, O) go to a workspace and a second
+// kernel combines them.
+
+typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
+typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+
+constexpr int kMlaHg = 16;     // heads per workgroup
+constexpr int kMlaChunk = 32;  // slots per chunk
+
+namespace {
+
+// 8 fp8 e4m3fn codes -> 8 bf16 (exact: every e4m3 value is a bf16 value)
+__device__ __forceinline__ v8bf16 fp8x8_to_bf16(uint2 c) {
+  const v2bf16 a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, false);
+  const v2bf16 b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.x, 1.0f, true);
+  const v2bf16 d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, false);
+  const v2bf16 e = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)c.y, 1.0f, true);
+  return v8bf16{a[0], a[1], b[0], b[1], d[0], d[1], e[0], e[1]};
+}
+
+__device__ __forceinline__ v8bf16 as_bf16x8(uint4 u) {
+  v8bf16 r;
+  __builtin_memcpy(&r, &u, 16);
+  return r;
+}
+
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
+// max over the 16 lanes that share lane / 16
+__device__ __forceinline__ float max16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v = fmaxf(v, __shfl_xor(v, o, 16));
+  return v;
+}
+__device__ __forceinline__ float sum16(float v) {
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1) v += __shfl_xor(v, o, 16);
+  return v;
+}
+
+struct alignas(16) MlaSmem {
+  uint8_t km[kMlaChunk][kMlaKv];          // codes, token-major
+  uint8_t vt[kMlaKv][kMlaChunk];          // codes, dim-major
+  float sc[kMlaChunk][4];                 // tile scales
+  uint16_t pe[kMlaChunk][kMlaRope];       // RoPE values (bf16)
+  int valid[kMlaChunk];
+  float part[4][2][64][4];                // per-wave partial scores (C layout)
+  uint16_t p[4][kMlaHg][kMlaChunk];       // per-wave P * tile scale (bf16), [head][token]
+};
+
+// Registers holding one chunk of gathered entries for one thread:
+// codes of tokens 4*(t/32)+0..3 at bytes [16*(t%32), +16), the RoPE piece
+// (token t/8, bytes 16*(t%8)) and, for t < 32, the scales of token t.
+struct MlaStage {
+  uint4 c[4];
+  uint4 pe;
+  uint4 sc;
+  int valid;  // token t < 32: slot valid
+};
+
+__device__ __forceinline__ int64_t mla_entry_off(int64_t slot, int64_t block_size, int64_t block_stride) {
+  return (slot / block_size) * block_stride + (slot % block_size) * kMlaEntry;
+}
+
+__device__ __forceinline__ MlaStage mla_gather(const uint8_t* __restrict__ cache,
+                                               const int32_t* __restrict__ srow, int base, int lim,
+                                               int64_t num_slots, int64_t block_size,
+                                               int64_t block_stride) {
+  const int t = threadIdx.x;
+  MlaStage st;
+  auto off_of = [&](int j, bool& ok) {  // entry of chunk token j (a valid address either way)
+    const int idx = base + j;
+    const int64_t s = idx < lim ? (int64_t)srow[idx] : -1;
+    ok = s >= 0 && s < num_slots;
+    return mla_entry_off(ok ? s : 0, block_size, block_stride);
+  };
+  const int tg = t >> 5, dp = t & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    bool ok;
+    const int64_t o = off_of(4 * tg + i, ok);
+    st.c[i] = *reinterpret_cast<const uint4*>(cache + o + 16 * dp);
+  }
+  {
+    bool ok;
+    const int64_t o = off_of(t >> 3, ok);
+    st.pe = *reinterpret_cast<const uint4*>(cache + o + kMlaRopeOff + 16 * (t & 7));
+  }
+  {
+    bool ok;
+    const int64_t o = off_of(t & 31, ok);
+    st.sc = *reinterpret_cast<const uint4*>(cache + o + kMlaScaleOff);
+    st.valid = ok;
+  }
+  return st;
+}
+
+// 4x4 byte transpose: out[d] byte i = in[i] byte d
+__device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32_t d, uint32_t (&o)[4]) {
+  // pairs first: ab_lo = [a0 b0 a1 b1], ab_hi = [a2 b2 a3 b3], same for cd
+  const uint32_t ab_lo = __builtin_amdgcn_perm(b, a, 0x05010400u);
+  const uint32_t ab_hi = __builtin_amdgcn_perm(b, a, 0x07030602u);
+  const uint32_t cd_lo = __builtin_amdgcn_perm(d, c, 0x05010400u);
+  const uint32_t cd_hi = __builtin_amdgcn_perm(d, c, 0x07030602u);
+  o[0] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x05040100u);  // a0 b0 c0 d0
+  o[1] = __builtin_amdgcn_perm(cd_lo, ab_lo, 0x07060302u);  // a1 b1 c1 d1
+  o[2] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x05040100u);
+  o[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
+}
+
+__device__ __forceinline__ void mla_stage_to_lds(MlaSmem& sm, const MlaStage& st) {
+  const int t = threadIdx.x;
+  const int tg = t >> 5, dp = t & 31;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sm.km[4 * tg + i][16 * dp]) = st.c[i];
+  const uint32_t w[4][4] = {{st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w},
+                            {st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w},
+                            {st.c[2].x, st.c[2].y, st.c[2].z, st.c[2].w},
+                            {st.c[3].x, st.c[3].y, st.c[3].z, st.c[3].w}};
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    uint32_t o[4];
+    tr4x4(w[0][q], w[1][q], w[2][q], w[3][q], o);
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+      *reinterpret_cast<uint32_t*>(&sm.vt[16 * dp + 4 * q + b][4 * tg]) = o[b];
+  }
+  *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.pe;
+  if (t < kMlaChunk) {
+    *reinterpret_cast<uint4*>(&sm.sc[t][0]) = st.sc;
+    sm.valid[t] = st.valid;
+  }
+}
+
+__global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
+    const uint8_t* __restrict__ cache, int64_t num_slots, int64_t block_size, int64_t block_stride,
+    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
+  __shared__ MlaSmem sm;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int ngroups = heads / kMlaHg;
+  const int split = blockIdx.x % nsplit;
+  const int hg = (blockIdx.x / nsplit) % ngroups;
+  const int row = blockIdx.x / (nsplit * ngroups);
+  const int base0 = split * split_len;
+  const int lim = min(k, base0 + split_len);
+  const int32_t* srow = slots + (int64_t)row * k;
+
+  // A operands: wave w's latent tile (4 steps of 32 dims) and its RoPE step
+  const int head = hg * kMlaHg + n;  // row n of the A operand
+  const uint16_t* qn = q_nope + ((int64_t)row * heads + head) * kMlaKv + w * kMlaTile;
+  v8bf16 qa[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(qn + 32 * s + 8 * g));
+  const int rope_nb = w >> 1, rope_ks = w & 1;  // this wave's RoPE MFMA: token block, 32-dim step
+  const v8bf16 qp = as_bf16x8(*reinterpret_cast<const uint4*>(
+      q_pe + ((int64_t)row * heads + head) * kMlaRope + 32 * rope_ks + 8 * g));
+
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  float m[4], l[4];  // running max (log2 units) and sum for heads 4g..4g+3
+  v4f o[8];          // O for heads 4g..4g+3, dims w*128 + nb*16 + n
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[e] = -INFINITY;
+    l[e] = 0.0f;
+  }
+#pragma unroll
+  for (int nb = 0; nb < 8; ++nb) o[nb] = zero;
+
+  MlaStage st = mla_gather(cache, srow, base0, lim, num_slots, block_size, block_stride);
+  for (int base = base0; base < lim; base += kMlaChunk) {
+    __syncthreads();  // the previous chunk is no longer read
+    mla_stage_to_lds(sm, st);
+    if (base + kMlaChunk < lim)
+      st = mla_gather(cache, srow, base + kMlaChunk, lim, num_slots, block_size, block_stride);
+    __syncthreads();
+
+    // partial scores: this wave's tile (scaled per token) + one RoPE step
+    v4f acc[2];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      v4f a = zero;
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        const uint2 c = *reinterpret_cast<const uint2*>(&sm.km[16 * nb + n][w * kMlaTile + 32 * s + 8 * g]);
+        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], fp8x8_to_bf16(c), a, 0, 0, 0);
+      }
+      const float scl = sm.sc[16 * nb + n][w];  // token 16nb+n, tile w
+      acc[nb] = a * scl;
+    }
+    {
+      const uint4 pe = *reinterpret_cast<const uint4*>(&sm.pe[16 * rope_nb + n][32 * rope_ks + 8 * g]);
+      const v4f r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp, as_bf16x8(pe), zero, 0, 0, 0);
+      if (rope_nb == 0) acc[0] += r;
+      else acc[1] += r;
+    }
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) *reinterpret_cast<v4f*>(&sm.part[w][nb][lane][0]) = acc[nb];
+    __syncthreads();
+    // full scores in log2 units; lane (g, n): heads 4g+e, tokens n and 16+n
+    float sc[2][4];
+#pragma unroll
+    for (int nb = 0; nb < 2; ++nb) {
+      v4f s = *reinterpret_cast<const v4f*>(&sm.part[0][nb][lane][0]);
+#pragma unroll
+      for (int ww = 1; ww < 4; ++ww) s += *reinterpret_cast<const v4f*>(&sm.part[ww][nb][lane][0]);
+      const bool ok = sm.valid[16 * nb + n] != 0 && base + 16 * nb + n < lim;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) sc[nb][e] = ok ? s[e] * sm_log2 : -INFINITY;
+    }
+    // online softmax (every wave computes the same), P * tile-w scale to LDS
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float cm = max16(fmaxf(sc[0][e], sc[1][e]));
+      const float mn = fmaxf(m[e], cm);
+      const float corr = mn == -INFINITY ? 1.0f : exp2f(m[e] - mn);
+      float ps = 0.0f;
+#pragma unroll
+      for (int nb = 0; nb < 2; ++nb) {
+        const float p = mn == -INFINITY ? 0.0f : exp2f(sc[nb][e] - mn);
+        ps += p;
+        sm.p[w][4 * g + e][16 * nb + n] = (uint16_t)f32_to_bf16_rne(p * sm.sc[16 * nb + n][w]);
+      }
+      l[e] = l[e] * corr + sum16(ps);
+      m[e] = mn;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) o[nb][e] *= corr;
+    }
+    // the P tile was written by other lanes of this wave
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const v8bf16 pa = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.p[w][n][8 * g]));
+#pragma unroll
+    for (int nb = 0; nb < 8; ++nb) {
+      const uint2 c = *reinterpret_cast<const uint2*>(&sm.vt[w * kMlaTile + 16 * nb + n][8 * g]);
+      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(c), o[nb], 0, 0, 0);
+    }
+  }
+
+  // lane (g, n): heads 4g+e, dims w*128 + nb*16 + n
+  const int64_t rh0 = (int64_t)row * heads + hg * kMlaHg;
+  if (nsplit == 1) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float inv = l[e] > 0.0f ? 1.0f / l[e] : 0.0f;
+      float* dst = out + (rh0 + 4 * g + e) * kMlaKv + w * kMlaTile + n;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) dst[16 * nb] = o[nb][e] * inv;
+      if (lse && w == 0 && n == 0)
+        lse[rh0 + 4 * g + e] = l[e] > 0.0f ? (m[e] + __log2f(l[e])) * 0.69314718055994531f : -INFINITY;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t rhs = (rh0 + 4 * g + e) * nsplit + split;
+      float* dst = ws_o + rhs * kMlaKv + w * kMlaTile + n;
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) dst[16 * nb] = o[nb][e];
+      if (w == 0 && n == 0) {
+        ws_ml[2 * rhs] = m[e];
+        ws_ml[2 * rhs + 1] = l[e];
+      }
+    }
+  }
+}
+
+// Combines the splits of one (row, head): 128 threads x 4 dims.
+__global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __restrict__ ws_o,
+                                                                 const float* __restrict__ ws_ml,
+                                                                 int nsplit, float* __restrict__ out,
+                                                                 float* __restrict__ lse) {
+  const int64_t rh = blockIdx.x;
+  const float* ml = ws_ml + rh * nsplit * 2;
+  float mx = -INFINITY;
+  for (int s = 0; s < nsplit; ++s) mx = fmaxf(mx, ml[2 * s]);
+  float L = 0.0f;
+  float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+  for (int s = 0; s < nsplit; ++s) {
+    const float ms = ml[2 * s], ls = ml[2 * s + 1];
+    const float f = (mx == -INFINITY || ls == 0.0f) ? 0.0f : exp2f(ms - mx);
+    L += ls * f;
+    const float4 v = *reinterpret_cast<const float4*>(ws_o + (rh * nsplit + s) * kMlaKv + 4 * threadIdx.x);
+    acc.x += v.x * f;
+    acc.y += v.y * f;
+    acc.z += v.z * f;
+    acc.w += v.w * f;
+  }
+  const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+  *reinterpret_cast<float4*>(out + rh * kMlaKv + 4 * threadIdx.x) =
+      make_float4(acc.x * inv, acc.y * inv, acc.z * inv, acc.w * inv);
+  if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (mx + __log2f(L)) * 0.69314718055994531f : -INFINITY;
+}
+
+// splits so that the grid has about 2 workgroups per CU, 32-slot multiples
+int mla_splits(int64_t rows, int heads, int k) {
+  const int64_t wgs = rows * (heads / kMlaHg);
+  const int max_split = (k + kMlaChunk - 1) / kMlaChunk;
+  int64_t ns = (512 + wgs - 1) / std::max<int64_t>(wgs, 1);
+  ns = std::min<int64_t>(std::max<int64_t>(ns, 1), std::min(max_split, 16));
+  return (int)ns;
+}
+
+}  // namespace
+
+extern "C" size_t sparse_mla_workspace_bytes(int32_t rows, int32_t heads, int32_t k) {
+  if (rows <= 0 || heads <= 0 || heads % kMlaHg || k <= 0) return 0;
+  const int ns = mla_splits(rows, heads, k);
+  if (ns <= 1) return 0;
+  return (size_t)rows * heads * ns * (kMlaKv + 2) * sizeof(float);
+}
+
+extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t rows, int32_t heads,
+                                 const void* cache, int64_t num_blocks, int32_t block_size,
+                                 const int32_t* slots, int32_t k, float sm_scale, float* out,
+                                 float* lse, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  if (rows < 0 || heads <= 0 || k < 0 || num_blocks < 0 || block_size <= 0) return SAI_EINVAL;
+  if (heads % kMlaHg || heads > 128) return SAI_EUNSUPPORTED;
+  if (rows == 0) return SAI_OK;
+  if (!q_nope || !q_pe || !cache || !out || (k > 0 && !slots) || num_blocks == 0) return SAI_EINVAL;
+  if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(cache) || !aligned16(out)) return SAI_EINVAL;
+  if (!(sm_scale == sm_scale)) return SAI_EINVAL;
+  if (num_blocks > INT64_MAX / ((int64_t)block_size * kMlaEntry)) return SAI_EUNSUPPORTED;
+  const int kk = std::max(k, 1);  // k == 0: every row is empty
+  const int ns = mla_splits(rows, heads, kk);
+  const int split_len = ((kk + ns - 1) / ns + kMlaChunk - 1) / kMlaChunk * kMlaChunk;
+  const int ns_used = (kk + split_len - 1) / split_len;
+  const size_t need = ns_used > 1 ? (size_t)rows * heads * ns_used * (kMlaKv + 2) * sizeof(float) : 0;
+  if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SAI_EWORKSPACE;
+  const int64_t grid = (int64_t)rows * (heads / kMlaHg) * ns_used;
+  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  float* ws_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
+  float* ws_ml = need ? ws_o + (size_t)rows * heads * ns_used * kMlaKv : nullptr;
+  launch(sparse_mla_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)q_nope,
+         (const uint16_t*)q_pe, (int)heads, (const uint8_t*)cache, num_blocks * (int64_t)block_size,
+         (int64_t)block_size, (int64_t)block_size * kMlaEntry, slots, k, sm_scale * 1.4426950408889634f,
+         ns_used, split_len, out, lse, ws_o, ws_ml);
+  if (hipGetLastError() != hipSuccess) return SAI_ELAUNCH;
+  if (ns_used > 1) {
+    launch(sparse_mla_combine_kernel, dim3((unsigned)(rows * (int64_t)heads)), dim3(128), 0, stream,
+           (const float*)ws_o, (const float*)ws_ml, ns_used, out, lse);
+    if (hipGetLastError() != hipSuccess) return SAI_ELAUNCH;
+  }
+  return SAI_OK;
+}

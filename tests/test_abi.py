@@ -34,7 +34,8 @@ def test_header_declares_the_boundary():
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
         "gather_indexer_k",
         "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
-        "topk_to_global_slots", "topk_rows_slots", "mla_cache_write"])
+        "topk_to_global_slots", "topk_rows_slots", "mla_cache_write", "sparse_mla_workspace_bytes",
+        "sparse_mla_decode"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -127,3 +128,29 @@ def test_mla_cache_write_host_checks(lib):
     assert f(fake, 512, fake, 64, fake, 3, fake, 4, 0, nul) == SAI_EINVAL        # block size
     assert f(nul, 512, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL        # null kv
     assert f(ctypes.c_void_p(4104), 512, fake, 64, fake, 3, fake, 4, 64, nul) == SAI_EINVAL  # unaligned
+
+
+def test_sparse_mla_decode_host_checks(lib):
+    """Workspace query and argument validation; no device work."""
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    ws = lib.sparse_mla_workspace_bytes
+    assert ws(64, 128, 2048) == 0                          # 512 workgroups: one pass
+    assert ws(2, 16, 2048) == 2 * 16 * 16 * (512 + 2) * 4  # 16 splits
+    assert ws(0, 16, 64) == 0 and ws(4, 24, 64) == 0 and ws(4, 16, 0) == 0
+    f = lib.sparse_mla_decode
+
+    def call(q=fake, rows=2, heads=16, nb=4, bs=64, k=64, scale=0.1, out=fake, w=nul, wb=0):
+        return f(q, fake, rows, heads, fake, nb, bs, fake, k, scale, out, fake, w, wb, nul)
+
+    assert call(rows=0) == SAI_OK
+    assert call(rows=-1) == SAI_EINVAL
+    assert call(heads=24) == SAI_EUNSUPPORTED
+    assert call(heads=256) == SAI_EUNSUPPORTED
+    assert call(bs=0) == SAI_EINVAL
+    assert call(nb=0) == SAI_EINVAL
+    assert call(k=-1) == SAI_EINVAL
+    assert call(q=nul) == SAI_EINVAL
+    assert call(out=ctypes.c_void_p(4100)) == SAI_EINVAL
+    assert call(scale=float("nan")) == SAI_EINVAL
+    assert call(k=2048) == SAI_EWORKSPACE                  # split path needs a workspace
+    assert call(k=2048, w=fake, wb=ws(2, 16, 2048) - 1) == SAI_EWORKSPACE

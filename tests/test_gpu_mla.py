@@ -55,3 +55,116 @@ def test_mla_cache_write_bit_exact(block_size, num_blocks):
     if not np.array_equal(got, ref):
         diff = np.argwhere(got != ref)
         raise AssertionError(f"{len(diff)} bytes differ, first at {diff[:5].tolist()}")
+
+
+# ------------------------------------------------------------ sparse decode
+# Tolerance, from the kernel's arithmetic: scores are fp32 sums of exact
+# bf16 x bf16 products (each fp8 code and each bf16 input converts exactly),
+# so their error is a few fp32 ulps of the summed magnitudes.  The P.V
+# product takes each softmax weight times its tile scale rounded to bf16
+# (relative error <= 2^-9), which moves out[t,h,d] by at most
+# 2^-9 * sum_j p_j |kv_j[d]|.  The bound used, 2^-8 * that sum, leaves room
+# for the score and exp2 errors.  lse is a log of an fp32 sum of exp2 values.
+def _mla_tol(out_abs):
+    return 2.0 ** -8 * out_abs + 1e-30
+
+
+LSE_ATOL, LSE_RTOL = 1e-4, 1e-5
+
+
+def _mla_cache(num_blocks, block_size, seed):
+    """A cache written by the oracle's writer from seeded bf16 rows whose
+    tiles span a wide range of magnitudes."""
+    n = num_blocks * block_size
+    rng = np.random.default_rng(seed)
+    kv = rng.standard_normal((n, 512)).astype(np.float32)
+    kv *= np.exp(rng.standard_normal((n, 4, 1)) * 1.5).astype(np.float32).repeat(128, axis=1).reshape(n, 512)
+    kpe = rng.standard_normal((n, 64)).astype(np.float32) * 2
+    kv = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(kv))
+    kpe = synth.bf16_bits_to_f32(synth.f32_to_bf16_bits(kpe))
+    cache = np.zeros((num_blocks, block_size, 656), np.uint8)
+    return O.mla.mla_cache_write(kv, kpe, np.arange(n), cache)
+
+
+def _mla_query(T, H, seed, scale=1.0):
+    rng = np.random.default_rng(seed)
+    qn = synth.f32_to_bf16_bits(rng.standard_normal((T, H, 512)).astype(np.float32) * scale)
+    qp = synth.f32_to_bf16_bits(rng.standard_normal((T, H, 64)).astype(np.float32) * scale)
+    return qn, qp
+
+
+def _check_decode(qn_bits, qp_bits, cache_np, slots_np, sm_scale, rows=None):
+    cache = torch.from_numpy(cache_np).to(DEV)
+    out, lse = sai.sparse_mla_decode(bf16_tensor(qn_bits), bf16_tensor(qp_bits), cache,
+                                     torch.from_numpy(slots_np).to(DEV), sm_scale)
+    torch.cuda.synchronize()
+    rows = np.arange(slots_np.shape[0]) if rows is None else rows
+    ref, ref_lse, ref_abs = O.mla.sparse_mla_decode(
+        synth.bf16_bits_to_f32(qn_bits[rows]), synth.bf16_bits_to_f32(qp_bits[rows]), cache_np,
+        slots_np[rows], sm_scale, with_abs=True)
+    got = out.cpu().numpy().astype(np.float64)[rows]
+    got_lse = lse.cpu().numpy().astype(np.float64)[rows]
+    err = np.abs(got - ref)
+    tol = _mla_tol(ref_abs)
+    bad = ~(err <= tol)
+    if bad.any():
+        i = np.argwhere(bad)[:5]
+        raise AssertionError(f"{bad.sum()} outputs outside tolerance, first {i.tolist()}: "
+                             f"got {got[tuple(i.T)]} want {ref[tuple(i.T)]} tol {tol[tuple(i.T)]}")
+    fin = np.isfinite(ref_lse)
+    assert np.array_equal(np.isfinite(got_lse), fin), "lse finiteness differs"
+    assert np.all(got_lse[~fin] == -np.inf)
+    assert np.all(got[~fin] == 0.0), "empty rows must give zeros"
+    lerr = np.abs(got_lse[fin] - ref_lse[fin])
+    assert np.all(lerr <= LSE_ATOL + LSE_RTOL * np.abs(ref_lse[fin])), f"lse max err {lerr.max()}"
+    return float((err / np.maximum(tol, 1e-300)).max())
+
+
+@pytest.mark.parametrize("T,H,K,block_size,num_blocks", [
+    (5, 16, 100, 64, 12),    # one head group, ragged tail, split path
+    (3, 64, 261, 16, 40),    # four head groups, block size 16
+    (2, 128, 2048, 64, 80),  # full top-k width, many splits
+])
+def test_sparse_mla_decode_parity(T, H, K, block_size, num_blocks):
+    _say(f"sparse_mla_decode: T {T} H {H} K {K} block_size {block_size}")
+    cache_np = _mla_cache(num_blocks, block_size, 100 + H)
+    n = num_blocks * block_size
+    rng = np.random.default_rng(H + K)
+    slots = np.stack([rng.choice(n, K, replace=K > n) for _ in range(T)]).astype(np.int32)
+    slots[0, K // 2:] = -1                      # padded row
+    if T > 1:
+        slots[1, ::7] = -1                      # holes
+        slots[1, 3::11] = n + 5                 # past the cache: skipped
+        slots[1, 5::13] = -1000
+        slots[1, 1] = slots[1, 0]               # repeated id counts twice
+    qn, qp = _mla_query(T, H, 7 + K)
+    r = _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0))
+    _say(f"  worst err / tol = {r:.3f}")
+
+
+def test_sparse_mla_decode_empty_and_peaked():
+    _say("sparse_mla_decode: empty rows, k = 0, a peaked softmax")
+    cache_np = _mla_cache(4, 64, 5)
+    qn, qp = _mla_query(3, 16, 9, scale=4.0)    # large scores: near one-hot weights
+    slots = np.full((3, 70), -1, np.int32)
+    slots[1, :40] = np.arange(40)
+    slots[2, 69] = 255                          # one slot, last position
+    _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0))
+    # k = 0: every row empty
+    out, lse = sai.sparse_mla_decode(bf16_tensor(qn), bf16_tensor(qp), torch.from_numpy(cache_np).to(DEV),
+                                     torch.zeros((3, 0), dtype=torch.int32, device=DEV), 0.1)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0).item() and torch.all(lse == float("-inf")).item()
+
+
+def test_sparse_mla_decode_full_size_sampled():
+    """The decode workload's shape (64 rows, 128 heads, top-2048 over a
+    640-block cache), one pass on the GPU, four rows checked."""
+    T, H, K, bs, nb = 64, 128, 2048, 64, 640
+    _say(f"sparse_mla_decode full size: T {T} H {H} K {K}")
+    cache_np = _mla_cache(nb, bs, 3)
+    rng = np.random.default_rng(4)
+    slots = np.stack([rng.choice(nb * bs, K, replace=False) for _ in range(T)]).astype(np.int32)
+    slots[5, 1000:] = -1
+    qn, qp = _mla_query(T, H, 6)
+    _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0), rows=np.array([0, 5, 31, 63]))
