@@ -22,6 +22,12 @@ the host cores (cpu_baseline), and two reference points taken after the
 timed region: the bandwidth of a plain 1 GiB device copy on the same box and
 the dominant kernel's time when it re-reads one pool (hot_dominant_us, much
 of its K then comes from the memory-side cache).
+
+Decode workloads add a second measured object, "sparse_mla_decode": sparse
+MLA decode (128 heads, fp8 MLA cache with the pool's block count) over the
+global slot ids the last indexer step produced, timed after the indexer's
+timed region with its own roofline (bf16 MFMA peak), and the oracle's decode
+on three sampled rows as its CPU baseline and parity check (--no-mla skips it).
 """
 import argparse
 import ctypes
@@ -44,6 +50,10 @@ Q_BYTES_PER_ROW = 64 * 128       # fp8 query codes
 W_BYTES_PER_ROW = 64 * 4         # fp32 head weights
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_counters.txt")
 COPY_BYTES = 256 << 20
+BF16_PEAK_TFLOPS = 2500.0
+MLA_HEADS = 128                  # query heads of one sparse MLA decode row
+MLA_FLOPS_PER_SLOT = 2 * (576 + 512)   # per (row, head, valid slot): q.k over 576, p.v over 512
+MLA_ENTRY_BYTES = 656
 
 
 class HipEvents:
@@ -262,6 +272,136 @@ def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
     }, ok
 
 
+def mla_inputs(torch, wl, dev):
+    """Seeded synthetic fp8 MLA cache with the indexer pool's block count
+    (finite e4m3fn codes, positive fp32 tile scales, bf16 RoPE values) and
+    bf16 queries for MLA_HEADS heads."""
+    nb, bs = wl.num_blocks, 64
+    g = torch.Generator(device=dev)
+    g.manual_seed(20240901)
+    cache = torch.empty((nb, bs, MLA_ENTRY_BYTES), dtype=torch.uint8, device=dev)
+    for b0 in range(0, nb, 4096):
+        b1 = min(nb, b0 + 4096)
+        n = b1 - b0
+        codes = torch.randint(0, 0x7F, (n, bs, 512), dtype=torch.uint8, device=dev, generator=g)
+        codes |= torch.randint(0, 2, (n, bs, 512), dtype=torch.uint8, device=dev, generator=g) << 7
+        cache[b0:b1, :, :512] = codes
+        sc = torch.rand((n, bs, 4), device=dev, generator=g) * 0.01 + 1e-3
+        cache[b0:b1, :, 512:528] = sc.view(torch.uint8).view(n, bs, 16)
+        pe = torch.randn((n, bs, 64), device=dev, generator=g).to(torch.bfloat16)
+        cache[b0:b1, :, 528:] = pe.view(torch.uint8).view(n, bs, 128)
+    rows = wl.rows
+    q_nope = torch.randn((rows, MLA_HEADS, 512), device=dev, generator=g).to(torch.bfloat16)
+    q_pe = torch.randn((rows, MLA_HEADS, 64), device=dev, generator=g).to(torch.bfloat16)
+    return cache, q_nope, q_pe
+
+
+def mla_leg(torch, lib, wl, slots, dev, steps, ev, arm, s_ptr, cpu_seconds):
+    """Sparse MLA decode over the global slot ids the indexer step produced
+    (the consumer of the hot path's output), timed on its own after the
+    indexer's timed region; roofline against the bf16 MFMA peak."""
+    cache, q_nope, q_pe = mla_inputs(torch, wl, dev)
+    rows, nb = wl.rows, wl.num_blocks
+    k = slots.shape[1]
+    sm_scale = 576 ** -0.5
+    out = torch.empty((rows, MLA_HEADS, 512), dtype=torch.float32, device=dev)
+    lse = torch.empty((rows, MLA_HEADS), dtype=torch.float32, device=dev)
+    ws_bytes = int(lib.sparse_mla_workspace_bytes(rows, MLA_HEADS, k))
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=dev)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def call():
+        return lib.sparse_mla_decode(P(q_nope), P(q_pe), rows, MLA_HEADS, P(cache), nb, 64, P(slots), k,
+                                     sm_scale, P(out), P(lse), P(ws), ws_bytes, s_ptr)
+    for _ in range(3):
+        assert call() == 0
+    torch.cuda.synchronize()
+    n_ev = max(1, steps // 5)
+    e0, e1 = ev.create(n_ev), ev.create(n_ev)
+    w0, w1 = ev.create(1), ev.create(1)
+    ev.hip.hipEventRecord(w0[0], s_ptr)
+    for i in range(steps):
+        if i % 5 == 0 and i // 5 < n_ev:
+            arm(e0[i // 5], e1[i // 5])
+        assert call() == 0
+    ev.hip.hipEventRecord(w1[0], s_ptr)
+    torch.cuda.synchronize()
+    t_kernel = float(np.mean([ev.elapsed_ms(e0[j], e1[j]) for j in range(n_ev)])) * 1e-3
+    t_call = ev.elapsed_ms(w0[0], w1[0]) * 1e-3 / steps
+    ev.destroy(e0 + e1 + w0 + w1)
+    valid = int((slots >= 0).sum().item())
+    flops = float(valid) * MLA_HEADS * MLA_FLOPS_PER_SLOT
+    alg_bytes = valid * MLA_ENTRY_BYTES + rows * k * 4 + rows * MLA_HEADS * (576 * 2 + 512 * 4 + 4)
+    achieved = flops / t_kernel / 1e12
+    res = {
+        "kernel": "sparse_mla_decode_kernel",
+        "workload": f"{rows} rows x {MLA_HEADS} heads x top-{k} slots from this step, fp8 MLA cache "
+                    f"{nb} blocks x 64 x {MLA_ENTRY_BYTES} B",
+        "avg_launch_us": round(t_kernel * 1e6, 3),
+        "call_us": round(t_call * 1e6, 3),
+        "splits_workspace_bytes": ws_bytes,
+        "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
+                     "alg_gbps": round(alg_bytes / t_kernel / 1e9, 1)},
+        "rows_per_s": round(rows / t_call, 1),
+    }
+    if cpu_seconds > 0:
+        res["cpu_baseline"], res["parity_sampled_rows"] = mla_cpu_baseline(
+            cache, q_nope, q_pe, slots, out, lse, sm_scale, cpu_seconds)
+    del cache
+    return res
+
+
+def mla_cpu_baseline(cache, q_nope, q_pe, slots, out, lse, sm_scale, min_seconds):
+    """The oracle's sparse MLA decode on three sampled rows (their entries
+    copied to the host), timed, and the GPU's out / lse on those rows checked
+    against it: |out - ref| <= 2^-8 * sum_j p_j |kv_j| per element (rounding
+    of the softmax weights to bf16 bounds the kernel at half that),
+    |lse - ref| <= 1e-4 + 1e-5 |ref|."""
+    import torch
+    import oracle as O
+    from sparse_attention_indexer_paged_amd import synth
+    rows = slots.shape[0]
+    pick = sorted({0, rows // 2, rows - 1})
+    sl = slots[pick].cpu().numpy().astype(np.int64)
+    flat = np.unique(sl[sl >= 0])
+    bs = cache.shape[1]
+    fi = torch.from_numpy(flat).to(cache.device)
+    ent = cache[fi // bs, fi % bs].cpu().numpy()               # [n, 656]
+    remap = np.full(sl.shape, -1, np.int64)
+    remap[sl >= 0] = np.searchsorted(flat, sl[sl >= 0])
+    host_cache = ent.reshape(len(flat), 1, MLA_ENTRY_BYTES)
+    qn = synth.bf16_bits_to_f32(q_nope[pick].view(torch.int16).cpu().numpy().view(np.uint16))
+    qp = synth.bf16_bits_to_f32(q_pe[pick].view(torch.int16).cpu().numpy().view(np.uint16))
+    reps, t0 = 0, time.perf_counter()
+    while True:
+        ref, ref_lse, ref_abs = O.mla.sparse_mla_decode(qn, qp, host_cache, remap, sm_scale, with_abs=True)
+        reps += 1
+        el = time.perf_counter() - t0
+        if el >= min_seconds:
+            break
+    got = out[pick].cpu().numpy().astype(np.float64)
+    got_lse = lse[pick].cpu().numpy().astype(np.float64)
+    fin = np.isfinite(ref_lse)
+    ok = bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * ref_abs + 1e-30)
+              and np.all(np.abs(got_lse[fin] - ref_lse[fin]) <= 1e-4 + 1e-5 * np.abs(ref_lse[fin]))
+              and np.all(np.isneginf(got_lse[~fin])))
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = 1
+    return {
+        "value": round(reps * len(pick) / el, 3),
+        "unit": "query-rows/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": (f"{len(pick)} of {rows} rows x {MLA_HEADS} heads x {reps} passes over their "
+                   f"{int((sl >= 0).sum())} selected slots, {el:.1f} s, numpy fp64"),
+    }, ok
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -280,6 +420,9 @@ def main():
                          "timed step (arming adds ~1 us to a step)")
     ap.add_argument("--no-refs", action="store_true",
                     help="skip the 1 GiB copy and hot-cache reference timings")
+    ap.add_argument("--no-mla", action="store_true",
+                    help="skip the sparse MLA decode leg over this step's slot ids")
+    ap.add_argument("--mla-steps", type=int, default=50)
     ap.add_argument("--profile-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device once (a known-size "
                          "transfer that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -403,6 +546,11 @@ def main():
             hot_us = float(np.median([ev.elapsed_ms(h0[j], h1[j]) for j in range(20)])) * 1e3
             ev.destroy(h0 + h1)
 
+    mla = None
+    if not args.no_mla and not prefill:
+        mla = mla_leg(torch, lib, wl, t["slots"], dev, args.mla_steps, ev, arm, s_ptr,
+                      0.0 if args.no_cpu_baseline else min(args.cpu_seconds, 5.0))
+
     if args.profile_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -475,6 +623,7 @@ def main():
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "parity_sampled_rows": parity_ok,
         "cpu_baseline": cpu,
+        "sparse_mla_decode": mla,
     }
     print(json.dumps(out), flush=True)
 

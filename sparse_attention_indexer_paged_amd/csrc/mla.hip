@@ -111,6 +111,8 @@ typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
 constexpr int kMlaHg = 16;     // heads per workgroup
 constexpr int kMlaChunk = 32;  // slots per chunk
+constexpr int kMlaKmPitch = kMlaKv + 16;  // token-major LDS row pitch (bytes)
+constexpr int kMlaVtPitch = kMlaKv + 16;  // dim-major slab pitch (words)
 
 namespace {
 
@@ -147,8 +149,11 @@ __device__ __forceinline__ float sum16(float v) {
 }
 
 struct alignas(16) MlaSmem {
-  uint8_t km[kMlaChunk][kMlaKv];          // codes, token-major
-  uint8_t vt[kMlaKv][kMlaChunk];          // codes, dim-major
+  uint8_t km[kMlaChunk][kMlaKmPitch];     // codes, token-major (padded rows)
+  // codes dim-major, one slab per 4 consecutive tokens: word d of slab q
+  // holds dim d of tokens 4q..4q+3 (byte i = token 4q+i); slabs padded so
+  // that the two slabs one P.V operand reads fall in different banks
+  uint32_t vt[kMlaChunk / 4][kMlaVtPitch];
   float sc[kMlaChunk][4];                 // tile scales
   uint16_t pe[kMlaChunk][kMlaRope];       // RoPE values (bf16)
   int valid[kMlaChunk];
@@ -166,40 +171,38 @@ struct MlaStage {
   int valid;  // token t < 32: slot valid
 };
 
-__device__ __forceinline__ int64_t mla_entry_off(int64_t slot, int64_t block_size, int64_t block_stride) {
-  return (slot / block_size) * block_stride + (slot % block_size) * kMlaEntry;
+// Lane l of every wave loads the slot id of chunk token l & 31, without a
+// branch (lim > 0 whenever this runs; a position past lim is masked where
+// the id is used, one chunk later, so that nothing waits on this load early).
+__device__ __forceinline__ int mla_load_id(const int32_t* __restrict__ srow, int base, int lim) {
+  return srow[min(base + (int)(threadIdx.x & 31), lim - 1)];
 }
 
-__device__ __forceinline__ MlaStage mla_gather(const uint8_t* __restrict__ cache,
-                                               const int32_t* __restrict__ srow, int base, int lim,
-                                               int64_t num_slots, int64_t block_size,
+// Issues the loads of one chunk's entries.  Each lane turns its token's id
+// into an entry offset (one 32-bit division); the loading threads fetch the
+// offsets they need by lane shuffle.  An invalid id (padding, outside the
+// cache, past the split) points at entry 0, so every load is unconditional
+// and in bounds.
+__device__ __forceinline__ MlaStage mla_gather(const uint8_t* __restrict__ cache, int id, int base,
+                                               int lim, int64_t num_slots, uint32_t block_size,
                                                int64_t block_stride) {
   const int t = threadIdx.x;
-  MlaStage st;
-  auto off_of = [&](int j, bool& ok) {  // entry of chunk token j (a valid address either way)
-    const int idx = base + j;
-    const int64_t s = idx < lim ? (int64_t)srow[idx] : -1;
-    ok = s >= 0 && s < num_slots;
-    return mla_entry_off(ok ? s : 0, block_size, block_stride);
+  const bool ok = base + (t & 31) < lim && id >= 0 && (int64_t)id < num_slots;
+  const uint32_t s = ok ? (uint32_t)id : 0u;
+  const uint32_t blk = s / block_size;
+  const int64_t off = (int64_t)blk * block_stride + (int64_t)(s - blk * block_size) * kMlaEntry;
+  const int lo = (int)(uint32_t)off, hi = (int)(uint32_t)((uint64_t)off >> 32);
+  auto off_of = [&](int j) {  // j: lane holding the token's offset
+    return (int64_t)(((uint64_t)(uint32_t)__shfl(hi, j) << 32) | (uint32_t)__shfl(lo, j));
   };
+  MlaStage st;
   const int tg = t >> 5, dp = t & 31;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    bool ok;
-    const int64_t o = off_of(4 * tg + i, ok);
-    st.c[i] = *reinterpret_cast<const uint4*>(cache + o + 16 * dp);
-  }
-  {
-    bool ok;
-    const int64_t o = off_of(t >> 3, ok);
-    st.pe = *reinterpret_cast<const uint4*>(cache + o + kMlaRopeOff + 16 * (t & 7));
-  }
-  {
-    bool ok;
-    const int64_t o = off_of(t & 31, ok);
-    st.sc = *reinterpret_cast<const uint4*>(cache + o + kMlaScaleOff);
-    st.valid = ok;
-  }
+  for (int i = 0; i < 4; ++i)
+    st.c[i] = *reinterpret_cast<const uint4*>(cache + off_of(4 * tg + i) + 16 * dp);
+  st.pe = *reinterpret_cast<const uint4*>(cache + off_of(t >> 3) + kMlaRopeOff + 16 * (t & 7));
+  st.sc = *reinterpret_cast<const uint4*>(cache + off + kMlaScaleOff);  // token t & 31
+  st.valid = ok;
   return st;
 }
 
@@ -225,13 +228,12 @@ __device__ __forceinline__ void mla_stage_to_lds(MlaSmem& sm, const MlaStage& st
                             {st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w},
                             {st.c[2].x, st.c[2].y, st.c[2].z, st.c[2].w},
                             {st.c[3].x, st.c[3].y, st.c[3].z, st.c[3].w}};
+  // this thread's 4 tokens x 16 dims, transposed: 64 contiguous bytes of slab tg
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
     uint32_t o[4];
     tr4x4(w[0][q], w[1][q], w[2][q], w[3][q], o);
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-      *reinterpret_cast<uint32_t*>(&sm.vt[16 * dp + 4 * q + b][4 * tg]) = o[b];
+    *reinterpret_cast<uint4*>(&sm.vt[tg][16 * dp + 4 * q]) = make_uint4(o[0], o[1], o[2], o[3]);
   }
   *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.pe;
   if (t < kMlaChunk) {
@@ -278,73 +280,79 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 #pragma unroll
   for (int nb = 0; nb < 8; ++nb) o[nb] = zero;
 
-  MlaStage st = mla_gather(cache, srow, base0, lim, num_slots, block_size, block_stride);
-  for (int base = base0; base < lim; base += kMlaChunk) {
-    __syncthreads();  // the previous chunk is no longer read
-    mla_stage_to_lds(sm, st);
-    if (base + kMlaChunk < lim)
-      st = mla_gather(cache, srow, base + kMlaChunk, lim, num_slots, block_size, block_stride);
-    __syncthreads();
+  // Entries are gathered one chunk ahead, slot ids two chunks ahead.
+  if (base0 < lim) {  // uniform
+    int id = mla_load_id(srow, base0, lim);
+    MlaStage st = mla_gather(cache, id, base0, lim, num_slots, (uint32_t)block_size, block_stride);
+    id = mla_load_id(srow, base0 + kMlaChunk, lim);
+    for (int base = base0; base < lim; base += kMlaChunk) {
+      __syncthreads();  // the previous chunk is no longer read
+      mla_stage_to_lds(sm, st);
+      st = mla_gather(cache, id, base + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
+      id = mla_load_id(srow, base + 2 * kMlaChunk, lim);
+      __syncthreads();
 
-    // partial scores: this wave's tile (scaled per token) + one RoPE step
-    v4f acc[2];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      v4f a = zero;
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        const uint2 c = *reinterpret_cast<const uint2*>(&sm.km[16 * nb + n][w * kMlaTile + 32 * s + 8 * g]);
-        a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], fp8x8_to_bf16(c), a, 0, 0, 0);
-      }
-      const float scl = sm.sc[16 * nb + n][w];  // token 16nb+n, tile w
-      acc[nb] = a * scl;
-    }
-    {
-      const uint4 pe = *reinterpret_cast<const uint4*>(&sm.pe[16 * rope_nb + n][32 * rope_ks + 8 * g]);
-      const v4f r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp, as_bf16x8(pe), zero, 0, 0, 0);
-      if (rope_nb == 0) acc[0] += r;
-      else acc[1] += r;
-    }
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) *reinterpret_cast<v4f*>(&sm.part[w][nb][lane][0]) = acc[nb];
-    __syncthreads();
-    // full scores in log2 units; lane (g, n): heads 4g+e, tokens n and 16+n
-    float sc[2][4];
-#pragma unroll
-    for (int nb = 0; nb < 2; ++nb) {
-      v4f s = *reinterpret_cast<const v4f*>(&sm.part[0][nb][lane][0]);
-#pragma unroll
-      for (int ww = 1; ww < 4; ++ww) s += *reinterpret_cast<const v4f*>(&sm.part[ww][nb][lane][0]);
-      const bool ok = sm.valid[16 * nb + n] != 0 && base + 16 * nb + n < lim;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) sc[nb][e] = ok ? s[e] * sm_log2 : -INFINITY;
-    }
-    // online softmax (every wave computes the same), P * tile-w scale to LDS
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const float cm = max16(fmaxf(sc[0][e], sc[1][e]));
-      const float mn = fmaxf(m[e], cm);
-      const float corr = mn == -INFINITY ? 1.0f : exp2f(m[e] - mn);
-      float ps = 0.0f;
+      // partial scores: this wave's tile (scaled per token) + one RoPE step
+      v4f acc[2];
 #pragma unroll
       for (int nb = 0; nb < 2; ++nb) {
-        const float p = mn == -INFINITY ? 0.0f : exp2f(sc[nb][e] - mn);
-        ps += p;
-        sm.p[w][4 * g + e][16 * nb + n] = (uint16_t)f32_to_bf16_rne(p * sm.sc[16 * nb + n][w]);
+        v4f a = zero;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          const uint2 c = *reinterpret_cast<const uint2*>(&sm.km[16 * nb + n][w * kMlaTile + 32 * s + 8 * g]);
+          a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], fp8x8_to_bf16(c), a, 0, 0, 0);
+        }
+        const float scl = sm.sc[16 * nb + n][w];  // token 16nb+n, tile w
+        acc[nb] = a * scl;
       }
-      l[e] = l[e] * corr + sum16(ps);
-      m[e] = mn;
+      {
+        const uint4 pe = *reinterpret_cast<const uint4*>(&sm.pe[16 * rope_nb + n][32 * rope_ks + 8 * g]);
+        const v4f r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp, as_bf16x8(pe), zero, 0, 0, 0);
+        if (rope_nb == 0) acc[0] += r;
+        else acc[1] += r;
+      }
 #pragma unroll
-      for (int nb = 0; nb < 8; ++nb) o[nb][e] *= corr;
-    }
-    // the P tile was written by other lanes of this wave
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    const v8bf16 pa = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.p[w][n][8 * g]));
+      for (int nb = 0; nb < 2; ++nb) *reinterpret_cast<v4f*>(&sm.part[w][nb][lane][0]) = acc[nb];
+      __syncthreads();
+      // full scores in log2 units; lane (g, n): heads 4g+e, tokens n and 16+n
+      float sc[2][4];
 #pragma unroll
-    for (int nb = 0; nb < 8; ++nb) {
-      const uint2 c = *reinterpret_cast<const uint2*>(&sm.vt[w * kMlaTile + 16 * nb + n][8 * g]);
-      o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(c), o[nb], 0, 0, 0);
+      for (int nb = 0; nb < 2; ++nb) {
+        v4f s = *reinterpret_cast<const v4f*>(&sm.part[0][nb][lane][0]);
+#pragma unroll
+        for (int ww = 1; ww < 4; ++ww) s += *reinterpret_cast<const v4f*>(&sm.part[ww][nb][lane][0]);
+        const bool ok = sm.valid[16 * nb + n] != 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[nb][e] = ok ? s[e] * sm_log2 : -INFINITY;
+      }
+      // online softmax (every wave computes the same), P * tile-w scale to LDS
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float cm = max16(fmaxf(sc[0][e], sc[1][e]));
+        const float mn = fmaxf(m[e], cm);
+        const float corr = mn == -INFINITY ? 1.0f : exp2f(m[e] - mn);
+        float ps = 0.0f;
+#pragma unroll
+        for (int nb = 0; nb < 2; ++nb) {
+          const float p = mn == -INFINITY ? 0.0f : exp2f(sc[nb][e] - mn);
+          ps += p;
+          sm.p[w][4 * g + e][16 * nb + n] = (uint16_t)f32_to_bf16_rne(p * sm.sc[16 * nb + n][w]);
+        }
+        l[e] = l[e] * corr + sum16(ps);
+        m[e] = mn;
+#pragma unroll
+        for (int nb = 0; nb < 8; ++nb) o[nb][e] *= corr;
+      }
+      // the P tile was written by other lanes of this wave
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      const v8bf16 pa = as_bf16x8(*reinterpret_cast<const uint4*>(&sm.p[w][n][8 * g]));
+#pragma unroll
+      for (int nb = 0; nb < 8; ++nb) {
+        const int d = w * kMlaTile + 16 * nb + n;  // tokens 8g..8g+7 of dim d
+        const uint2 c = make_uint2(sm.vt[2 * g][d], sm.vt[2 * g + 1][d]);
+        o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(c), o[nb], 0, 0, 0);
+      }
     }
   }
 
