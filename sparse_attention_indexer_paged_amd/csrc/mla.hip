@@ -109,10 +109,12 @@ extern "C" int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 
-constexpr int kMlaHg = 16;     // heads per workgroup
+constexpr int kMlaHg = 16;     // heads per workgroup (narrow kernel) and per wave (wide)
+constexpr int kMlaWideHeads = 64;  // heads per workgroup of the wide kernel
 constexpr int kMlaChunk = 32;  // slots per chunk
 constexpr int kMlaKmPitch = kMlaKv + 16;  // token-major LDS row pitch (bytes)
 constexpr int kMlaVtPitch = kMlaKv + 16;  // dim-major slab pitch (words)
+constexpr int kMlaPePitch = kMlaRope + 8;  // RoPE LDS row pitch (bf16 values)
 
 namespace {
 
@@ -148,15 +150,20 @@ __device__ __forceinline__ float sum16(float v) {
   return v;
 }
 
-struct alignas(16) MlaSmem {
+// One staged chunk of 32 entries.
+struct alignas(16) MlaChunkLds {
   uint8_t km[kMlaChunk][kMlaKmPitch];     // codes, token-major (padded rows)
   // codes dim-major, one slab per 4 consecutive tokens: word d of slab q
   // holds dim d of tokens 4q..4q+3 (byte i = token 4q+i); slabs padded so
   // that the two slabs one P.V operand reads fall in different banks
   uint32_t vt[kMlaChunk / 4][kMlaVtPitch];
-  float sc[kMlaChunk][4];                 // tile scales
-  uint16_t pe[kMlaChunk][kMlaRope];       // RoPE values (bf16)
+  uint16_t pe[kMlaChunk][kMlaPePitch];    // RoPE values (bf16), padded rows
+  float sct[4][kMlaChunk];                // tile scales, [tile][token]
   int valid[kMlaChunk];
+};
+
+struct alignas(16) MlaSmem {
+  MlaChunkLds c;
   float part[4][2][64][4];                // per-wave partial scores (C layout)
   uint16_t p[4][kMlaHg][kMlaChunk];       // per-wave P * tile scale (bf16), [head][token]
 };
@@ -219,7 +226,7 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
   o[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
 }
 
-__device__ __forceinline__ void mla_stage_to_lds(MlaSmem& sm, const MlaStage& st) {
+__device__ __forceinline__ void mla_stage_to_lds(MlaChunkLds& sm, const MlaStage& st) {
   const int t = threadIdx.x;
   const int tg = t >> 5, dp = t & 31;
 #pragma unroll
@@ -237,7 +244,10 @@ __device__ __forceinline__ void mla_stage_to_lds(MlaSmem& sm, const MlaStage& st
   }
   *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.pe;
   if (t < kMlaChunk) {
-    *reinterpret_cast<uint4*>(&sm.sc[t][0]) = st.sc;
+    sm.sct[0][t] = __uint_as_float(st.sc.x);
+    sm.sct[1][t] = __uint_as_float(st.sc.y);
+    sm.sct[2][t] = __uint_as_float(st.sc.z);
+    sm.sct[3][t] = __uint_as_float(st.sc.w);
     sm.valid[t] = st.valid;
   }
 }
@@ -287,7 +297,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
     id = mla_load_id(srow, base0 + kMlaChunk, lim);
     for (int base = base0; base < lim; base += kMlaChunk) {
       __syncthreads();  // the previous chunk is no longer read
-      mla_stage_to_lds(sm, st);
+      mla_stage_to_lds(sm.c, st);
       st = mla_gather(cache, id, base + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
       id = mla_load_id(srow, base + 2 * kMlaChunk, lim);
       __syncthreads();
@@ -299,14 +309,14 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
         v4f a = zero;
 #pragma unroll
         for (int s = 0; s < 4; ++s) {
-          const uint2 c = *reinterpret_cast<const uint2*>(&sm.km[16 * nb + n][w * kMlaTile + 32 * s + 8 * g]);
+          const uint2 c = *reinterpret_cast<const uint2*>(&sm.c.km[16 * nb + n][w * kMlaTile + 32 * s + 8 * g]);
           a = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[s], fp8x8_to_bf16(c), a, 0, 0, 0);
         }
-        const float scl = sm.sc[16 * nb + n][w];  // token 16nb+n, tile w
+        const float scl = sm.c.sct[w][16 * nb + n];  // token 16nb+n, tile w
         acc[nb] = a * scl;
       }
       {
-        const uint4 pe = *reinterpret_cast<const uint4*>(&sm.pe[16 * rope_nb + n][32 * rope_ks + 8 * g]);
+        const uint4 pe = *reinterpret_cast<const uint4*>(&sm.c.pe[16 * rope_nb + n][32 * rope_ks + 8 * g]);
         const v4f r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qp, as_bf16x8(pe), zero, 0, 0, 0);
         if (rope_nb == 0) acc[0] += r;
         else acc[1] += r;
@@ -321,7 +331,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
         v4f s = *reinterpret_cast<const v4f*>(&sm.part[0][nb][lane][0]);
 #pragma unroll
         for (int ww = 1; ww < 4; ++ww) s += *reinterpret_cast<const v4f*>(&sm.part[ww][nb][lane][0]);
-        const bool ok = sm.valid[16 * nb + n] != 0;
+        const bool ok = sm.c.valid[16 * nb + n] != 0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) sc[nb][e] = ok ? s[e] * sm_log2 : -INFINITY;
       }
@@ -336,7 +346,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
         for (int nb = 0; nb < 2; ++nb) {
           const float p = mn == -INFINITY ? 0.0f : exp2f(sc[nb][e] - mn);
           ps += p;
-          sm.p[w][4 * g + e][16 * nb + n] = (uint16_t)f32_to_bf16_rne(p * sm.sc[16 * nb + n][w]);
+          sm.p[w][4 * g + e][16 * nb + n] = (uint16_t)f32_to_bf16_rne(p * sm.c.sct[w][16 * nb + n]);
         }
         l[e] = l[e] * corr + sum16(ps);
         m[e] = mn;
@@ -350,7 +360,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 #pragma unroll
       for (int nb = 0; nb < 8; ++nb) {
         const int d = w * kMlaTile + 16 * nb + n;  // tokens 8g..8g+7 of dim d
-        const uint2 c = make_uint2(sm.vt[2 * g][d], sm.vt[2 * g + 1][d]);
+        const uint2 c = make_uint2(sm.c.vt[2 * g][d], sm.c.vt[2 * g + 1][d]);
         o[nb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(c), o[nb], 0, 0, 0);
       }
     }
@@ -383,6 +393,171 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
   }
 }
 
+// 64 heads per workgroup, 16 per wave; every wave scores the chunk over all
+// 576 dims and multiplies by all 512 value dims for its own heads, and the
+// four waves share the staged chunk (double-buffered, one barrier a chunk).
+// Scores are formed transposed, S^T = K Q^T: lane (g, n) then holds head n
+// for tokens 4g..4g+3 and 16+4g..16+4g+3, which are exactly the eight
+// tokens it supplies as the A operand of P.V when the B operand (V) is read
+// from slabs g and 4+g.  The softmax state of head n is therefore per lane;
+// the running max is shared by the four lanes of a head (two shuffles a
+// chunk) and the running sum is reduced once at the end.  O is rescaled
+// only when a head's max grows by more than 2^8 (until then the weights
+// 2^(s - m) stay below 2^8, harmless in bf16 and fp32).
+__global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
+    const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
+    const uint8_t* __restrict__ cache, int64_t num_slots, int64_t block_size, int64_t block_stride,
+    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len,
+    float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
+    float* __restrict__ ws_ml) {
+  __shared__ MlaChunkLds buf[2];
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int g = lane >> 4, n = lane & 15;
+  const int ngroups = heads / kMlaWideHeads;
+  const int split = blockIdx.x % nsplit;
+  const int hg = (blockIdx.x / nsplit) % ngroups;
+  const int row = blockIdx.x / (nsplit * ngroups);
+  const int base0 = split * split_len;
+  const int lim = min(k, base0 + split_len);
+  const int32_t* srow = slots + (int64_t)row * k;
+  const int head0 = hg * kMlaWideHeads + wv * kMlaHg;  // this wave's 16 heads
+
+  // B operands of S^T: lane (g, n) holds head head0+n, dims 32s+8g .. +7
+  const int64_t qh = (int64_t)row * heads + head0 + n;
+  v8bf16 qa[kMlaKv / 32], qp[kMlaRope / 32];
+#pragma unroll
+  for (int s = 0; s < kMlaKv / 32; ++s)
+    qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q_nope + qh * kMlaKv + 32 * s + 8 * g));
+#pragma unroll
+  for (int s = 0; s < kMlaRope / 32; ++s)
+    qp[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q_pe + qh * kMlaRope + 32 * s + 8 * g));
+
+  const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
+  v4f o[kMlaKv / 16];  // O rows = heads head0+4g+e, column dim 16i+n
+#pragma unroll
+  for (int i = 0; i < kMlaKv / 16; ++i) o[i] = zero;
+  float m_run = -INFINITY, l_run = 0.0f;  // head head0+n (l: this lane's tokens only)
+
+  const int nchunks = base0 < lim ? (lim - base0 + kMlaChunk - 1) / kMlaChunk : 0;
+  if (nchunks > 0) {  // uniform
+    int id = mla_load_id(srow, base0, lim);
+    MlaStage st = mla_gather(cache, id, base0, lim, num_slots, (uint32_t)block_size, block_stride);
+    id = mla_load_id(srow, base0 + kMlaChunk, lim);
+    mla_stage_to_lds(buf[0], st);
+    st = mla_gather(cache, id, base0 + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
+    id = mla_load_id(srow, base0 + 2 * kMlaChunk, lim);
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      const MlaChunkLds& b = buf[c & 1];
+      // S^T for tokens n (acc 0) and 16+n (acc 1), per latent tile, scaled
+      v4f s0 = zero, s1 = zero;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        v4f a0 = zero, a1 = zero;
+#pragma unroll
+        for (int st4 = 0; st4 < 4; ++st4) {
+          const int col = w * kMlaTile + 32 * st4 + 8 * g;
+          const uint2 c0 = *reinterpret_cast<const uint2*>(&b.km[n][col]);
+          const uint2 c1 = *reinterpret_cast<const uint2*>(&b.km[16 + n][col]);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c0), qa[4 * w + st4], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c1), qa[4 * w + st4], a1, 0, 0, 0);
+        }
+        s0 += a0 * *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
+        s1 += a1 * *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
+      }
+#pragma unroll
+      for (int rs = 0; rs < kMlaRope / 32; ++rs) {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(&b.pe[n][32 * rs + 8 * g]);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(&b.pe[16 + n][32 * rs + 8 * g]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp[rs], s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp[rs], s1, 0, 0, 0);
+      }
+      // scores in log2 units; token order 4g+e, then 16+4g+e
+      const int4 ok0 = *reinterpret_cast<const int4*>(&b.valid[4 * g]);
+      const int4 ok1 = *reinterpret_cast<const int4*>(&b.valid[16 + 4 * g]);
+      float sv[8] = {ok0.x ? s0[0] * sm_log2 : -INFINITY, ok0.y ? s0[1] * sm_log2 : -INFINITY,
+                     ok0.z ? s0[2] * sm_log2 : -INFINITY, ok0.w ? s0[3] * sm_log2 : -INFINITY,
+                     ok1.x ? s1[0] * sm_log2 : -INFINITY, ok1.y ? s1[1] * sm_log2 : -INFINITY,
+                     ok1.z ? s1[2] * sm_log2 : -INFINITY, ok1.w ? s1[3] * sm_log2 : -INFINITY};
+      float mx = fmaxf(fmaxf(fmaxf(sv[0], sv[1]), fmaxf(sv[2], sv[3])),
+                       fmaxf(fmaxf(sv[4], sv[5]), fmaxf(sv[6], sv[7])));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const bool grow = m_new > m_run + 8.0f;  // m_run = -inf and a finite score: true
+      if (__any(grow)) {
+        const float corr = grow ? __builtin_amdgcn_exp2f(m_run - m_new) : 1.0f;
+        l_run *= corr;
+        m_run = grow ? m_new : m_run;
+        float ce[4];  // factors of O's rows, heads 4g+e (held by lanes 4g+e)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) ce[e] = __shfl(corr, 4 * g + e);
+#pragma unroll
+        for (int i = 0; i < kMlaKv / 16; ++i) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[i][e] *= ce[e];
+        }
+      }
+      const float mu = m_run == -INFINITY ? 0.0f : m_run;  // then every score here is -inf
+      float pv[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        pv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
+        l_run += pv[i];
+      }
+      // P.V per latent tile: weights times the tile's scales, bf16
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const v4f t0 = *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
+        const v4f t1 = *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
+        const v8bf16 pa = {(__bf16)(pv[0] * t0[0]), (__bf16)(pv[1] * t0[1]), (__bf16)(pv[2] * t0[2]),
+                           (__bf16)(pv[3] * t0[3]), (__bf16)(pv[4] * t1[0]), (__bf16)(pv[5] * t1[1]),
+                           (__bf16)(pv[6] * t1[2]), (__bf16)(pv[7] * t1[3])};
+#pragma unroll
+        for (int d = 0; d < kMlaTile / 16; ++d) {
+          const int dim = w * kMlaTile + 16 * d + n;
+          const uint2 cv = make_uint2(b.vt[g][dim], b.vt[4 + g][dim]);
+          o[w * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(cv), o[w * 8 + d], 0, 0, 0);
+        }
+      }
+      // stage the next chunk into the other buffer (its last readers passed
+      // the previous barrier) and issue the loads of the one after; past the
+      // end these touch only valid addresses and are never read
+      mla_stage_to_lds(buf[(c + 1) & 1], st);
+      st = mla_gather(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
+                      block_stride);
+      id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
+      __syncthreads();
+    }
+  }
+
+  // row sums over the four lanes of a head; O's rows need heads 4g+e
+  float l_tot = l_run + __shfl_xor(l_run, 16);
+  l_tot += __shfl_xor(l_tot, 32);
+  const int64_t rh0 = (int64_t)row * heads + head0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const float me = __shfl(m_run, 4 * g + e), le = __shfl(l_tot, 4 * g + e);
+    const int64_t rh = rh0 + 4 * g + e;
+    if (nsplit == 1) {
+      const float inv = le > 0.0f ? 1.0f / le : 0.0f;
+      float* dst = out + rh * kMlaKv + n;
+#pragma unroll
+      for (int i = 0; i < kMlaKv / 16; ++i) dst[16 * i] = o[i][e] * inv;
+      if (lse && n == 0) lse[rh] = le > 0.0f ? (me + __log2f(le)) * 0.69314718055994531f : -INFINITY;
+    } else {
+      const int64_t rhs = rh * nsplit + split;
+      float* dst = ws_o + rhs * kMlaKv + n;
+#pragma unroll
+      for (int i = 0; i < kMlaKv / 16; ++i) dst[16 * i] = o[i][e];
+      if (n == 0) {
+        ws_ml[2 * rhs] = me;
+        ws_ml[2 * rhs + 1] = le;
+      }
+    }
+  }
+}
+
 // Combines the splits of one (row, head): 128 threads x 4 dims.
 __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __restrict__ ws_o,
                                                                  const float* __restrict__ ws_ml,
@@ -410,22 +585,40 @@ __global__ __launch_bounds__(128) void sparse_mla_combine_kernel(const float* __
   if (lse && threadIdx.x == 0) lse[rh] = L > 0.0f ? (mx + __log2f(L)) * 0.69314718055994531f : -INFINITY;
 }
 
-// splits so that the grid has about 2 workgroups per CU, 32-slot multiples
-int mla_splits(int64_t rows, int heads, int k) {
-  const int64_t wgs = rows * (heads / kMlaHg);
-  const int max_split = (k + kMlaChunk - 1) / kMlaChunk;
-  int64_t ns = (512 + wgs - 1) / std::max<int64_t>(wgs, 1);
+// Launch plan: the wide kernel when the heads come in groups of 64 (one
+// workgroup per CU), else the narrow one (16 heads, about two per CU); the
+// slot list is split in 32-slot multiples until the grid fills the chip.
+struct MlaPlan {
+  bool wide;
+  int nsplit;     // splits actually launched
+  int split_len;  // slots per split (multiple of 32)
+  int64_t grid;
+};
+
+MlaPlan mla_plan(int64_t rows, int heads, int k) {
+  MlaPlan p;
+  p.wide = heads % kMlaWideHeads == 0;
+  const int64_t wgs = rows * (heads / (p.wide ? kMlaWideHeads : kMlaHg));
+  const int64_t target = p.wide ? 256 : 512;
+  const int kk = std::max(k, 1);
+  const int max_split = (kk + kMlaChunk - 1) / kMlaChunk;
+  int64_t ns = (target + wgs - 1) / std::max<int64_t>(wgs, 1);
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), std::min(max_split, 16));
-  return (int)ns;
+  p.split_len = (int)(((kk + ns - 1) / ns + kMlaChunk - 1) / kMlaChunk * kMlaChunk);
+  p.nsplit = (kk + p.split_len - 1) / p.split_len;
+  p.grid = wgs * p.nsplit;
+  return p;
+}
+
+size_t mla_workspace(int64_t rows, int heads, const MlaPlan& p) {
+  return p.nsplit > 1 ? (size_t)rows * heads * p.nsplit * (kMlaKv + 2) * sizeof(float) : 0;
 }
 
 }  // namespace
 
 extern "C" size_t sparse_mla_workspace_bytes(int32_t rows, int32_t heads, int32_t k) {
-  if (rows <= 0 || heads <= 0 || heads % kMlaHg || k <= 0) return 0;
-  const int ns = mla_splits(rows, heads, k);
-  if (ns <= 1) return 0;
-  return (size_t)rows * heads * ns * (kMlaKv + 2) * sizeof(float);
+  if (rows <= 0 || heads <= 0 || heads % kMlaHg || heads > 128 || k <= 0) return 0;
+  return mla_workspace(rows, heads, mla_plan(rows, heads, k));
 }
 
 extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t rows, int32_t heads,
@@ -440,24 +633,21 @@ extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t r
   if (!aligned16(q_nope) || !aligned16(q_pe) || !aligned16(cache) || !aligned16(out)) return SAI_EINVAL;
   if (!(sm_scale == sm_scale)) return SAI_EINVAL;
   if (num_blocks > INT64_MAX / ((int64_t)block_size * kMlaEntry)) return SAI_EUNSUPPORTED;
-  const int kk = std::max(k, 1);  // k == 0: every row is empty
-  const int ns = mla_splits(rows, heads, kk);
-  const int split_len = ((kk + ns - 1) / ns + kMlaChunk - 1) / kMlaChunk * kMlaChunk;
-  const int ns_used = (kk + split_len - 1) / split_len;
-  const size_t need = ns_used > 1 ? (size_t)rows * heads * ns_used * (kMlaKv + 2) * sizeof(float) : 0;
+  const MlaPlan p = mla_plan(rows, heads, k);
+  const size_t need = mla_workspace(rows, heads, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SAI_EWORKSPACE;
-  const int64_t grid = (int64_t)rows * (heads / kMlaHg) * ns_used;
-  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  if (p.grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   float* ws_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
-  float* ws_ml = need ? ws_o + (size_t)rows * heads * ns_used * kMlaKv : nullptr;
-  launch(sparse_mla_decode_kernel, dim3((unsigned)grid), dim3(256), 0, stream, (const uint16_t*)q_nope,
-         (const uint16_t*)q_pe, (int)heads, (const uint8_t*)cache, num_blocks * (int64_t)block_size,
-         (int64_t)block_size, (int64_t)block_size * kMlaEntry, slots, k, sm_scale * 1.4426950408889634f,
-         ns_used, split_len, out, lse, ws_o, ws_ml);
+  float* ws_ml = need ? ws_o + (size_t)rows * heads * p.nsplit * kMlaKv : nullptr;
+  launch(p.wide ? sparse_mla_decode_wide_kernel : sparse_mla_decode_kernel, dim3((unsigned)p.grid),
+         dim3(256), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_pe, (int)heads,
+         (const uint8_t*)cache, num_blocks * (int64_t)block_size, (int64_t)block_size,
+         (int64_t)block_size * kMlaEntry, slots, k, sm_scale * 1.4426950408889634f, p.nsplit,
+         p.split_len, out, lse, ws_o, ws_ml);
   if (hipGetLastError() != hipSuccess) return SAI_ELAUNCH;
-  if (ns_used > 1) {
+  if (p.nsplit > 1) {
     launch(sparse_mla_combine_kernel, dim3((unsigned)(rows * (int64_t)heads)), dim3(128), 0, stream,
-           (const float*)ws_o, (const float*)ws_ml, ns_used, out, lse);
+           (const float*)ws_o, (const float*)ws_ml, p.nsplit, out, lse);
     if (hipGetLastError() != hipSuccess) return SAI_ELAUNCH;
   }
   return SAI_OK;

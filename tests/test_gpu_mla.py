@@ -121,9 +121,11 @@ def _check_decode(qn_bits, qp_bits, cache_np, slots_np, sm_scale, rows=None):
 
 
 @pytest.mark.parametrize("T,H,K,block_size,num_blocks", [
-    (5, 16, 100, 64, 12),    # one head group, ragged tail, split path
-    (3, 64, 261, 16, 40),    # four head groups, block size 16
-    (2, 128, 2048, 64, 80),  # full top-k width, many splits
+    (5, 16, 100, 64, 12),    # 16-head workgroups, ragged tail, split path
+    (3, 32, 130, 64, 12),    # 16-head workgroups, two groups
+    (3, 64, 261, 16, 40),    # 64-head workgroups, block size 16
+    (2, 128, 2048, 64, 80),  # full top-k width, two 64-head groups, many splits
+    (256, 64, 64, 64, 30),   # 64-head workgroups, one split (no combine)
 ])
 def test_sparse_mla_decode_parity(T, H, K, block_size, num_blocks):
     _say(f"sparse_mla_decode: T {T} H {H} K {K} block_size {block_size}")
@@ -142,10 +144,11 @@ def test_sparse_mla_decode_parity(T, H, K, block_size, num_blocks):
     _say(f"  worst err / tol = {r:.3f}")
 
 
-def test_sparse_mla_decode_empty_and_peaked():
-    _say("sparse_mla_decode: empty rows, k = 0, a peaked softmax")
+@pytest.mark.parametrize("H", [16, 64])
+def test_sparse_mla_decode_empty_and_peaked(H):
+    _say(f"sparse_mla_decode: empty rows, k = 0, a peaked softmax, H {H}")
     cache_np = _mla_cache(4, 64, 5)
-    qn, qp = _mla_query(3, 16, 9, scale=4.0)    # large scores: near one-hot weights
+    qn, qp = _mla_query(3, H, 9, scale=4.0)     # large scores: near one-hot weights
     slots = np.full((3, 70), -1, np.int32)
     slots[1, :40] = np.arange(40)
     slots[2, 69] = 255                          # one slot, last position
@@ -155,6 +158,25 @@ def test_sparse_mla_decode_empty_and_peaked():
                                      torch.zeros((3, 0), dtype=torch.int32, device=DEV), 0.1)
     torch.cuda.synchronize()
     assert torch.all(out == 0).item() and torch.all(lse == float("-inf")).item()
+
+
+@pytest.mark.parametrize("H", [16, 64])
+def test_sparse_mla_decode_rising_scores(H):
+    """Slots ordered by increasing score, so that the running maximum keeps
+    growing across chunks (every rescale path of the online softmax)."""
+    _say(f"sparse_mla_decode: rising scores, H {H}")
+    T, K, bs, nb = 2, 1000, 64, 20
+    cache_np = _mla_cache(nb, bs, 21)
+    rng = np.random.default_rng(22)
+    base = rng.standard_normal(512).astype(np.float32)
+    qn = np.stack([np.stack([base * (1.0 + 0.02 * h) for h in range(H)])] * T)
+    qn_bits = synth.f32_to_bf16_bits(qn * 0.5)
+    qp_bits = synth.f32_to_bf16_bits(np.zeros((T, H, 64), np.float32))
+    q0 = synth.bf16_bits_to_f32(qn_bits[0, 0]).astype(np.float64)
+    ids = rng.choice(nb * bs, K, replace=False)
+    order = np.argsort([q0 @ O.mla.mla_entry(cache_np, int(i))[0] for i in ids])
+    slots = np.stack([ids[order], ids[order[::-1]]]).astype(np.int32)  # rising, falling
+    _check_decode(qn_bits, qp_bits, cache_np, slots, 1.0 / np.sqrt(576.0))
 
 
 def test_sparse_mla_decode_full_size_sampled():
