@@ -134,8 +134,9 @@ def test_sparse_mla_decode_host_checks(lib):
     """Workspace query and argument validation; no device work."""
     nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
     ws = lib.sparse_mla_workspace_bytes
-    assert ws(64, 128, 2048) == 0                          # 512 workgroups: one pass
-    assert ws(2, 16, 2048) == 2 * 16 * 16 * (512 + 2) * 4  # 16 splits
+    assert ws(128, 128, 2048) == 0                         # 256 64-head workgroups: one pass
+    assert ws(64, 128, 2048) == 64 * 128 * 2 * (512 + 2) * 4   # 2 splits fill the chip
+    assert ws(2, 16, 2048) == 2 * 16 * 16 * (512 + 2) * 4  # 16-head groups, 16 splits
     assert ws(0, 16, 64) == 0 and ws(4, 24, 64) == 0 and ws(4, 16, 0) == 0
     f = lib.sparse_mla_decode
 
