@@ -334,7 +334,7 @@ def mla_leg(torch, lib, wl, slots, dev, steps, ev, arm, s_ptr, cpu_seconds):
     alg_bytes = valid * MLA_ENTRY_BYTES + rows * k * 4 + rows * MLA_HEADS * (576 * 2 + 512 * 4 + 4)
     achieved = flops / t_kernel / 1e12
     res = {
-        "kernel": "sparse_mla_decode_kernel",
+        "kernel": ("sparse_mla_decode_wide_kernel" if MLA_HEADS % 64 == 0 else "sparse_mla_decode_kernel"),
         "workload": f"{rows} rows x {MLA_HEADS} heads x top-{k} slots from this step, fp8 MLA cache "
                     f"{nb} blocks x 64 x {MLA_ENTRY_BYTES} B",
         "avg_launch_us": round(t_kernel * 1e6, 3),

@@ -86,7 +86,8 @@ def stats(args):
     lines = [f"# rocprofv3 kernel statistics", f"command: {args.command}",
              "name | calls | average_us | min_us | max_us | percent"]
     for r in rows:
-        lines.append(f"{r['Name']} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
+        name = r["Name"] if len(r["Name"]) <= 200 else r["Name"][:200] + " ..."
+        lines.append(f"{name} | {r['Calls']} | {float(r['AverageNs']) / 1e3:.3f} | "
                      f"{float(r['MinNs']) / 1e3:.3f} | {float(r['MaxNs']) / 1e3:.3f} | "
                      f"{float(r['Percentage']):.2f}")
     open(args.out, "w").write("\n".join(lines) + "\n")
