@@ -175,7 +175,8 @@ struct MlaStage {
   uint4 c[4];
   uint4 pe;
   uint4 sc;
-  int valid;  // token t < 32: slot valid
+  int valid;       // token t < 32: slot valid
+  uint32_t vmask;  // bit j: chunk token j valid
 };
 
 // Lane l of every wave loads the slot id of chunk token l & 31, without a
@@ -210,6 +211,7 @@ __device__ __forceinline__ MlaStage mla_gather(const uint8_t* __restrict__ cache
   st.pe = *reinterpret_cast<const uint4*>(cache + off_of(t >> 3) + kMlaRopeOff + 16 * (t & 7));
   st.sc = *reinterpret_cast<const uint4*>(cache + off + kMlaScaleOff);  // token t & 31
   st.valid = ok;
+  st.vmask = (uint32_t)__ballot(ok);  // lanes 0..31 hold tokens 0..31
   return st;
 }
 
@@ -226,15 +228,24 @@ __device__ __forceinline__ void tr4x4(uint32_t a, uint32_t b, uint32_t c, uint32
   o[3] = __builtin_amdgcn_perm(cd_hi, ab_hi, 0x07060302u);
 }
 
+// Invalid tokens (padding, ids outside the cache, past the split) were read
+// from entry 0; their codes and scales are staged as zeros, so whatever
+// bytes that entry holds cannot reach a product (their weights are 0 and
+// 0 * NaN would not be).
 __device__ __forceinline__ void mla_stage_to_lds(MlaChunkLds& sm, const MlaStage& st) {
   const int t = threadIdx.x;
   const int tg = t >> 5, dp = t & 31;
+  uint4 c[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(&sm.km[4 * tg + i][16 * dp]) = st.c[i];
-  const uint32_t w[4][4] = {{st.c[0].x, st.c[0].y, st.c[0].z, st.c[0].w},
-                            {st.c[1].x, st.c[1].y, st.c[1].z, st.c[1].w},
-                            {st.c[2].x, st.c[2].y, st.c[2].z, st.c[2].w},
-                            {st.c[3].x, st.c[3].y, st.c[3].z, st.c[3].w}};
+  for (int i = 0; i < 4; ++i) {
+    const bool v = (st.vmask >> (4 * tg + i)) & 1u;
+    c[i] = v ? st.c[i] : make_uint4(0u, 0u, 0u, 0u);
+    *reinterpret_cast<uint4*>(&sm.km[4 * tg + i][16 * dp]) = c[i];
+  }
+  const uint32_t w[4][4] = {{c[0].x, c[0].y, c[0].z, c[0].w},
+                            {c[1].x, c[1].y, c[1].z, c[1].w},
+                            {c[2].x, c[2].y, c[2].z, c[2].w},
+                            {c[3].x, c[3].y, c[3].z, c[3].w}};
   // this thread's 4 tokens x 16 dims, transposed: 64 contiguous bytes of slab tg
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
@@ -244,11 +255,73 @@ __device__ __forceinline__ void mla_stage_to_lds(MlaChunkLds& sm, const MlaStage
   }
   *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.pe;
   if (t < kMlaChunk) {
-    sm.sct[0][t] = __uint_as_float(st.sc.x);
-    sm.sct[1][t] = __uint_as_float(st.sc.y);
-    sm.sct[2][t] = __uint_as_float(st.sc.z);
-    sm.sct[3][t] = __uint_as_float(st.sc.w);
+    sm.sct[0][t] = st.valid ? __uint_as_float(st.sc.x) : 0.0f;
+    sm.sct[1][t] = st.valid ? __uint_as_float(st.sc.y) : 0.0f;
+    sm.sct[2][t] = st.valid ? __uint_as_float(st.sc.z) : 0.0f;
+    sm.sct[3][t] = st.valid ? __uint_as_float(st.sc.w) : 0.0f;
     sm.valid[t] = st.valid;
+  }
+}
+
+// The same chunk staged by 512 threads: thread t loads 8 code bytes of 4
+// tokens (tokens 4(t/64)..+3, bytes 8(t%64)..+7) and one 16-byte piece of an
+// entry's tail: a RoPE piece for t < 256 (token t/8, piece t%8), the tile
+// scales of token t%32 otherwise.
+struct MlaStage8 {
+  uint2 c[4];
+  uint4 tail;
+  int valid;       // token t % 32: slot valid
+  uint32_t vmask;  // bit j: chunk token j valid
+};
+
+__device__ __forceinline__ MlaStage8 mla_gather8(const uint8_t* __restrict__ cache, int id, int base,
+                                                 int lim, int64_t num_slots, uint32_t block_size,
+                                                 int64_t block_stride) {
+  const int t = threadIdx.x;
+  const bool ok = base + (t & 31) < lim && id >= 0 && (int64_t)id < num_slots;
+  const uint32_t s = ok ? (uint32_t)id : 0u;
+  const uint32_t blk = s / block_size;
+  const int64_t off = (int64_t)blk * block_stride + (int64_t)(s - blk * block_size) * kMlaEntry;
+  const int lo = (int)(uint32_t)off, hi = (int)(uint32_t)((uint64_t)off >> 32);
+  auto off_of = [&](int j) {  // j: lane holding the token's offset
+    return (int64_t)(((uint64_t)(uint32_t)__shfl(hi, j) << 32) | (uint32_t)__shfl(lo, j));
+  };
+  MlaStage8 st;
+  const int tg = t >> 6, dp = t & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    st.c[i] = *reinterpret_cast<const uint2*>(cache + off_of(4 * tg + i) + 8 * dp);
+  const int64_t tail = t < 256 ? off_of((t >> 3) & 31) + kMlaRopeOff + 16 * (t & 7) : off + kMlaScaleOff;
+  st.tail = *reinterpret_cast<const uint4*>(cache + tail);
+  st.valid = ok;
+  st.vmask = (uint32_t)__ballot(ok);  // lanes 0..31 hold tokens 0..31
+  return st;
+}
+
+__device__ __forceinline__ void mla_stage8_to_lds(MlaChunkLds& sm, const MlaStage8& st) {
+  const int t = threadIdx.x;
+  const int tg = t >> 6, dp = t & 63;
+  uint2 c[4];  // invalid tokens staged as zeros (see mla_stage_to_lds)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool v = (st.vmask >> (4 * tg + i)) & 1u;
+    c[i] = v ? st.c[i] : make_uint2(0u, 0u);
+    *reinterpret_cast<uint2*>(&sm.km[4 * tg + i][8 * dp]) = c[i];
+  }
+  uint32_t lo[4], hi[4];
+  tr4x4(c[0].x, c[1].x, c[2].x, c[3].x, lo);
+  tr4x4(c[0].y, c[1].y, c[2].y, c[3].y, hi);
+  *reinterpret_cast<uint4*>(&sm.vt[tg][8 * dp]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
+  *reinterpret_cast<uint4*>(&sm.vt[tg][8 * dp + 4]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
+  if (t < 256) {
+    *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.tail;
+  } else if (t < 256 + kMlaChunk) {
+    const int j = t - 256;
+    sm.sct[0][j] = st.valid ? __uint_as_float(st.tail.x) : 0.0f;
+    sm.sct[1][j] = st.valid ? __uint_as_float(st.tail.y) : 0.0f;
+    sm.sct[2][j] = st.valid ? __uint_as_float(st.tail.z) : 0.0f;
+    sm.sct[3][j] = st.valid ? __uint_as_float(st.tail.w) : 0.0f;
+    sm.valid[j] = st.valid;
   }
 }
 
@@ -393,9 +466,13 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
   }
 }
 
-// 64 heads per workgroup, 16 per wave; every wave scores the chunk over all
-// 576 dims and multiplies by all 512 value dims for its own heads, and the
-// four waves share the staged chunk (double-buffered, one barrier a chunk).
+// 64 heads per workgroup in eight waves: wave w takes heads 16(w%4)..+15
+// and latent tiles 2(w/4), 2(w/4)+1 (value dims 256(w/4)..+255) plus RoPE
+// step w/4.  The two waves of a head block add their partial scores through
+// LDS, so each wave holds a quarter of Q and half of O (under 256
+// registers: two waves share a SIMD), and the eight waves share the staged
+// chunk (double-buffered; a barrier for the partial scores and one for the
+// staging, per chunk).
 // Scores are formed transposed, S^T = K Q^T: lane (g, n) then holds head n
 // for tokens 4g..4g+3 and 16+4g..16+4g+3, which are exactly the eight
 // tokens it supplies as the A operand of P.V when the B operand (V) is read
@@ -404,13 +481,14 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 // chunk) and the running sum is reduced once at the end.  O is rescaled
 // only when a head's max grows by more than 2^8 (until then the weights
 // 2^(s - m) stay below 2^8, harmless in bf16 and fp32).
-__global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
+__global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
     const uint8_t* __restrict__ cache, int64_t num_slots, int64_t block_size, int64_t block_stride,
     const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   __shared__ MlaChunkLds buf[2];
+  __shared__ v4f xs[4][2][2][64];  // partial scores [head block][tile half][token half][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
   const int ngroups = heads / kMlaWideHeads;
@@ -420,58 +498,66 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
   const int base0 = split * split_len;
   const int lim = min(k, base0 + split_len);
   const int32_t* srow = slots + (int64_t)row * k;
-  const int head0 = hg * kMlaWideHeads + wv * kMlaHg;  // this wave's 16 heads
+  const int hw = wv & 3, dh = wv >> 2;  // head block, value-dim half
+  const int head0 = hg * kMlaWideHeads + hw * kMlaHg;  // this wave's 16 heads
 
-  // B operands of S^T: lane (g, n) holds head head0+n, dims 32s+8g .. +7
+  // B operands of S^T: lane (g, n) holds head head0+n, dims 256dh + 32s+8g .. +7
+  // of the latent part and 32dh+8g .. +7 of the RoPE part
   const int64_t qh = (int64_t)row * heads + head0 + n;
-  v8bf16 qa[kMlaKv / 32], qp[kMlaRope / 32];
+  v8bf16 qa[kMlaKv / 64];
 #pragma unroll
-  for (int s = 0; s < kMlaKv / 32; ++s)
-    qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q_nope + qh * kMlaKv + 32 * s + 8 * g));
-#pragma unroll
-  for (int s = 0; s < kMlaRope / 32; ++s)
-    qp[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q_pe + qh * kMlaRope + 32 * s + 8 * g));
+  for (int s = 0; s < kMlaKv / 64; ++s)
+    qa[s] = as_bf16x8(*reinterpret_cast<const uint4*>(q_nope + qh * kMlaKv + 256 * dh + 32 * s + 8 * g));
+  const v8bf16 qp = as_bf16x8(*reinterpret_cast<const uint4*>(q_pe + qh * kMlaRope + 32 * dh + 8 * g));
 
   const v4f zero = {0.0f, 0.0f, 0.0f, 0.0f};
-  v4f o[kMlaKv / 16];  // O rows = heads head0+4g+e, column dim 16i+n
+  v4f o[kMlaKv / 32];  // O rows = heads head0+4g+e, column dim 256dh + 16i + n
 #pragma unroll
-  for (int i = 0; i < kMlaKv / 16; ++i) o[i] = zero;
+  for (int i = 0; i < kMlaKv / 32; ++i) o[i] = zero;
   float m_run = -INFINITY, l_run = 0.0f;  // head head0+n (l: this lane's tokens only)
 
   const int nchunks = base0 < lim ? (lim - base0 + kMlaChunk - 1) / kMlaChunk : 0;
   if (nchunks > 0) {  // uniform
     int id = mla_load_id(srow, base0, lim);
-    MlaStage st = mla_gather(cache, id, base0, lim, num_slots, (uint32_t)block_size, block_stride);
+    MlaStage8 st = mla_gather8(cache, id, base0, lim, num_slots, (uint32_t)block_size, block_stride);
     id = mla_load_id(srow, base0 + kMlaChunk, lim);
-    mla_stage_to_lds(buf[0], st);
-    st = mla_gather(cache, id, base0 + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
+    mla_stage8_to_lds(buf[0], st);
+    st = mla_gather8(cache, id, base0 + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
     id = mla_load_id(srow, base0 + 2 * kMlaChunk, lim);
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
       const MlaChunkLds& b = buf[c & 1];
-      // S^T for tokens n (acc 0) and 16+n (acc 1), per latent tile, scaled
+      // partial S^T over this wave's two tiles (each scaled) and RoPE step,
+      // tokens n (acc 0) and 16+n (acc 1)
       v4f s0 = zero, s1 = zero;
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const int w = 2 * dh + w2;
         v4f a0 = zero, a1 = zero;
 #pragma unroll
         for (int st4 = 0; st4 < 4; ++st4) {
           const int col = w * kMlaTile + 32 * st4 + 8 * g;
           const uint2 c0 = *reinterpret_cast<const uint2*>(&b.km[n][col]);
           const uint2 c1 = *reinterpret_cast<const uint2*>(&b.km[16 + n][col]);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c0), qa[4 * w + st4], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c1), qa[4 * w + st4], a1, 0, 0, 0);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c0), qa[4 * w2 + st4], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c1), qa[4 * w2 + st4], a1, 0, 0, 0);
         }
         s0 += a0 * *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
         s1 += a1 * *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
       }
-#pragma unroll
-      for (int rs = 0; rs < kMlaRope / 32; ++rs) {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(&b.pe[n][32 * rs + 8 * g]);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(&b.pe[16 + n][32 * rs + 8 * g]);
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp[rs], s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp[rs], s1, 0, 0, 0);
+      {
+        const uint4 p0 = *reinterpret_cast<const uint4*>(&b.pe[n][32 * dh + 8 * g]);
+        const uint4 p1 = *reinterpret_cast<const uint4*>(&b.pe[16 + n][32 * dh + 8 * g]);
+        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp, s0, 0, 0, 0);
+        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp, s1, 0, 0, 0);
       }
+      // the pair's halves meet in LDS; both waves form the same sum
+      // (x + y == y + x), hence the same softmax state
+      xs[hw][dh][0][lane] = s0;
+      xs[hw][dh][1][lane] = s1;
+      __syncthreads();
+      s0 += xs[hw][dh ^ 1][0][lane];
+      s1 += xs[hw][dh ^ 1][1][lane];
       // scores in log2 units; token order 4g+e, then 16+4g+e
       const int4 ok0 = *reinterpret_cast<const int4*>(&b.valid[4 * g]);
       const int4 ok1 = *reinterpret_cast<const int4*>(&b.valid[16 + 4 * g]);
@@ -493,7 +579,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
 #pragma unroll
         for (int e = 0; e < 4; ++e) ce[e] = __shfl(corr, 4 * g + e);
 #pragma unroll
-        for (int i = 0; i < kMlaKv / 16; ++i) {
+        for (int i = 0; i < kMlaKv / 32; ++i) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) o[i][e] *= ce[e];
         }
@@ -505,9 +591,10 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
         pv[i] = __builtin_amdgcn_exp2f(sv[i] - mu);
         l_run += pv[i];
       }
-      // P.V per latent tile: weights times the tile's scales, bf16
+      // P.V over this wave's two latent tiles: weights times the tile's scales, bf16
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w2 = 0; w2 < 2; ++w2) {
+        const int w = 2 * dh + w2;
         const v4f t0 = *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
         const v4f t1 = *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
         const v8bf16 pa = {(__bf16)(pv[0] * t0[0]), (__bf16)(pv[1] * t0[1]), (__bf16)(pv[2] * t0[2]),
@@ -517,14 +604,14 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
         for (int d = 0; d < kMlaTile / 16; ++d) {
           const int dim = w * kMlaTile + 16 * d + n;
           const uint2 cv = make_uint2(b.vt[g][dim], b.vt[4 + g][dim]);
-          o[w * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(cv), o[w * 8 + d], 0, 0, 0);
+          o[w2 * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(cv), o[w2 * 8 + d], 0, 0, 0);
         }
       }
       // stage the next chunk into the other buffer (its last readers passed
       // the previous barrier) and issue the loads of the one after; past the
       // end these touch only valid addresses and are never read
-      mla_stage_to_lds(buf[(c + 1) & 1], st);
-      st = mla_gather(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
+      mla_stage8_to_lds(buf[(c + 1) & 1], st);
+      st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
                       block_stride);
       id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
       __syncthreads();
@@ -541,16 +628,16 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_wide_kernel(
     const int64_t rh = rh0 + 4 * g + e;
     if (nsplit == 1) {
       const float inv = le > 0.0f ? 1.0f / le : 0.0f;
-      float* dst = out + rh * kMlaKv + n;
+      float* dst = out + rh * kMlaKv + 256 * dh + n;
 #pragma unroll
-      for (int i = 0; i < kMlaKv / 16; ++i) dst[16 * i] = o[i][e] * inv;
-      if (lse && n == 0) lse[rh] = le > 0.0f ? (me + __log2f(le)) * 0.69314718055994531f : -INFINITY;
+      for (int i = 0; i < kMlaKv / 32; ++i) dst[16 * i] = o[i][e] * inv;
+      if (lse && dh == 0 && n == 0) lse[rh] = le > 0.0f ? (me + __log2f(le)) * 0.69314718055994531f : -INFINITY;
     } else {
       const int64_t rhs = rh * nsplit + split;
-      float* dst = ws_o + rhs * kMlaKv + n;
+      float* dst = ws_o + rhs * kMlaKv + 256 * dh + n;
 #pragma unroll
-      for (int i = 0; i < kMlaKv / 16; ++i) dst[16 * i] = o[i][e];
-      if (n == 0) {
+      for (int i = 0; i < kMlaKv / 32; ++i) dst[16 * i] = o[i][e];
+      if (dh == 0 && n == 0) {
         ws_ml[2 * rhs] = me;
         ws_ml[2 * rhs + 1] = le;
       }
@@ -640,7 +727,7 @@ extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t r
   float* ws_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
   float* ws_ml = need ? ws_o + (size_t)rows * heads * p.nsplit * kMlaKv : nullptr;
   launch(p.wide ? sparse_mla_decode_wide_kernel : sparse_mla_decode_kernel, dim3((unsigned)p.grid),
-         dim3(256), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_pe, (int)heads,
+         dim3(p.wide ? 512 : 256), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_pe, (int)heads,
          (const uint8_t*)cache, num_blocks * (int64_t)block_size, (int64_t)block_size,
          (int64_t)block_size * kMlaEntry, slots, k, sm_scale * 1.4426950408889634f, p.nsplit,
          p.split_len, out, lse, ws_o, ws_ml);

@@ -179,6 +179,26 @@ def test_sparse_mla_decode_rising_scores(H):
     _check_decode(qn_bits, qp_bits, cache_np, slots, 1.0 / np.sqrt(576.0))
 
 
+@pytest.mark.parametrize("H", [16, 64])
+def test_sparse_mla_decode_poisoned_entry_zero(H):
+    """Skipped ids (padding, out of range, past the end of a split) must not
+    let the bytes of any entry reach the result: entry 0 holds NaN codes, a
+    NaN scale and NaN RoPE values, and no row names slot 0."""
+    _say(f"sparse_mla_decode: NaN-poisoned entry 0 behind skipped ids, H {H}")
+    T, K, bs, nb = 3, 150, 64, 10
+    cache_np = _mla_cache(nb, bs, 31)
+    cache_np[0, 0, :512] = 0x7F
+    cache_np[0, 0, 512:528] = np.frombuffer(np.full(4, np.nan, np.float32).tobytes(), np.uint8)
+    cache_np[0, 0, 528:] = 0xFF
+    rng = np.random.default_rng(32)
+    slots = np.stack([rng.choice(np.arange(1, nb * bs), K, replace=False) for _ in range(T)]).astype(np.int32)
+    slots[0, ::3] = -1
+    slots[1, 5::9] = nb * bs + 3
+    slots[2, 100:] = -1
+    qn, qp = _mla_query(T, H, 33)
+    _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0))
+
+
 def test_sparse_mla_decode_full_size_sampled():
     """The decode workload's shape (64 rows, 128 heads, top-2048 over a
     640-block cache), one pass on the GPU, four rows checked."""
