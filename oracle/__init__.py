@@ -25,7 +25,7 @@ Parity status: every function here is pinned by tests/test_oracle_pins.py.
 from .indexer import (  # noqa: F401
     BLOCK, HEADS, DIM, BLOCK_BYTES, FLT_MIN, INV_448,
     e4m3fn_table, fp8_encode, quantize_rows, quantize_q,
-    k_cache_write, gather_indexer_k, paged_mqa_logits, mqa_logits,
+    k_cache_write, gather_indexer_k, paged_mqa_logits, mqa_logits, mqa_logits_chunked,
     topk_rows, topk_to_global_slots, decode_limits,
 )
 from . import mla  # noqa: F401,E402  (fp8 MLA cache and sparse MLA decode)

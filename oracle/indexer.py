@@ -290,6 +290,44 @@ def mqa_logits(q_codes, w, k_codes, k_scale, cu_seq_lens, width, rows=None):
     return out
 
 
+def mqa_logits_chunked(q_codes, w, k_codes, k_scale, cu_q, cu_k, width, rows=None):
+    """Prefill logits of a chunk of each request's queries against the
+    request's whole gathered context (chunked prefill; a ragged batch of
+    such requests).
+
+    Request b's queries are rows [cu_q[b], cu_q[b+1]) and its keys the K rows
+    [cu_k[b], cu_k[b+1]) that ``gather_indexer_k`` writes with cu_k (ROCm/ATOM
+    PR #1094, Technical Details, "sparse MLA prefill KV mapping"; vLLM PR
+    #25869, the gather over cu_seq_lens).  The queries are the last
+    n_q = cu_q[b+1] - cu_q[b] tokens of the request's n_k = cu_k[b+1] - cu_k[b]
+    tokens, so query i sees keys [0, n_k - n_q + i + 1) -- the rule a decode
+    request with next_n = n_q follows (reading R4); n_q = n_k is plain prefill.
+    Column j is the request-local key index; later columns are -inf (all of
+    them when n_k - n_q + i + 1 <= 0, a context shorter than its chunk).  A
+    row whose limit exceeds ``width`` is not scored and stays NaN, like rows
+    outside ``rows`` and rows of no request.
+    """
+    cq = np.asarray(cu_q).tolist()
+    ck = np.asarray(cu_k).tolist()
+    total = q_codes.shape[0]
+    out = np.full((total, width), np.nan, dtype=np.float64)
+    want = set(range(total)) if rows is None else set(int(r) for r in rows)
+    for b in range(len(cq) - 1):
+        n_q = cq[b + 1] - cq[b]
+        n_k = ck[b + 1] - ck[b]
+        for i in range(max(n_q, 0)):
+            p = cq[b] + i
+            lim = max(n_k - n_q + i + 1, 0)
+            if p not in want or lim > width:
+                continue
+            row = np.full(width, -np.inf, dtype=np.float64)
+            if lim > 0:
+                row[:lim] = _score(q_codes[p], w[p], k_codes[ck[b]:ck[b] + lim],
+                                   k_scale[ck[b]:ck[b] + lim])
+            out[p] = row
+    return out
+
+
 # --------------------------------------------------------------------------
 # top-k and slot ids
 # --------------------------------------------------------------------------

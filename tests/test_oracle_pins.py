@@ -354,6 +354,61 @@ def test_decode_next_n_equals_prefill_on_gathered_k():
     assert np.array_equal(Ld, Lp)
 
 
+def test_chunked_prefill_equals_paged_decode_with_next_n():
+    """Chunked prefill: the last N tokens of each request scored against its
+    gathered context == paged decode with next_n = N (a different route: the
+    paged cache and the decode limit rule)."""
+    N, ctx = 5, [150, 97, 64]
+    wl, pool, qc, weff = _small_workload(ctx, N, 3, 12, seed=15)
+    Ld = O.paged_mqa_logits(qc, weff, pool, wl.block_table, wl.ctx, N, 192)
+    cu_k = np.concatenate([[0], np.cumsum(ctx)])
+    kv, ks = O.gather_indexer_k(pool, wl.block_table, cu_k, int(cu_k[-1]))
+    cu_q = np.arange(len(ctx) + 1) * N
+    Lc = O.mqa_logits_chunked(qc.reshape(-1, 64, 128), weff, kv, ks, cu_q, cu_k, 192)
+    assert np.array_equal(Ld, Lc)
+
+
+def test_chunked_prefill_whole_request_is_prefill_and_batching_is_invisible():
+    """n_q = n_k reduces to mqa_logits; in a ragged batch each request's rows
+    equal that request scored alone."""
+    rng = np.random.default_rng(16)
+    n_q, n_k = [7, 1, 12, 0, 3], [30, 1, 12, 9, 70]
+    cu_q = np.concatenate([[0], np.cumsum(n_q)])
+    cu_k = np.concatenate([[0], np.cumsum(n_k)])
+    q = O.fp8_encode(rng.standard_normal((cu_q[-1], 64, 128)).astype(np.float32))
+    w = rng.standard_normal((cu_q[-1], 64)).astype(np.float32)
+    k = O.fp8_encode(rng.standard_normal((cu_k[-1], 128)).astype(np.float32))
+    ks = (rng.random(cu_k[-1]) + 0.5).astype(np.float32)
+    L = O.mqa_logits_chunked(q, w, k, ks, cu_q, cu_k, 80)
+    for b in range(len(n_q)):
+        qs, ksl = slice(cu_q[b], cu_q[b + 1]), slice(cu_k[b], cu_k[b + 1])
+        one = O.mqa_logits_chunked(q[qs], w[qs], k[ksl], ks[ksl], [0, n_q[b]], [0, n_k[b]], 80)
+        assert np.array_equal(L[qs], one)
+        if n_q[b] == n_k[b]:
+            assert np.array_equal(one, O.mqa_logits(q[qs], w[qs], k[ksl], ks[ksl], [0, n_q[b]], 80))
+        for i in range(n_q[b]):  # the limit rule, column by column
+            lim = n_k[b] - n_q[b] + i + 1
+            assert np.all(np.isfinite(one[i, :lim])) and np.all(np.isneginf(one[i, lim:]))
+
+
+def test_chunked_prefill_short_context_and_width_clamp():
+    """A context shorter than its chunk leaves leading rows with no visible
+    key (all -inf); a row whose limit exceeds the width is not written."""
+    rng = np.random.default_rng(17)
+    q = O.fp8_encode(rng.standard_normal((6, 64, 128)).astype(np.float32))
+    w = np.ones((6, 64), np.float32)
+    k = O.fp8_encode(rng.standard_normal((10, 128)).astype(np.float32))
+    ks = np.ones(10, np.float32)
+    L = O.mqa_logits_chunked(q, w, k, ks, [0, 4, 6], [0, 2, 10], 7)
+    # request 0: n_q 4, n_k 2 -> limits 0, 0, 1, 2
+    assert np.all(np.isneginf(L[0])) and np.all(np.isneginf(L[1]))
+    assert np.isfinite(L[2, 0]) and np.all(np.isneginf(L[2, 1:]))
+    assert np.all(np.isfinite(L[3, :2])) and np.all(np.isneginf(L[3, 2:]))
+    # request 1: n_q 2, n_k 8 -> limits 7 (= width: written) and 8 (> width: not written)
+    assert np.all(np.isfinite(L[4]))
+    assert np.all(np.isnan(L[5]))
+
+
 def test_exact_power_of_two_scaling():
     """P7: scaling w or every k_scale by 2^m scales the logits by exactly 2^m."""
     wl, pool, qc, weff = _small_workload([150, 33], 2, 3, 8, seed=15)
