@@ -189,6 +189,33 @@ int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
                int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
 
 /*
+ * mqa_logits_chunked -- prefill logits of a chunk of each request's queries
+ * against the request's whole gathered context (chunked prefill, ragged
+ * batches of such requests).  The pages fix the gather over cu_seq_lens
+ * (vLLM PR #25869 review) and name the prefill KV mapping (ROCm/ATOM PR
+ * #1094, Technical Details) without the causal rule; the rule taken is the
+ * decode one: the queries are the last n_q = cu_q[b+1] - cu_q[b] of the
+ * request's n_k = cu_k[b+1] - cu_k[b] tokens, so request-local query i sees
+ * keys [0, n_k - n_q + i + 1) (none when that is <= 0).  Same score as
+ * paged_mqa_logits; column j is the request-local key index (K row
+ * cu_k[b] + j); columns past the limit are -inf.  A row whose limit exceeds
+ * logits_stride is left untouched, as are rows of no request.  With
+ * cu_k = cu_q this is mqa_logits.
+ *
+ *   q_fp8 [total_q, 64, 128]; weights [total_q, 64];
+ *   k_fp8 [total_k, 128]; k_scale [total_k] (gather_indexer_k with cu_k);
+ *   cu_seq_lens_q, cu_seq_lens_k [batch+1] int32 (device),
+ *   cu_q[batch] <= total_q, cu_k[batch] <= total_k;
+ *   logits [total_q, logits_stride];
+ *   row_len_out / row_req_out: [total_q] int32, the row's limit and b (may be NULL)
+ */
+int mqa_logits_chunked(const void* q_fp8, const float* weights, const void* k_fp8,
+                       const float* k_scale, const int32_t* cu_seq_lens_q,
+                       const int32_t* cu_seq_lens_k, int32_t batch, int64_t total_q,
+                       int64_t total_k, float* logits, int64_t logits_stride,
+                       int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
+
+/*
  * topk_rows -- per-row top-k of the indexer logits (ROCm/ATOM PR #1094,
  * Technical Details: sparse top-k handed on in a 2-D index buffer).
  *

@@ -7,7 +7,7 @@ library; the first call does, and raises if it has not been built.
 """
 __all__ = [
     "indexer_k_cache_write", "indexer_q_quant", "gather_indexer_k", "paged_mqa_logits",
-    "mqa_logits", "topk_rows", "topk_workspace_bytes", "topk_to_global_slots", "decode_indexer",
+    "mqa_logits", "mqa_logits_chunked", "topk_rows", "topk_workspace_bytes", "topk_to_global_slots", "decode_indexer",
     "mla_cache_write", "sparse_mla_decode", "sparse_mla_workspace_bytes",
 ]
 

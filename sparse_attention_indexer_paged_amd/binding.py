@@ -37,6 +37,8 @@ SIGNATURES = {
                          _i32, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p],
     "mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _c_void_p,
                    _i64, _c_void_p, _c_void_p, _c_void_p],
+    "mqa_logits_chunked": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
+                           _i64, _i64, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p],
     "topk_workspace_bytes": [_i32, _i64, _i32],
     "topk_rows": [_c_void_p, _i64, _c_void_p, _i32, _i32, _c_void_p, _c_void_p, ctypes.c_size_t,
                   _c_void_p],
@@ -293,6 +295,37 @@ def mqa_logits(q_fp8, weights, k_fp8, k_scale, cu_seq_lens, width, logits=None, 
     _check(load().mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(k_fp8), _ptr(k_scale),
                              _ptr(cu_seq_lens), batch, total, _ptr(logits), logits.stride(0),
                              _ptr(row_len), _ptr(row_req), _stream()), "mqa_logits")
+    return logits, row_len, row_req
+
+
+def mqa_logits_chunked(q_fp8, weights, k_fp8, k_scale, cu_q, cu_k, width, logits=None, row_len=None,
+                       row_req=None):
+    """Chunked-prefill logits: request b's queries (rows cu_q[b]..cu_q[b+1]) are
+    the last tokens of its context (K rows cu_k[b]..cu_k[b+1]).  q_fp8 u8
+    [total_q,64,128]; weights f32 [total_q,64]; k_fp8 u8 [total_k,128]; k_scale
+    f32 [total_k]; cu_q, cu_k i32 [B+1]."""
+    _need(q_fp8, torch.uint8, "q_fp8", 3)
+    _need(weights, torch.float32, "weights", 2)
+    _need(k_fp8, torch.uint8, "k_fp8", 2)
+    _need(k_scale, torch.float32, "k_scale", 1)
+    _need(cu_q, torch.int32, "cu_q", 1)
+    _need(cu_k, torch.int32, "cu_k", 1)
+    total_q, total_k = q_fp8.shape[0], k_fp8.shape[0]
+    if weights.shape[0] != total_q or k_scale.shape[0] != total_k:
+        raise ValueError("weights need one row per query, k_scale one per key")
+    if cu_q.shape[0] != cu_k.shape[0]:
+        raise ValueError("cu_q and cu_k need one entry per request plus one")
+    batch = cu_q.shape[0] - 1
+    dev = q_fp8.device
+    logits = torch.empty((total_q, width), dtype=torch.float32, device=dev) if logits is None else logits
+    row_len = torch.empty((total_q,), dtype=torch.int32, device=dev) if row_len is None else row_len
+    row_req = torch.empty((total_q,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    _out(logits, torch.float32, "logits", (total_q, width))
+    _out(row_len, torch.int32, "row_len", (total_q,))
+    _out(row_req, torch.int32, "row_req", (total_q,))
+    _check(load().mqa_logits_chunked(_ptr(q_fp8), _ptr(weights), _ptr(k_fp8), _ptr(k_scale), _ptr(cu_q),
+                                     _ptr(cu_k), batch, total_q, total_k, _ptr(logits), logits.stride(0),
+                                     _ptr(row_len), _ptr(row_req), _stream()), "mqa_logits_chunked")
     return logits, row_len, row_req
 
 

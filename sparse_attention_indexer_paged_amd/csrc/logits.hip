@@ -83,6 +83,7 @@ __device__ __forceinline__ void store_logit4(float* p, float4 v) {
 constexpr uint32_t kNaNBits = 0x7FC00000u;
 
 __device__ __forceinline__ int64_t min64(int64_t a, int64_t b) { return a < b ? a : b; }
+__device__ __forceinline__ int64_t max64(int64_t a, int64_t b) { return a > b ? a : b; }
 
 static inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
@@ -527,11 +528,16 @@ __device__ __forceinline__ v8i pf_operand(const PfBlock& blk, int t) {
 #else
 #define SAI_PF_ATTR
 #endif
+// Request b's query rows are [cu[b], cu[b+1]) and its keys the K rows
+// [cu_k[b], cu_k[b+1]); the queries are the last n_q of the request's n_k
+// tokens, so request-local query i sees keys [0, n_k - n_q + i + 1) (plain
+// prefill: cu_k = cu).  Rows whose limit exceeds the stride are not written.
 __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ k,
-    const float* __restrict__ ks, const int32_t* __restrict__ cu, int32_t batch, int64_t total,
-    float* __restrict__ logits, int64_t stride, int32_t* __restrict__ row_len_out,
-    int32_t* __restrict__ row_req_out, int32_t nchunks, int32_t ntiles_max, bool vec) {
+    const float* __restrict__ ks, const int32_t* __restrict__ cu, const int32_t* __restrict__ cu_k,
+    int32_t batch, int64_t total, float* __restrict__ logits, int64_t stride,
+    int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out, int32_t nchunks,
+    int32_t ntiles_max, bool vec) {
   extern __shared__ int smem[];
   int* s_tile = smem;                  // [batch+1] prefix of query tiles
   int* scratch = smem + (batch + 1);
@@ -570,8 +576,13 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
     if (s_tile[mid] <= tile) lo = mid; else hi = mid;
   }
   const int b = lo;
-  const int64_t base_tok = cu[b];
-  const int len = (int)min64(max(cu[b + 1] - cu[b], 0), stride);
+  const int64_t base_tok = cu[b];   // first query row
+  const int64_t kb0 = cu_k[b];      // first key row
+  const int nq = max(cu[b + 1] - cu[b], 0);
+  const int nk = max(cu_k[b + 1] - kb0, 0);
+  const int off = nk - nq;          // keys before the first query's own
+  // rows written: i with off + i + 1 <= stride; keys in play: the first nk
+  const int len = (int)max64(0, min64(nq, stride - off));
   const int i0 = (tile - s_tile[b]) * kPfTileRows;
   if (i0 >= len) return;  // the whole tile lies past a clamped request
 
@@ -586,16 +597,16 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
   const int wave = threadIdx.x >> 6;
   const int ir0 = i0 + wave * kPfRowsPerWave;            // first request-local row of this wave
   const int nrows = max(0, min(kPfRowsPerWave, len - ir0));
-  const int wlim = ir0 + nrows;                          // keys visible to the wave's last row
+  const int wlim = off + ir0 + nrows;                    // keys visible to the wave's last row
 
   if (chunk == 0 && lane < nrows) {
-    if (row_len_out) row_len_out[base_tok + ir0 + lane] = ir0 + lane + 1;
+    if (row_len_out) row_len_out[base_tok + ir0 + lane] = max(off + ir0 + lane + 1, 0);
     if (row_req_out) row_req_out[base_tok + ir0 + lane] = b;
   }
 
   const int col0 = chunk * kChunk;
   const int col_end = (int)min64((int64_t)col0 + kChunk, stride);
-  const int kend = min(col_end, min(i0 + kPfTileRows, len));  // keys any row of the tile sees
+  const int kend = min(col_end, off + min(i0 + kPfTileRows, len));  // keys any row of the tile sees
   const int nblk = kend > col0 ? cdiv_i(kend - col0, kBlock) : 0;
   const float ninf = __uint_as_float(kNegInfBits);
 
@@ -630,11 +641,11 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
   // loop is unrolled by DEPTH so the register stages rotate statically, and
   // no global store sits in it (results go to s_res), so the in-order vmcnt
   // accounting only ever waits for the oldest fetch.
-  const int64_t kbase = base_tok + col0;
+  const int64_t kbase = kb0 + col0;
   PfStage sa, sb, sc;
   if (nblk > 0) {
     sc = pf_fetch(k, ks, kbase, total);
-    pf_store(s_k[0], sc, len - col0);  // waits for Q and w as well
+    pf_store(s_k[0], sc, nk - col0);  // waits for Q and w as well
     sa = pf_fetch(k, ks, kbase + kBlock, total);
     if (SAI_PF_DEPTH > 2) sb = pf_fetch(k, ks, kbase + 2 * kBlock, total);
   }
@@ -690,13 +701,13 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
       const float sc = blk.scale[lane];                                                       \
       _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r) {                            \
         const float v = reduce_scatter4(p[r][0], p[r][1], p[r][2], p[r][3]) * sc;             \
-        res[r * kChunk + j_ * kBlock + lane] = select_f(col < ir0 + r + 1, v, kNegInfBits);   \
+        res[r * kChunk + j_ * kBlock + lane] = select_f(col < off + ir0 + r + 1, v, kNegInfBits); \
       }                                                                                       \
     } else if (j_ < nblk) { /* steps past the last block write nothing */                   \
       _Pragma("unroll") for (int r = 0; r < kPfRowsPerWave; ++r)                              \
         res[r * kChunk + j_ * kBlock + lane] = ninf;                                          \
     }                                                                                         \
-    pf_store(s_k[(j_ + 1) & 1], CUR, len - (key0 + kBlock));                                   \
+    pf_store(s_k[(j_ + 1) & 1], CUR, nk - (key0 + kBlock));                                    \
     __syncthreads();                                                                          \
   }
 #if SAI_PF_DEPTH > 2
@@ -780,25 +791,45 @@ extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const v
   }
 }
 
-extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
-                          const float* k_scale, const int32_t* cu_seq_lens, int32_t batch,
-                          int64_t total_tokens, float* logits, int64_t logits_stride,
-                          int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
-  if (batch < 0 || total_tokens < 0 || logits_stride < 0) return SAI_EINVAL;
-  if (batch == 0 || total_tokens == 0) return SAI_OK;
-  if (!q_fp8 || !weights || !k_fp8 || !k_scale || !cu_seq_lens || !logits || logits_stride == 0)
-    return SAI_EINVAL;
-  if (!aligned16(q_fp8) || !aligned16(weights) || !aligned16(k_fp8)) return SAI_EINVAL;
+namespace {
+int launch_prefill(const void* q_fp8, const float* weights, const void* k_fp8, const float* k_scale,
+                   const int32_t* cu_q, const int32_t* cu_k, int32_t batch, int64_t total_q,
+                   int64_t total_k, float* logits, int64_t logits_stride, int32_t* row_len_out,
+                   int32_t* row_req_out, hipStream_t stream) {
+  if (batch < 0 || total_q < 0 || total_k < 0 || logits_stride < 0) return SAI_EINVAL;
+  if (batch == 0 || total_q == 0) return SAI_OK;
+  if (!q_fp8 || !weights || !cu_q || !cu_k || !logits || logits_stride == 0) return SAI_EINVAL;
+  if (total_k > 0 && (!k_fp8 || !k_scale)) return SAI_EINVAL;
+  if (!aligned16(q_fp8) || !aligned16(weights) || (total_k > 0 && !aligned16(k_fp8))) return SAI_EINVAL;
   if (batch > 4096 || logits_stride > 0x7FFFFFFF - kChunk) return SAI_EUNSUPPORTED;
   const int64_t nchunks = (logits_stride + kChunk - 1) / kChunk;
-  const int64_t ntiles = (total_tokens + kPfTileRows - 1) / kPfTileRows + batch;
+  const int64_t ntiles = (total_q + kPfTileRows - 1) / kPfTileRows + batch;
   const int64_t G = 8 * ((ntiles + 7) / 8) * nchunks;
   if (G > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   // prefix of query tiles [batch+1] + the block scan's scratch [waves+1]
   const size_t lds = (size_t)((batch + 1) + kPfWaves + 1) * sizeof(int);
   launch(prefill_logits_kernel, dim3((unsigned)G), dim3(kPfThreads), lds, stream,
-                     (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_seq_lens,
-                     batch, total_tokens, logits, logits_stride, row_len_out, row_req_out,
-                     (int32_t)nchunks, (int32_t)ntiles, logits_stride % 4 == 0 && aligned16(logits));
+         (const uint8_t*)q_fp8, weights, (const uint8_t*)k_fp8, k_scale, cu_q, cu_k, batch,
+         total_k, logits, logits_stride, row_len_out, row_req_out, (int32_t)nchunks,
+         (int32_t)ntiles, logits_stride % 4 == 0 && aligned16(logits));
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
+}
+}  // namespace
+
+extern "C" int mqa_logits(const void* q_fp8, const float* weights, const void* k_fp8,
+                          const float* k_scale, const int32_t* cu_seq_lens, int32_t batch,
+                          int64_t total_tokens, float* logits, int64_t logits_stride,
+                          int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
+  if (total_tokens > 0 && batch > 0 && (!k_fp8 || !k_scale)) return SAI_EINVAL;
+  return launch_prefill(q_fp8, weights, k_fp8, k_scale, cu_seq_lens, cu_seq_lens, batch, total_tokens,
+                        total_tokens, logits, logits_stride, row_len_out, row_req_out, stream);
+}
+
+extern "C" int mqa_logits_chunked(const void* q_fp8, const float* weights, const void* k_fp8,
+                                  const float* k_scale, const int32_t* cu_seq_lens_q,
+                                  const int32_t* cu_seq_lens_k, int32_t batch, int64_t total_q,
+                                  int64_t total_k, float* logits, int64_t logits_stride,
+                                  int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
+  return launch_prefill(q_fp8, weights, k_fp8, k_scale, cu_seq_lens_q, cu_seq_lens_k, batch, total_q,
+                        total_k, logits, logits_stride, row_len_out, row_req_out, stream);
 }

@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
         "gather_indexer_k",
-        "paged_mqa_logits", "mqa_logits", "topk_workspace_bytes", "topk_rows",
+        "paged_mqa_logits", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
         "topk_to_global_slots", "topk_rows_slots", "mla_cache_write", "sparse_mla_workspace_bytes",
         "sparse_mla_decode"])
 
@@ -155,3 +155,19 @@ def test_sparse_mla_decode_host_checks(lib):
     assert call(scale=float("nan")) == SAI_EINVAL
     assert call(k=2048) == SAI_EWORKSPACE                  # split path needs a workspace
     assert call(k=2048, w=fake, wb=ws(2, 16, 2048) - 1) == SAI_EWORKSPACE
+
+
+def test_mqa_logits_chunked_host_checks(lib):
+    """Argument validation of the chunked prefill call; no device work."""
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    f = lib.mqa_logits_chunked
+
+    def call(q=fake, cq=fake, ck=fake, batch=2, tq=10, tk=30, stride=64, k=fake):
+        return f(q, fake, k, fake, cq, ck, batch, tq, tk, fake, stride, nul, nul, nul)
+
+    assert call(batch=0) == SAI_OK and call(tq=0) == SAI_OK
+    assert call(batch=-1) == SAI_EINVAL and call(tk=-1) == SAI_EINVAL
+    assert call(ck=nul) == SAI_EINVAL and call(cq=nul) == SAI_EINVAL and call(q=nul) == SAI_EINVAL
+    assert call(k=nul) == SAI_EINVAL
+    assert call(stride=0) == SAI_EINVAL
+    assert call(batch=5000) == SAI_EUNSUPPORTED

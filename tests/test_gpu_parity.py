@@ -367,6 +367,77 @@ def test_prefill_matches_decode_next_n():
     assert torch.equal(ld, lp)
 
 
+def _chunked_case(ctx, n_q, width, seed, sentinel=None):
+    """Gather each request's whole context, score a chunk of its last n_q
+    tokens on the GPU and with the oracle."""
+    wl = synth.custom(len(ctx), 0, ctx, num_blocks=sum(-(-c // 64) for c in ctx) + 3,
+                      bt_width=max(-(-c // 64) for c in ctx) + 1, seed=seed)
+    g = GpuWorkload(wl)
+    o = OracleWorkload(wl)
+    cu_k = np.concatenate([[0], np.cumsum(ctx)]).astype(np.int32)
+    cu_q = np.concatenate([[0], np.cumsum(n_q)]).astype(np.int32)
+    tq, tk = int(cu_q[-1]), int(cu_k[-1])
+    rng = np.random.default_rng(seed + 1)
+    qbits = synth.f32_to_bf16_bits(rng.standard_normal((tq, 64, 128)).astype(np.float32))
+    w = (rng.standard_normal((tq, 64)) / 64).astype(np.float32)
+    qf, weff, _ = sai.indexer_q_quant(bf16_tensor(qbits), torch.from_numpy(w).to(DEV))
+    ck, cq = torch.from_numpy(cu_k).to(DEV), torch.from_numpy(cu_q).to(DEV)
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, ck, tk)
+    logits = torch.full((tq, width), sentinel if sentinel is not None else 0.0, dtype=torch.float32, device=DEV)
+    logits, row_len, row_req = sai.mqa_logits_chunked(qf, weff, kv, ks, cq, ck, width, logits=logits)
+    rv, rs = O.gather_indexer_k(o.pool, wl.block_table, cu_k, tk)
+    qc, ow, _ = O.quantize_q(synth.bf16_bits_to_f32(qbits), w)
+    ref = O.mqa_logits_chunked(qc, ow, rv, rs, cu_q, cu_k, width)
+    return wl, g, logits, row_len, row_req, ref, cu_q, cu_k
+
+
+def test_chunked_prefill_ragged_batch():
+    """Chunks of 200 (of 700), 130 (the whole request), 1 (of 64) and 5 (of a
+    3-token context: two rows see nothing), scored against the gathered
+    contexts; top-k and slot ids on the result."""
+    ctx, n_q = [700, 130, 64, 3], [200, 130, 1, 5]
+    _say(f"mqa_logits_chunked: contexts {ctx}, chunks {n_q}")
+    wl, g, logits, row_len, row_req, ref, cu_q, cu_k = _chunked_case(ctx, n_q, 768, 41)
+    got = logits.cpu().numpy()
+    assert_logits_close(got, ref, "chunked prefill")
+    want_len = [max(c - n + i + 1, 0) for c, n in zip(ctx, n_q) for i in range(n)]
+    assert row_len.cpu().tolist() == want_len
+    assert row_req.cpu().tolist() == [b for b, n in enumerate(n_q) for _ in range(n)]
+    idx = sai.topk_rows(logits, row_len, 64)
+    assert np.array_equal(idx.cpu().numpy(), O.topk_rows(got, row_len.cpu().numpy(), 64))
+    slots = sai.topk_to_global_slots(idx, row_req, g.block_table)
+    ref_slots = O.topk_to_global_slots(idx.cpu().numpy(), row_req.cpu().numpy(), wl.block_table)
+    assert np.array_equal(slots.cpu().numpy(), ref_slots)
+
+
+def test_chunked_prefill_width_clamp_leaves_rows_untouched():
+    """Rows whose limit exceeds the width are not written (sentinel kept)."""
+    ctx, n_q = [300, 90], [100, 90]
+    _say(f"mqa_logits_chunked: width 256 under contexts {ctx}")
+    _, _, logits, _, _, ref, _, _ = _chunked_case(ctx, n_q, 256, 43, sentinel=12345.0)
+    got = logits.cpu().numpy()
+    untouched = np.isnan(ref).all(axis=1)
+    assert untouched.sum() == 44                     # request 0 rows with limit 257..300
+    assert np.all(got[untouched] == 12345.0)
+    assert_logits_close(got[~untouched], ref[~untouched], "chunked prefill, clamped width")
+
+
+def test_chunked_prefill_matches_paged_decode_next_n():
+    """Bitwise: chunks of 4 at the end of each context == paged decode with
+    next_n = 4 on the same cache (the same arithmetic order in both kernels)."""
+    ctx = [260, 65, 4]
+    _say(f"mqa_logits_chunked vs paged_mqa_logits, next_n 4, contexts {ctx}")
+    wl = synth.custom(3, 4, ctx, num_blocks=12, bt_width=5, seed=44)
+    g = GpuWorkload(wl)
+    ld, _, _ = sai.paged_mqa_logits(g.q_fp8.view(3, 4, 64, 128), g.w_eff, g.pool, g.block_table, g.ctx,
+                                    width=320)
+    cu_k = torch.tensor(np.concatenate([[0], np.cumsum(ctx)]), dtype=torch.int32, device=DEV)
+    cu_q = torch.tensor([0, 4, 8, 12], dtype=torch.int32, device=DEV)
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, cu_k, sum(ctx))
+    lc, _, _ = sai.mqa_logits_chunked(g.q_fp8, g.w_eff, kv, ks, cu_q, cu_k, 320)
+    assert torch.equal(ld, lc)
+
+
 # ---------------------------------------------------------------- graph capture
 def test_decode_pipeline_graph_capture_replays_match_eager():
     _say("hipGraph capture of the decode pipeline")
