@@ -198,13 +198,23 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
     return t, launches, 0, dict(bound="hbm", alg_bytes=alg_bytes, k_bytes=k_bytes, flops=flops)
 
 
+def prefill_limits(wl):
+    """Visible keys of every prefill row: i+1 for a whole request, and
+    n_k - n_q + i + 1 for a chunk of the last n_q of n_k tokens."""
+    n_q = np.diff(wl.cu_q)
+    return np.concatenate([np.maximum(int(c) - int(n) + np.arange(int(n)) + 1, 0)
+                           for c, n in zip(wl.ctx, n_q)]).astype(np.int64)
+
+
 def prefill_pipeline(torch, sai, lib, wl, dev, npools):
-    """Prefill step: gather_indexer_k -> mqa_logits -> topk_rows_slots."""
+    """Prefill step: gather_indexer_k -> mqa_logits (or mqa_logits_chunked for
+    a chunked workload) -> topk_rows_slots."""
     rows, width, total = wl.rows, wl.width, wl.total_tokens
     pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
     bt = torch.from_numpy(wl.block_table).to(dev)
-    cu = torch.from_numpy(wl.cu_seq_lens).to(dev)
-    t = dict(pools=pools, q=q_fp8, w=w_eff, bt=bt, cu=cu,
+    cu = torch.from_numpy(wl.cu_seq_lens).to(dev)      # keys per request
+    cu_q = torch.from_numpy(wl.cu_q).to(dev)           # query rows per request
+    t = dict(pools=pools, q=q_fp8, w=w_eff, bt=bt, cu=cu, cu_q=cu_q,
              k=torch.empty((total, 128), dtype=torch.uint8, device=dev),
              ks=torch.empty((total,), dtype=torch.float32, device=dev),
              logits=torch.empty((rows, width), dtype=torch.float32, device=dev),
@@ -217,20 +227,25 @@ def prefill_pipeline(torch, sai, lib, wl, dev, npools):
     P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
 
     def launches(s):
+        if wl.chunked:
+            logits_call = ("mqa_logits_chunked", lambda i: lib.mqa_logits_chunked(
+                P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu_q), P(cu), wl.batch, rows, total,
+                P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), s))
+        else:
+            logits_call = ("mqa_logits", lambda i: lib.mqa_logits(
+                P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu), wl.batch, total, P(t["logits"]),
+                width, P(t["row_len"]), P(t["row_req"]), s))
         return [
             ("gather_indexer_k", lambda i: lib.gather_indexer_k(
                 P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0), P(cu), wl.batch, total,
                 P(t["k"]), P(t["ks"]), s)),
-            ("mqa_logits", lambda i: lib.mqa_logits(
-                P(q_fp8), P(w_eff), P(t["k"]), P(t["ks"]), P(cu), wl.batch, total, P(t["logits"]),
-                width, P(t["row_len"]), P(t["row_req"]), s)),
+            logits_call,
             ("topk_rows_slots", lambda i: lib.topk_rows_slots(
                 P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), P(bt), bt.stride(0),
                 wl.batch, rows, 2048, P(t["idx"]), P(t["slots"]), P(t["ws"]), ws_bytes, s)),
         ]
-    lim = np.concatenate([np.arange(1, int(c) + 1) for c in wl.ctx]).astype(np.float64)
-    flops = float(lim.sum()) * 64 * 128 * 2
-    alg_bytes = total * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + 132 + width * 4)
+    flops = float(prefill_limits(wl).sum()) * 64 * 128 * 2
+    alg_bytes = total * 132 + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
     return t, launches, 1, dict(bound="mfma", alg_bytes=alg_bytes, k_bytes=total * 132, flops=flops)
 
 
@@ -248,14 +263,15 @@ def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
         O.k_cache_write(synth.bf16_bits_to_f32(wl.k_request(b)), wl.slots_request(b), pool)
     qc, weff, _ = O.quantize_q(synth.bf16_bits_to_f32(wl.q()), wl.w())
     total = wl.total_tokens
-    rows = np.linspace(0, total - 1, nrows).astype(int).tolist()
+    rows = np.linspace(0, wl.rows - 1, nrows).astype(int).tolist()
     kv, ks = O.gather_indexer_k(pool, wl.block_table, wl.cu_seq_lens, total)
-    row_len = np.arange(1, total + 1)
+    row_len = prefill_limits(wl)
+    row_req = np.repeat(np.arange(wl.batch), np.diff(wl.cu_q))
     reps, t0 = 0, time.perf_counter()
     while True:
-        ref = O.mqa_logits(qc, weff, kv, ks, wl.cu_seq_lens, wl.width, rows=rows)
+        ref = O.mqa_logits_chunked(qc, weff, kv, ks, wl.cu_q, wl.cu_seq_lens, wl.width, rows=rows)
         top = O.topk_rows(ref[rows], row_len[rows], 2048)
-        O.topk_to_global_slots(top, np.zeros(len(rows), np.int64), wl.block_table)
+        O.topk_to_global_slots(top, row_req[rows], wl.block_table)
         reps += 1
         el = time.perf_counter() - t0
         if el >= min_seconds:
@@ -267,7 +283,7 @@ def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
     return {
         "value": round(reps * len(rows) / el, 2), "unit": "query-tokens/s", "cores": threads,
         "kind": "oracle",
-        "sample": f"{len(rows)} of {total} prefill rows spread over the request x {reps} passes of "
+        "sample": f"{len(rows)} of {wl.rows} prefill rows spread over the batch x {reps} passes of "
                   f"gather+logits+top-2048+slot ids, {el:.1f} s, numpy/OpenBLAS fp64",
     }, ok
 
@@ -409,7 +425,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1,
                     help="workload preset: 0 tiny decode, 1 decode B=64 (default), 2 MTP decode, "
-                         "3 prefill 8192, 4 long decode")
+                         "3 prefill 8192, 4 long decode, 5 chunked prefill (4 x 2048 of 2K-16K)")
     ap.add_argument("--pools", type=int, default=4, help="cache copies rotated across steps")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--cpu-sample", type=int, default=16, help="requests in the oracle sample")
@@ -609,6 +625,7 @@ def main():
             "heads": 64, "head_dim": 128, "block_size": 64, "topk": 2048,
             "pool_blocks": wl.num_blocks, "pool_copies_rotated": npools,
             "logits_width": width,
+            "chunk_tokens": None if not wl.chunked else [int(x) for x in np.diff(wl.cu_q)],
             "step": [name for name, _ in calls],
         },
         "roofline": roof,

@@ -65,14 +65,27 @@ class Workload:
     width: int                  # logits row width (columns) = bt_width * 64
     topk: int = TOPK
     _ss: list = field(default=None, repr=False)
+    chunk: np.ndarray = None    # prefill only: query tokens per request (the last of its context)
 
     @property
     def prefill(self):
         return self.next_n == 0
 
     @property
+    def chunked(self):
+        return self.prefill and self.chunk is not None
+
+    @property
     def rows(self):
+        if self.chunked:
+            return int(self.chunk.sum())
         return int(self.ctx.sum()) if self.prefill else self.batch * self.next_n
+
+    @property
+    def cu_q(self):
+        """Prefill query rows per request (its chunk, or its whole context)."""
+        n = self.chunk if self.chunked else self.ctx
+        return np.concatenate([[0], np.cumsum(n)]).astype(np.int32)
 
     @property
     def total_tokens(self):
@@ -142,6 +155,8 @@ def make(cfg, seed=None):
        pool ceil(1.25 * blocks needed)
     3  prefill: one request of 8192 tokens, pool 256 blocks
     4  long-context decode: batch 32, next_n 1, contexts 131072, pool 70000
+    5  chunked prefill: 4 requests with contexts 16384, 8192, 6144, 2048, each
+       scoring its last 2048 tokens (8192 query rows), pool 640 blocks
     """
     seed = 1000 + cfg if seed is None else seed
     ss = np.random.SeedSequence(seed)
@@ -175,12 +190,17 @@ def make(cfg, seed=None):
         name, batch, next_n = "long_decode_b32_ctx128k", 32, 1
         ctx = np.full(batch, 131072, dtype=np.int32)
         num_blocks, bt_width = 70000, 2048
+    elif cfg == 5:
+        name, batch, next_n = "chunked_prefill_b4_chunk2048", 4, 0
+        ctx = np.array([16384, 8192, 6144, 2048], dtype=np.int32)
+        num_blocks, bt_width = 640, 256
     else:
         raise ValueError(f"unknown workload {cfg}")
     bt = _assign_blocks(meta, ctx, num_blocks, bt_width)
+    chunk = np.full(batch, 2048, dtype=np.int32) if cfg == 5 else None
     return Workload(name=name, seed=seed, batch=batch, next_n=next_n, ctx=ctx,
                     num_blocks=num_blocks, block_table=bt, width=bt_width * BLOCK,
-                    _ss=ss.spawn(2 + batch))
+                    _ss=ss.spawn(2 + batch), chunk=chunk)
 
 
 def custom(batch, next_n, ctx, num_blocks, bt_width, seed, name="custom"):

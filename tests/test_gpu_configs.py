@@ -90,3 +90,36 @@ def test_config3_prefill_8192():
     assert np.array_equal(idx.cpu().numpy(), want)
     assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, row_req.cpu().numpy(),
                                                                      wl.block_table))
+
+
+def test_config5_chunked_prefill():
+    """Four prompts at contexts 16384 / 8192 / 6144 / 2048, each scoring its
+    last 2048 tokens against the gathered context (the bench's chunked-prefill
+    workload at full size): logits on sampled rows, row limits on every row,
+    top-k and slot ids on sampled rows."""
+    wl = synth.make(5)
+    _say("config 5 (chunked prefill): building on GPU")
+    g = GpuWorkload(wl)
+    total_k = wl.total_tokens
+    cu_q = torch.from_numpy(wl.cu_q).to(DEV)
+    kv, ks = sai.gather_indexer_k(g.pool, g.block_table, g.cu, total_k)
+    logits, row_len, row_req = sai.mqa_logits_chunked(g.q_fp8, g.w_eff, kv, ks, cu_q, g.cu, wl.width)
+    idx = sai.topk_rows(logits, row_len, 2048)
+    slots = sai.topk_to_global_slots(idx, row_req, g.block_table)
+    torch.cuda.synchronize()
+    o = OracleWorkload(wl)
+    rv, rs = O.gather_indexer_k(o.pool, wl.block_table, wl.cu_seq_lens, total_k)
+    assert np.array_equal(kv.cpu().numpy(), rv)
+    rows = [0, 1, 2047, 2048, 2049, 4095, 4096, 5000, 6143, 6144, 6145, 8190, 8191]
+    ref = O.mqa_logits_chunked(o.q_codes, o.w_eff, rv, rs, wl.cu_q, wl.cu_seq_lens, wl.width, rows=rows)
+    gl = logits.cpu().numpy()
+    worst = assert_logits_close(gl[rows], ref[rows], wl.name)
+    _say(f"config 5: logits ok on {len(rows)} rows, worst err/tol {worst:.3g}")
+    n_q = np.diff(wl.cu_q)
+    want_len = np.concatenate([int(c) - int(n) + np.arange(int(n)) + 1 for c, n in zip(wl.ctx, n_q)])
+    assert np.array_equal(row_len.cpu().numpy(), want_len)
+    assert np.array_equal(row_req.cpu().numpy(), np.repeat(np.arange(wl.batch), n_q))
+    want = O.topk_rows(gl[rows], want_len[rows], 2048)
+    assert np.array_equal(idx.cpu().numpy()[rows], want)
+    assert np.array_equal(slots.cpu().numpy()[rows],
+                          O.topk_to_global_slots(want, row_req.cpu().numpy()[rows], wl.block_table))
