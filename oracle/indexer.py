@@ -222,7 +222,7 @@ def _score(q_codes_row, w_row, k_codes, k_scale):
 
 
 def paged_mqa_logits(q_codes, w, cache, block_table, context_lens, next_n, width,
-                     rows=None):
+                     rows=None, clean=True):
     """FP8 paged MQA logits with the causal -inf mask (clean logits).
 
     vLLM PR #36250 (Purpose): ``fp8_paged_mqa_logits`` scores every query
@@ -236,7 +236,9 @@ def paged_mqa_logits(q_codes, w, cache, block_table, context_lens, next_n, width
     q_codes: uint8 [B, next_n, H, D]; w: float32 [B*next_n, H];
     cache: uint8 [num_blocks, BLOCK_BYTES]; block_table: int [B, max_blocks];
     context_lens: int [B].  ``rows`` optionally restricts the computation to
-    a subset of row ids (other rows are left NaN).
+    a subset of row ids (other rows are left NaN).  ``clean=False`` is the
+    review's non-clean variant: columns from the end of the request's last
+    key block on are not written (NaN here, untouched on the GPU).
     Returns float64 [B*next_n, width].
     """
     ctx = np.asarray(context_lens).tolist()
@@ -260,6 +262,8 @@ def paged_mqa_logits(q_codes, w, cache, block_table, context_lens, next_n, width
             row = np.full(width, -np.inf, dtype=np.float64)
             if lim > 0:
                 row[:lim] = _score(q_codes[b, j], w[r], kc[:lim], ks[:lim])
+            if not clean:
+                row[nblk * BLOCK:] = np.nan
             out[r] = row
     return out
 

@@ -409,6 +409,23 @@ def test_chunked_prefill_short_context_and_width_clamp():
     assert np.all(np.isnan(L[5]))
 
 
+def test_non_clean_logits_differ_only_past_the_last_block_and_keep_the_top_k():
+    """The non-clean variant equals clean logits on every request's key
+    blocks and leaves the rest unwritten; the top-k, which reads a row only
+    up to its limit, is the same on both."""
+    ctx = [1, 64, 65, 130]
+    wl, pool, qc, weff = _small_workload(ctx, 2, 4, 12, seed=18)
+    clean = O.paged_mqa_logits(qc, weff, pool, wl.block_table, wl.ctx, 2, 256)
+    vis = O.paged_mqa_logits(qc, weff, pool, wl.block_table, wl.ctx, 2, 256, clean=False)
+    lim, _ = O.decode_limits(wl.ctx, 2)
+    for b, c in enumerate(ctx):
+        end = -(-c // 64) * 64
+        rows = slice(2 * b, 2 * b + 2)
+        assert np.array_equal(vis[rows, :end], clean[rows, :end])
+        assert np.all(np.isnan(vis[rows, end:])) and np.all(np.isneginf(clean[rows, end:]))
+    assert np.array_equal(O.topk_rows(vis, lim, 16), O.topk_rows(clean, lim, 16))
+
+
 def test_exact_power_of_two_scaling():
     """P7: scaling w or every k_scale by 2^m scales the logits by exactly 2^m."""
     wl, pool, qc, weff = _small_workload([150, 33], 2, 3, 8, seed=15)
