@@ -165,8 +165,9 @@ def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
     }, ok
 
 
-def decode_pipeline(torch, sai, lib, wl, dev, npools):
-    """Decode step: paged_mqa_logits -> topk_rows_slots."""
+def decode_pipeline(torch, sai, lib, wl, dev, npools, visible=False):
+    """Decode step: paged_mqa_logits -> topk_rows_slots (with visible=True,
+    paged_mqa_logits_visible: no -inf fill past each request's key blocks)."""
     nn, rows, width = wl.next_n, wl.rows, wl.width
     pools, q_fp8, w_eff = build_inputs(torch, sai, wl, dev, npools)
     bt = torch.from_numpy(wl.block_table).to(dev)
@@ -183,7 +184,8 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
 
     def launches(s):
         return [
-            ("paged_mqa_logits", lambda i: lib.paged_mqa_logits(
+            ("paged_mqa_logits_visible" if visible else "paged_mqa_logits",
+             lambda i: (lib.paged_mqa_logits_visible if visible else lib.paged_mqa_logits)(
                 P(q_fp8), P(w_eff), P(pools[i % len(pools)]), pools[0].shape[0], P(bt), bt.stride(0),
                 P(ctx), wl.batch, nn, P(t["logits"]), width, P(t["row_len"]), P(t["row_req"]), s)),
             ("topk_rows_slots", lambda i: lib.topk_rows_slots(
@@ -192,7 +194,10 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools):
         ]
     ctx_np = wl.ctx.astype(np.int64)
     k_bytes = int(ctx_np.sum()) * K_BYTES_PER_TOKEN
-    alg_bytes = k_bytes + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
+    # logits written: the full row width, or (visible) the request's key blocks only
+    written = (np.repeat(np.minimum((ctx_np + 63) // 64 * 64, width), nn) if visible
+               else np.full(rows, width, np.int64))
+    alg_bytes = k_bytes + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW) + int(written.sum()) * 4
     lim = np.repeat(ctx_np, nn) - nn + np.tile(np.arange(nn), wl.batch) + 1
     flops = float(np.clip(lim, 0, None).sum()) * 64 * 128 * 2
     return t, launches, 0, dict(bound="hbm", alg_bytes=alg_bytes, k_bytes=k_bytes, flops=flops)
@@ -436,6 +441,9 @@ def main():
                          "timed step (arming adds ~1 us to a step)")
     ap.add_argument("--no-refs", action="store_true",
                     help="skip the 1 GiB copy and hot-cache reference timings")
+    ap.add_argument("--visible-logits", action="store_true",
+                    help="decode: write logits only over each request's key blocks "
+                         "(paged_mqa_logits_visible; same top-k and slot ids)")
     ap.add_argument("--no-mla", action="store_true",
                     help="skip the sparse MLA decode leg over this step's slot ids")
     ap.add_argument("--mla-steps", type=int, default=50)
@@ -461,7 +469,10 @@ def main():
     prefill = wl.prefill
     npools = 1 if prefill or args.config == 4 else args.pools
     make = prefill_pipeline if prefill else decode_pipeline
-    t, launches, dom, work = make(torch, sai, lib, wl, dev, npools)
+    if prefill:
+        t, launches, dom, work = make(torch, sai, lib, wl, dev, npools)
+    else:
+        t, launches, dom, work = make(torch, sai, lib, wl, dev, npools, visible=args.visible_logits)
     rows, width = wl.rows, wl.width
     torch.cuda.synchronize()
 
@@ -581,7 +592,7 @@ def main():
         achieved = work["alg_bytes"] / t_dom_s / 1e9
         roof = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBPS, 4),
-                "traffic": counter_traffic() if args.config == 1 else None}
+                "traffic": counter_traffic() if args.config == 1 and not args.visible_logits else None}
     else:
         achieved = work["flops"] / t_dom_s / 1e12
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,

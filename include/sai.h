@@ -164,6 +164,22 @@ int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cac
                      int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
 
 /*
+ * paged_mqa_logits_visible -- paged_mqa_logits without the -inf fill: the
+ * non-clean variant the review of vLLM PR #36250 sets beside "clean
+ * logits", for a consumer that reads each row only up to its limit (the
+ * top-k calls below do).  Columns of request b's key blocks,
+ * [0, min(64*ceil(ctx_b/64), logits_stride)), are written exactly as
+ * paged_mqa_logits writes them (-inf from the limit to the end of the last
+ * block); later columns are left untouched.  Arguments and errors as for
+ * paged_mqa_logits.
+ */
+int paged_mqa_logits_visible(const void* q_fp8, const float* weights, const void* kv_cache,
+                             int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                             const int32_t* context_lens, int32_t batch, int32_t next_n,
+                             float* logits, int64_t logits_stride,
+                             int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream);
+
+/*
  * mqa_logits -- prefill logits against contiguous K (the output of
  * gather_indexer_k).  Not one of the calls the pages name: the prefill path
  * scores gathered K (vLLM PR #25869, review of cp_gather_indexer_k_quant_cache;

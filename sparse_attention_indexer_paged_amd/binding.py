@@ -35,6 +35,8 @@ SIGNATURES = {
                          _c_void_p, _c_void_p],
     "paged_mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32,
                          _i32, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p],
+    "paged_mqa_logits_visible": [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32,
+                                 _i32, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p],
     "mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32, _i64, _c_void_p,
                    _i64, _c_void_p, _c_void_p, _c_void_p],
     "mqa_logits_chunked": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _c_void_p, _i32,
@@ -242,10 +244,12 @@ def gather_indexer_k(kv_cache, block_table, cu_seq_lens, total_tokens, out_k=Non
 
 
 def paged_mqa_logits(q_fp8, weights, kv_cache, block_table, context_lens, width=None,
-                     logits=None, row_len=None, row_req=None):
+                     logits=None, row_len=None, row_req=None, clean=True):
     """Decode logits.  q_fp8 u8 [B, next_n, 64, 128]; weights f32 [B*next_n, 64];
     block_table i32 [B, bt_width]; context_lens i32 [B].  Row width defaults to
-    bt_width*64.  Returns (logits f32 [B*next_n, width], row_len i32, row_req i32)."""
+    bt_width*64.  Returns (logits f32 [B*next_n, width], row_len i32, row_req i32).
+    clean=False calls paged_mqa_logits_visible (columns past each request's
+    last key block are left as they were)."""
     _need(q_fp8, torch.uint8, "q_fp8", 4)
     _need(weights, torch.float32, "weights", 2)
     _need(kv_cache, torch.uint8, "kv_cache", 2)
@@ -265,10 +269,11 @@ def paged_mqa_logits(q_fp8, weights, kv_cache, block_table, context_lens, width=
     _out(logits, torch.float32, "logits", (rows, width))
     _out(row_len, torch.int32, "row_len", (rows,))
     _out(row_req, torch.int32, "row_req", (rows,))
-    _check(load().paged_mqa_logits(_ptr(q_fp8), _ptr(weights), _ptr(kv_cache), kv_cache.shape[0],
-                                   _ptr(block_table), block_table.stride(0), _ptr(context_lens),
-                                   B, next_n, _ptr(logits), logits.stride(0), _ptr(row_len),
-                                   _ptr(row_req), _stream()), "paged_mqa_logits")
+    name = "paged_mqa_logits" if clean else "paged_mqa_logits_visible"
+    _check(getattr(load(), name)(_ptr(q_fp8), _ptr(weights), _ptr(kv_cache), kv_cache.shape[0],
+                                 _ptr(block_table), block_table.stride(0), _ptr(context_lens),
+                                 B, next_n, _ptr(logits), logits.stride(0), _ptr(row_len),
+                                 _ptr(row_req), _stream()), name)
     return logits, row_len, row_req
 
 
@@ -392,9 +397,12 @@ def topk_rows_slots(logits, row_len, row_req, block_table, k=TOPK_MAX, out=None,
     return out, slots
 
 
-def decode_indexer(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None):
-    """The decode hot path: logits -> top-k -> global slot ids, one stream, no host sync."""
+def decode_indexer(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None,
+                   clean=True):
+    """The decode hot path: logits -> top-k -> global slot ids, one stream, no
+    host sync.  clean=False skips the -inf fill past each request's key blocks
+    (the top-k reads a row only up to its limit; same indices and slot ids)."""
     logits, row_len, row_req = paged_mqa_logits(q_fp8, weights, kv_cache, block_table,
-                                                context_lens, width)
+                                                context_lens, width, clean=clean)
     idx, slots = topk_rows_slots(logits, row_len, row_req, block_table, k)
     return logits, idx, slots

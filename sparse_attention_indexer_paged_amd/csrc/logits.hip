@@ -253,7 +253,8 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ bt, int64_t bt_stride,
     const int32_t* __restrict__ ctx_lens, int32_t batch, float* __restrict__ logits,
-    int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out, bool vec) {
+    int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out, bool vec,
+    bool clean) {
   constexpr int kSlots = kStageFloats / (kBlock * NN);  // staged units per wave
   constexpr int kCap = CAP < kSlots ? CAP : kSlots;      // a group fits the stage
   static_assert(kCap >= 1, "stage too small");
@@ -275,7 +276,8 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       const int c = min(max(ctx_lens[bb], 0), maxc);
       s_ctx[bb] = c;
       nu = cdiv_i(c, kBlock);
-      nf = (int)((max(stride - (int64_t)nu * kBlock, (int64_t)0) + kFillCols - 1) / kFillCols);
+      // no fill pieces when only the request's own blocks are to be written
+      nf = clean ? (int)((max(stride - (int64_t)nu * kBlock, (int64_t)0) + kFillCols - 1) / kFillCols) : 0;
     }
     const int iu = wave_inclusive_scan(nu), jf = wave_inclusive_scan(nf);
     if (lane == 63) {
@@ -745,7 +747,7 @@ __global__ __launch_bounds__(kPfThreads) SAI_PF_ATTR void prefill_logits_kernel(
 template <int NN>
 int launch_paged(const void* q, const float* w, const void* cache, int64_t num_blocks,
                  const int32_t* bt, int64_t bt_stride, const int32_t* ctx, int32_t batch,
-                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, hipStream_t s) {
+                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, bool clean, hipStream_t s) {
   if (batch > 4096) return SAI_EUNSUPPORTED;  // LDS prefix arrays
   const int64_t wblocks = (stride + kBlock - 1) / kBlock;
   const int64_t units_max = (int64_t)batch * wblocks;
@@ -763,17 +765,17 @@ int launch_paged(const void* q, const float* w, const void* cache, int64_t num_b
   const bool vec = stride % 4 == 0 && aligned16(logits);
   launch((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap>), dim3((unsigned)G),
                      dim3(256), lds, s, (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt,
-                     bt_stride, ctx, batch, logits, stride, rl, rr, vec);
+                     bt_stride, ctx, batch, logits, stride, rl, rr, vec, clean);
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
 
 }  // namespace
 
-extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
-                                int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
-                                const int32_t* context_lens, int32_t batch, int32_t next_n,
-                                float* logits, int64_t logits_stride, int32_t* row_len_out,
-                                int32_t* row_req_out, hipStream_t stream) {
+namespace {
+int paged_entry(const void* q_fp8, const float* weights, const void* kv_cache, int64_t num_blocks,
+                const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                int32_t batch, int32_t next_n, float* logits, int64_t logits_stride,
+                int32_t* row_len_out, int32_t* row_req_out, bool clean, hipStream_t stream) {
   if (batch < 0 || num_blocks < 0 || bt_stride < 0 || logits_stride < 0) return SAI_EINVAL;
   if (next_n < 1 || next_n > SAI_NEXT_N_MAX) return SAI_EUNSUPPORTED;
   if (batch == 0) return SAI_OK;
@@ -784,11 +786,30 @@ extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const v
   if ((int64_t)batch * wblocks > 0x7FFFFFFF / 2 || logits_stride > 0x7FFFFFFF - kBlock)
     return SAI_EUNSUPPORTED;
   switch (next_n) {
-    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
-    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
-    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
-    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, stream);
+    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
+    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
+    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
+    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
   }
+}
+}  // namespace
+
+extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
+                                int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                                const int32_t* context_lens, int32_t batch, int32_t next_n,
+                                float* logits, int64_t logits_stride, int32_t* row_len_out,
+                                int32_t* row_req_out, hipStream_t stream) {
+  return paged_entry(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
+                     next_n, logits, logits_stride, row_len_out, row_req_out, true, stream);
+}
+
+extern "C" int paged_mqa_logits_visible(const void* q_fp8, const float* weights, const void* kv_cache,
+                                        int64_t num_blocks, const int32_t* block_table,
+                                        int64_t bt_stride, const int32_t* context_lens, int32_t batch,
+                                        int32_t next_n, float* logits, int64_t logits_stride,
+                                        int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
+  return paged_entry(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
+                     next_n, logits, logits_stride, row_len_out, row_req_out, false, stream);
 }
 
 namespace {

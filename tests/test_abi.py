@@ -33,7 +33,7 @@ def test_header_declares_the_boundary():
     assert names == sorted([
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
         "gather_indexer_k",
-        "paged_mqa_logits", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
+        "paged_mqa_logits", "paged_mqa_logits_visible", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
         "topk_to_global_slots", "topk_rows_slots", "mla_cache_write", "sparse_mla_workspace_bytes",
         "sparse_mla_decode"])
 

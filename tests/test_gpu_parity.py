@@ -438,6 +438,32 @@ def test_chunked_prefill_matches_paged_decode_next_n():
     assert torch.equal(ld, lc)
 
 
+@pytest.mark.parametrize("next_n", [1, 2])
+def test_visible_logits_write_only_the_key_blocks(next_n):
+    """paged_mqa_logits_visible: the request's key blocks exactly as the
+    clean call writes them, everything after them untouched (sentinel), and
+    the same top-k and slot ids downstream."""
+    ctx = [1, 64, 65, 300, 2049]
+    _say(f"paged_mqa_logits_visible: contexts {ctx}, next_n={next_n}")
+    wl = synth.custom(len(ctx), next_n, ctx, num_blocks=60, bt_width=40, seed=51 + next_n)
+    g = GpuWorkload(wl)
+    q = g.q_fp8.view(len(ctx), next_n, 64, 128)
+    lc, rl, rr = sai.paged_mqa_logits(q, g.w_eff, g.pool, g.block_table, g.ctx)
+    sentinel = torch.full_like(lc, 777.0)
+    lv, rlv, rrv = sai.paged_mqa_logits(q, g.w_eff, g.pool, g.block_table, g.ctx, logits=sentinel, clean=False)
+    torch.cuda.synchronize()
+    c, v = lc.cpu().numpy(), lv.cpu().numpy()
+    for b, cb in enumerate(ctx):
+        end = -(-cb // 64) * 64
+        rows = slice(next_n * b, next_n * (b + 1))
+        assert np.array_equal(v[rows, :end].view(np.uint32), c[rows, :end].view(np.uint32))
+        assert np.all(v[rows, end:] == 777.0)
+    assert torch.equal(rl, rlv) and torch.equal(rr, rrv)
+    ic = sai.topk_rows(lc, rl, 2048)
+    iv = sai.topk_rows(lv, rlv, 2048)
+    assert torch.equal(ic, iv)
+
+
 # ---------------------------------------------------------------- graph capture
 def test_decode_pipeline_graph_capture_replays_match_eager():
     _say("hipGraph capture of the decode pipeline")
