@@ -684,11 +684,15 @@ struct Shape {
   int nt, vpt;  // nt == 0: no register-resident shape holds the work
 };
 
-Shape shape_for(int64_t n, int64_t wgs) {
+// max_vpt: one-pass launches of many rows stop at 16 positions per thread
+// (then 1024 threads): 32-position shapes were slower there (16384-column
+// rows: 404 -> 286 us, 8192-column rows: 150 -> 140 us); segment passes keep
+// 32 (the 4-segment MTP pass: 50.6 us with 512 x 32, 56.1 with 1024 x 16).
+Shape shape_for(int64_t n, int64_t wgs, int max_vpt = 32) {
   if (wgs >= kManyWgs) {
     for (int nt : {256, 512})
       for (int vpt : {4, 8, 16, 32})
-        if (n <= (int64_t)nt * vpt) return {nt, vpt};
+        if (vpt <= max_vpt && n <= (int64_t)nt * vpt) return {nt, vpt};
   }
   for (int vpt : {4, 8, 16})
     if (n <= 1024LL * vpt) return {1024, vpt};
@@ -704,7 +708,7 @@ struct TopkPlan {
 };
 
 TopkPlan plan_for(int64_t stride, int k, int64_t rows) {
-  if (stride <= kSegCols) return {shape_for(stride, rows), 0, {0, 0}, {0, 0}, false};
+  if (stride <= kSegCols) return {shape_for(stride, rows, 16), 0, {0, 0}, {0, 0}, false};
   const int64_t nseg = (stride + kSegCols - 1) / kSegCols;
   const Shape merge = shape_for(nseg * k, rows);
   if (merge.nt == 0) return {{0, 0}, 0, {0, 0}, {0, 0}, true};
