@@ -210,3 +210,34 @@ def test_sparse_mla_decode_full_size_sampled():
     slots[5, 1000:] = -1
     qn, qp = _mla_query(T, H, 6)
     _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0), rows=np.array([0, 5, 31, 63]))
+
+
+def test_sparse_mla_decode_cache_past_4_gib():
+    """A 4.3 GB MLA cache (105 000 blocks of 64 entries): the selected slots
+    sit past byte 2^32.  The oracle runs on a compact copy of those entries."""
+    nb, bs, T, H, K = 105_000, 64, 2, 64, 300
+    _say(f"sparse_mla_decode with a {nb}-block cache (entries past 4 GiB)")
+    rng = np.random.default_rng(71)
+    lo = (2 ** 32) // 656 + 1
+    ids = rng.choice(np.arange(lo, nb * bs), (T, K), replace=False).astype(np.int32)
+    ids[1, ::5] = -1
+    flat = np.unique(ids[ids >= 0])
+    small = _mla_cache(-(-len(flat) // bs), bs, 72)          # oracle-written entries
+    ent = small.reshape(-1, 656)[:len(flat)]
+    cache = torch.zeros((nb, bs, 656), dtype=torch.uint8, device=DEV)
+    cflat = cache.view(-1, 656)
+    cflat[torch.from_numpy(flat.astype(np.int64)).to(DEV)] = torch.from_numpy(ent).to(DEV)
+    qn, qp = _mla_query(T, H, 73)
+    out, lse = sai.sparse_mla_decode(bf16_tensor(qn), bf16_tensor(qp), cache, torch.from_numpy(ids).to(DEV),
+                                     1.0 / np.sqrt(576.0))
+    torch.cuda.synchronize()
+    remap = np.full(ids.shape, -1, np.int32)
+    remap[ids >= 0] = np.searchsorted(flat, ids[ids >= 0])
+    host = ent.reshape(len(flat), 1, 656)
+    ref, ref_lse, ref_abs = O.mla.sparse_mla_decode(synth.bf16_bits_to_f32(qn), synth.bf16_bits_to_f32(qp),
+                                                    host, remap, 1.0 / np.sqrt(576.0), with_abs=True)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= _mla_tol(ref_abs))
+    assert np.all(np.abs(lse.cpu().numpy() - ref_lse) <= LSE_ATOL + LSE_RTOL * np.abs(ref_lse))
+    del cache, cflat
+    torch.cuda.empty_cache()

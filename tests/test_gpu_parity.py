@@ -525,3 +525,43 @@ def test_slots_wide_table_elementwise_path():
         ok = (idx[r] >= 0) & (blk >= 0)
         want[r, ok] = blk[ok] * 64 + idx[r][ok] % 64
     assert np.array_equal(got, want)
+
+
+# ---------------------------------------------------------------- past 4 GiB
+def test_paged_pipeline_cache_past_4_gib():
+    """A 520 000-block pool (4.39 GB): the requests' blocks sit past byte
+    2^32, so every cache address needs 64-bit arithmetic.  Logits, top-k and
+    slot ids against the oracle on a compact copy of the used blocks."""
+    nb_big = 520_000
+    ctx = [300, 1000, 65]
+    _say(f"paged pipeline with a {nb_big}-block pool (blocks past 4 GiB), contexts {ctx}")
+    wl = synth.custom(len(ctx), 2, ctx, num_blocks=40, bt_width=16, seed=61)
+    used = np.unique(wl.block_table[wl.block_table >= 0])
+    # big ids: the last len(used) blocks of the big pool (offsets > 2^32)
+    big_of = {int(b): nb_big - len(used) + i for i, b in enumerate(used)}
+    assert min(big_of.values()) * synth.BLOCK_BYTES > 2 ** 32
+    bt_big = np.where(wl.block_table >= 0, np.vectorize(lambda b: big_of.get(int(b), -1))(wl.block_table), -1)
+    bt_big = bt_big.astype(np.int32)
+    pool = torch.empty((nb_big, synth.BLOCK_BYTES), dtype=torch.uint8, device=DEV)
+    pool[nb_big - len(used):] = torch.from_numpy(np.tile(synth.poison_block(), (len(used), 1))).to(DEV)
+    for b in range(wl.batch):
+        c = int(wl.ctx[b])
+        nblk = -(-c // 64)
+        slots = (bt_big[b, :nblk].astype(np.int64)[:, None] * 64 + np.arange(64)[None, :]).reshape(-1)[:c]
+        sai.indexer_k_cache_write(bf16_tensor(wl.k_request(b)), torch.from_numpy(slots).to(DEV), pool)
+    q_fp8, w_eff, _ = sai.indexer_q_quant(bf16_tensor(wl.q()), torch.from_numpy(wl.w()).to(DEV))
+    btg = torch.from_numpy(bt_big).to(DEV)
+    ctxg = torch.from_numpy(wl.ctx).to(DEV)
+    logits, row_len, row_req = sai.paged_mqa_logits(q_fp8.view(3, 2, 64, 128), w_eff, pool, btg, ctxg)
+    idx, slots = sai.topk_rows_slots(logits, row_len, row_req, btg, 256)
+    torch.cuda.synchronize()
+    o = OracleWorkload(wl)  # the same tokens in the small pool under the original block ids
+    ref = O.paged_mqa_logits(o.q_codes.reshape(3, 2, 64, 128), o.w_eff, o.pool, wl.block_table, wl.ctx, 2,
+                             wl.width)
+    got = logits.cpu().numpy()
+    assert_logits_close(got, ref, "pool past 4 GiB")
+    want = O.topk_rows(got, row_len.cpu().numpy(), 256)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, row_req.cpu().numpy(), bt_big))
+    del pool
+    torch.cuda.empty_cache()
