@@ -199,6 +199,48 @@ def test_sparse_mla_decode_poisoned_entry_zero(H):
     _check_decode(qn, qp, cache_np, slots, 1.0 / np.sqrt(576.0))
 
 
+@pytest.mark.parametrize("T,H", [(2, 64), (256, 64), (3, 16)])
+def test_sparse_mla_decode_graph_capture_replays_match_eager(T, H):
+    """Captured in a HIP graph (split + combine, one pass, 16-head kernel),
+    replayed three times with eager calls in between: every replay equals
+    the eager result bit for bit."""
+    _say(f"sparse_mla_decode: graph capture, T {T} H {H}")
+    K, bs, nb = 300, 64, 12
+    cache = torch.from_numpy(_mla_cache(nb, bs, 81)).to(DEV)
+    rng = np.random.default_rng(82)
+    slots = torch.from_numpy(np.stack([rng.choice(nb * bs, K, replace=False) for _ in range(T)]).astype(np.int32)).to(DEV)
+    slots[0, ::4] = -1
+    qn, qp = _mla_query(T, H, 83)
+    qn, qp = bf16_tensor(qn), bf16_tensor(qp)
+    ws_bytes = sai.sparse_mla_workspace_bytes(T, H, K)
+    ws = torch.empty((max(ws_bytes, 16),), dtype=torch.uint8, device=DEV)
+    out = torch.empty((T, H, 512), dtype=torch.float32, device=DEV)
+    lse = torch.empty((T, H), dtype=torch.float32, device=DEV)
+    scale = 1.0 / np.sqrt(576.0)
+    eo, el = sai.sparse_mla_decode(qn, qp, cache, slots, scale, workspace=ws)
+    eo, el = eo.clone(), el.clone()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        sai.sparse_mla_decode(qn, qp, cache, slots, scale, out=out, lse=lse, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        sai.sparse_mla_decode(qn, qp, cache, slots, scale, out=out, lse=lse, workspace=ws)
+    for rep in range(3):
+        out.fill_(-7.0)
+        lse.fill_(-7.0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eo) and torch.equal(lse, el), f"replay {rep} differs"
+        o2, l2 = sai.sparse_mla_decode(qn, qp, cache, slots, scale, workspace=ws)
+        torch.cuda.synchronize()
+        assert torch.equal(o2, eo) and torch.equal(l2, el)
+
+
 def test_sparse_mla_decode_full_size_sampled():
     """The decode workload's shape (64 rows, 128 heads, top-2048 over a
     640-block cache), one pass on the GPU, four rows checked."""
