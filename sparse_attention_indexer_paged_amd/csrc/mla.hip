@@ -92,8 +92,12 @@ extern "C" int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const
 //   out[t,h] = sum_j softmax(s)_j kv_j,  lse[t,h] = log sum_j exp(s_j),
 // kv_j the dequantised latent (code * tile scale), kpe_j the stored RoPE part.
 //
-// Workgroup = one query row x 16 heads x one split of the slot list, 4 waves.
-// Slots go through in chunks of 32: the chunk's entries are gathered one
+// Two kernels share the staging below: the 64-head (wide) kernel, described
+// at its definition, for head counts in groups of 64, and the 16-head
+// (narrow) kernel described here for the rest.
+//
+// Narrow: workgroup = one query row x 16 heads x one split of the slot list,
+// 4 waves.  Slots go through in chunks of 32: the chunk's entries are gathered one
 // chunk ahead into registers, then written to LDS twice -- codes
 // token-major (the B operand of Q.K^T: 8 consecutive dims of one token per
 // lane) and dim-major (the B operand of P.V: 8 consecutive tokens of one dim
