@@ -8,7 +8,7 @@ import oracle as O
 from sparse_attention_indexer_paged_amd import binding as sai
 from sparse_attention_indexer_paged_amd import synth
 
-from gpu_common import DEV, bf16_tensor
+from gpu_common import DEV, GpuWorkload, bf16_tensor
 
 pytestmark = pytest.mark.gpu
 
@@ -283,3 +283,32 @@ def test_sparse_mla_decode_cache_past_4_gib():
     assert np.all(np.abs(lse.cpu().numpy() - ref_lse) <= LSE_ATOL + LSE_RTOL * np.abs(ref_lse))
     del cache, cflat
     torch.cuda.empty_cache()
+
+
+def test_indexer_then_sparse_mla_decode_end_to_end():
+    """The whole decode chain: indexer logits -> top-k -> global slot ids ->
+    sparse MLA decode over those ids, on one stream; the oracle runs the
+    same chain (its top-k on the GPU's logits, as everywhere the selection is
+    decided in the kernel's fp32), and the attention output is compared."""
+    ctx, nn, H = [3000, 700, 64, 2049], 2, 64
+    _say(f"indexer -> sparse MLA decode: contexts {ctx}, next_n {nn}, {H} heads")
+    wl = synth.custom(len(ctx), nn, ctx, num_blocks=120, bt_width=60, seed=91)
+    g = GpuWorkload(wl)
+    logits, idx, slots = sai.decode_indexer(g.q_fp8.view(len(ctx), nn, 64, 128), g.w_eff, g.pool,
+                                            g.block_table, g.ctx, k=512)
+    mla_np = _mla_cache(wl.num_blocks, 64, 92)
+    mla = torch.from_numpy(mla_np).to(DEV)
+    qn, qp = _mla_query(wl.rows, H, 93)
+    out, lse = sai.sparse_mla_decode(bf16_tensor(qn), bf16_tensor(qp), mla, slots, 1.0 / np.sqrt(576.0))
+    torch.cuda.synchronize()
+    lim, req = O.decode_limits(wl.ctx, nn)
+    want_idx = O.topk_rows(logits.cpu().numpy(), lim, 512)
+    want_slots = O.topk_to_global_slots(want_idx, req, wl.block_table)
+    assert np.array_equal(idx.cpu().numpy(), want_idx)
+    assert np.array_equal(slots.cpu().numpy(), want_slots)
+    ref, ref_lse, ref_abs = O.mla.sparse_mla_decode(synth.bf16_bits_to_f32(qn), synth.bf16_bits_to_f32(qp),
+                                                    mla_np, want_slots, 1.0 / np.sqrt(576.0), with_abs=True)
+    got = out.cpu().numpy().astype(np.float64)
+    assert np.all(np.abs(got - ref) <= _mla_tol(ref_abs))
+    fin = np.isfinite(ref_lse)
+    assert np.all(np.abs(lse.cpu().numpy()[fin] - ref_lse[fin]) <= LSE_ATOL + LSE_RTOL * np.abs(ref_lse[fin]))
