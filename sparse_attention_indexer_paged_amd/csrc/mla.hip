@@ -116,7 +116,7 @@ typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
 constexpr int kMlaHg = 16;     // heads per workgroup (narrow kernel) and per wave (wide)
 constexpr int kMlaWideHeads = 64;  // heads per workgroup of the wide kernel
 constexpr int kMlaChunk = 32;  // slots per chunk
-constexpr int kMlaKmPitch = kMlaKv + 16;  // token-major LDS row pitch (bytes)
+constexpr int kMlaKmPitch = kMlaKv + 8;   // token-major LDS row pitch (bytes): 130 words, so 16 rows' 8-byte operand reads cover the 32 banks once
 constexpr int kMlaVtPitch = kMlaKv + 16;  // dim-major slab pitch (words)
 constexpr int kMlaPePitch = kMlaRope + 8;  // RoPE LDS row pitch (bf16 values)
 
@@ -244,7 +244,9 @@ __device__ __forceinline__ void mla_stage_to_lds(MlaChunkLds& sm, const MlaStage
   for (int i = 0; i < 4; ++i) {
     const bool v = (st.vmask >> (4 * tg + i)) & 1u;
     c[i] = v ? st.c[i] : make_uint4(0u, 0u, 0u, 0u);
-    *reinterpret_cast<uint4*>(&sm.km[4 * tg + i][16 * dp]) = c[i];
+    // two 8-byte stores: rows are 8-byte (not 16-byte) aligned
+    *reinterpret_cast<uint2*>(&sm.km[4 * tg + i][16 * dp]) = make_uint2(c[i].x, c[i].y);
+    *reinterpret_cast<uint2*>(&sm.km[4 * tg + i][16 * dp + 8]) = make_uint2(c[i].z, c[i].w);
   }
   const uint32_t w[4][4] = {{c[0].x, c[0].y, c[0].z, c[0].w},
                             {c[1].x, c[1].y, c[1].z, c[1].w},
