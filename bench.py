@@ -49,6 +49,7 @@ K_BYTES_PER_TOKEN = 132          # 128 fp8 codes + one fp32 scale
 Q_BYTES_PER_ROW = 64 * 128       # fp8 query codes
 W_BYTES_PER_ROW = 64 * 4         # fp32 head weights
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_counters.txt")
+MLA_PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_mla_decode_b64_h128_counters.txt")
 COPY_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
 MLA_HEADS = 128                  # query heads of one sparse MLA decode row
@@ -89,20 +90,20 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_source_hash():
-    from sparse_attention_indexer_paged_amd.profile_summary import logits_source_hash
-    return logits_source_hash()
+def kernel_source_hash(files=("logits.hip", "sai_device.h")):
+    from sparse_attention_indexer_paged_amd.profile_summary import source_hash
+    return source_hash(files)
 
 
-def counter_traffic():
-    """HBM bytes per paged_mqa_logits launch from the committed rocprofv3 PMC
+def counter_traffic(path=PROFILE_COUNTERS, files=("logits.hip", "sai_device.h")):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 PMC
     summary, or None if absent or taken on different kernel source."""
-    if not os.path.exists(PROFILE_COUNTERS):
+    if not os.path.exists(path):
         return None
-    text = open(PROFILE_COUNTERS).read()
+    text = open(path).read()
     m_hash = re.search(r"kernel_source_hash:\s*(\w+)", text)
     m_val = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
-    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash():
+    if not m_hash or not m_val or m_hash.group(1) != kernel_source_hash(files):
         return None
     return float(m_val.group(1))
 
@@ -362,7 +363,9 @@ def mla_leg(torch, lib, wl, slots, dev, steps, ev, arm, s_ptr, cpu_seconds):
         "call_us": round(t_call * 1e6, 3),
         "splits_workspace_bytes": ws_bytes,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4), "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
+                     "traffic": (counter_traffic(MLA_PROFILE_COUNTERS, ("mla.hip", "sai_device.h"))
+                                 if wl.name.startswith("decode_b64") else None),
                      "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
                      "alg_gbps": round(alg_bytes / t_kernel / 1e9, 1)},
         "rows_per_s": round(rows / t_call, 1),

@@ -334,7 +334,7 @@ __device__ __forceinline__ void mla_stage8_to_lds(MlaChunkLds& sm, const MlaStag
 __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
     const uint8_t* __restrict__ cache, int64_t num_slots, int64_t block_size, int64_t block_stride,
-    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len,
+    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len, int rows,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   __shared__ MlaSmem sm;
@@ -490,17 +490,23 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
     const uint8_t* __restrict__ cache, int64_t num_slots, int64_t block_size, int64_t block_stride,
-    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len,
+    const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len, int rows,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
   __shared__ MlaChunkLds buf[2];
   __shared__ v4f xs[4][2][2][64];  // partial scores [head block][tile half][token half][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
+  // Workgroup g runs on XCD g % 8.  The head groups of one (row, split) pair
+  // take the same g % 8 and neighbouring dispatch slots, so they read the
+  // pair's entries through one XCD's L2 at about the same time.
   const int ngroups = heads / kMlaWideHeads;
-  const int split = blockIdx.x % nsplit;
-  const int hg = (blockIdx.x / nsplit) % ngroups;
-  const int row = blockIdx.x / (nsplit * ngroups);
+  const int xcd = blockIdx.x & 7, jx = blockIdx.x >> 3;
+  const int hg = jx % ngroups;
+  const int pair = (jx / ngroups) * 8 + xcd;
+  if (pair >= rows * nsplit) return;  // grid padded to a multiple of 8 pairs
+  const int split = pair % nsplit;
+  const int row = pair / nsplit;
   const int base0 = split * split_len;
   const int lim = min(k, base0 + split_len);
   const int32_t* srow = slots + (int64_t)row * k;
@@ -699,7 +705,8 @@ MlaPlan mla_plan(int64_t rows, int heads, int k) {
   ns = std::min<int64_t>(std::max<int64_t>(ns, 1), std::min(max_split, 16));
   p.split_len = (int)(((kk + ns - 1) / ns + kMlaChunk - 1) / kMlaChunk * kMlaChunk);
   p.nsplit = (kk + p.split_len - 1) / p.split_len;
-  p.grid = wgs * p.nsplit;
+  // the wide kernel pads its pairs (row, split) to a multiple of 8 (XCD map)
+  p.grid = p.wide ? (rows * p.nsplit + 7) / 8 * 8 * (heads / kMlaWideHeads) : wgs * p.nsplit;
   return p;
 }
 
@@ -736,7 +743,7 @@ extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t r
          dim3(p.wide ? 512 : 256), 0, stream, (const uint16_t*)q_nope, (const uint16_t*)q_pe, (int)heads,
          (const uint8_t*)cache, num_blocks * (int64_t)block_size, (int64_t)block_size,
          (int64_t)block_size * kMlaEntry, slots, k, sm_scale * 1.4426950408889634f, p.nsplit,
-         p.split_len, out, lse, ws_o, ws_ml);
+         p.split_len, (int)rows, out, lse, ws_o, ws_ml);
   if (hipGetLastError() != hipSuccess) return SAI_ELAUNCH;
   if (p.nsplit > 1) {
     launch(sparse_mla_combine_kernel, dim3((unsigned)(rows * (int64_t)heads)), dim3(128), 0, stream,

@@ -5,6 +5,7 @@
   HBM traffic:    python -m sparse_attention_indexer_paged_amd.profile_summary traffic \\
                       --fetch <fetch ..._counter_collection.csv> --write <write ..._counter_collection.csv> \\
                       --kernel paged_logits_kernel --copy-bytes 268435456 \\
+                      [--sources logits.hip,sai_device.h] \\
                       --command "<both rocprofv3 commands>" --out <txt>
 
 FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  They are scaled by what the
@@ -21,12 +22,17 @@ import statistics
 HERE = os.path.dirname(os.path.abspath(__file__))
 
 
-def logits_source_hash():
+def source_hash(files=("logits.hip", "sai_device.h")):
+    """Hash of the kernel sources a counter summary was taken on."""
     h = hashlib.sha256()
-    for f in ("logits.hip", "sai_device.h"):
+    for f in files:
         with open(os.path.join(HERE, "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def logits_source_hash():
+    return source_hash(("logits.hip", "sai_device.h"))
 
 
 def _per_dispatch(path, counter):
@@ -75,7 +81,7 @@ def traffic(args):
         f"fetch_bytes_per_launch: {fk * 1024:.0f}",
         f"write_bytes_per_launch: {wk * 1024:.0f}",
         f"traffic_bytes_per_launch: {(fk + wk) * 1024:.0f}",
-        f"kernel_source_hash: {logits_source_hash()}",
+        f"kernel_source_hash: {source_hash(tuple(args.sources.split(',')))}",
     ]
     open(args.out, "w").write("\n".join(lines) + "\n")
     print("\n".join(lines))
@@ -103,6 +109,8 @@ def main():
     t.add_argument("--kernel", default="paged_logits_kernel")
     t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--copy-bytes", type=int, default=256 << 20)
+    t.add_argument("--sources", default="logits.hip,sai_device.h",
+                   help="kernel sources (csrc/) whose hash the summary records")
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
     s = sub.add_parser("stats")
