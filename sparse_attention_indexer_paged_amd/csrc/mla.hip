@@ -477,8 +477,7 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 // step w/4.  The two waves of a head block add their partial scores through
 // LDS, so each wave holds a quarter of Q and half of O (under 256
 // registers: two waves share a SIMD), and the eight waves share the staged
-// chunk (double-buffered; a barrier for the partial scores and one for the
-// staging, per chunk).
+// chunks (three rotating buffers, one barrier per chunk).
 // Scores are formed transposed, S^T = K Q^T: lane (g, n) then holds head n
 // for tokens 4g..4g+3 and 16+4g..16+4g+3, which are exactly the eight
 // tokens it supplies as the A operand of P.V when the B operand (V) is read
@@ -493,8 +492,8 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len, int rows,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
-  __shared__ MlaChunkLds buf[2];
-  __shared__ v4f xs[4][2][2][64];  // partial scores [head block][tile half][token half][lane]
+  __shared__ MlaChunkLds buf[3];
+  __shared__ v4f xs[2][4][2][2][64];  // partial scores [chunk parity][head block][tile half][token half][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
   // Workgroup g runs on XCD g % 8.  The head groups of one (row, split) pair
@@ -537,8 +536,9 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     st = mla_gather8(cache, id, base0 + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
     id = mla_load_id(srow, base0 + 2 * kMlaChunk, lim);
     __syncthreads();
+    int cur = 0, nxt = 1;  // buffers of chunks c and c+1 (three rotate)
     for (int c = 0; c < nchunks; ++c) {
-      const MlaChunkLds& b = buf[c & 1];
+      const MlaChunkLds& b = buf[cur];
       // partial S^T over this wave's two tiles (each scaled) and RoPE step,
       // tokens n (acc 0) and 16+n (acc 1)
       v4f s0 = zero, s1 = zero;
@@ -565,11 +565,21 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
       }
       // the pair's halves meet in LDS; both waves form the same sum
       // (x + y == y + x), hence the same softmax state
-      xs[hw][dh][0][lane] = s0;
-      xs[hw][dh][1][lane] = s1;
+      xs[c & 1][hw][dh][0][lane] = s0;
+      xs[c & 1][hw][dh][1][lane] = s1;
+      // One barrier a chunk: before it, stage chunk c+1 into the third
+      // buffer (its last reader, chunk c-2's P.V, finished before every wave
+      // reached the previous barrier) and issue the loads of chunk c+2; after
+      // it, the partial scores and chunk c+1 are visible.  The partial
+      // scores alternate between two arrays for the same reason.  Past the
+      // end these touch only valid addresses and are never read.
+      mla_stage8_to_lds(buf[nxt], st);
+      st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
+                      block_stride);
+      id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
       __syncthreads();
-      s0 += xs[hw][dh ^ 1][0][lane];
-      s1 += xs[hw][dh ^ 1][1][lane];
+      s0 += xs[c & 1][hw][dh ^ 1][0][lane];
+      s1 += xs[c & 1][hw][dh ^ 1][1][lane];
       // scores in log2 units; token order 4g+e, then 16+4g+e
       const int4 ok0 = *reinterpret_cast<const int4*>(&b.valid[4 * g]);
       const int4 ok1 = *reinterpret_cast<const int4*>(&b.valid[16 + 4 * g]);
@@ -619,14 +629,8 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
           o[w2 * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(cv), o[w2 * 8 + d], 0, 0, 0);
         }
       }
-      // stage the next chunk into the other buffer (its last readers passed
-      // the previous barrier) and issue the loads of the one after; past the
-      // end these touch only valid addresses and are never read
-      mla_stage8_to_lds(buf[(c + 1) & 1], st);
-      st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
-                      block_stride);
-      id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
-      __syncthreads();
+      cur = nxt;
+      nxt = nxt == 2 ? 0 : nxt + 1;
     }
   }
 
