@@ -373,8 +373,42 @@ def mla_leg(torch, lib, wl, slots, dev, steps, ev, arm, s_ptr, cpu_seconds):
     if cpu_seconds > 0:
         res["cpu_baseline"], res["parity_sampled_rows"] = mla_cpu_baseline(
             cache, q_nope, q_pe, slots, out, lse, sm_scale, cpu_seconds)
+    # after the parity check: the writer overwrites entries of this cache
+    res["cache_write"] = mla_cache_write_leg(torch, lib, cache, dev, ev, arm, s_ptr)
     del cache
     return res
+
+
+def mla_cache_write_leg(torch, lib, cache, dev, ev, arm, s_ptr, n=65536, reps=10):
+    """mla_cache_write of n bf16 tokens (kv [n, 512], kpe [n, 64]) to scattered
+    slots of the MLA cache, timed with dispatch-carried events; HBM-bound:
+    per token 1024 + 128 B read, 8 B slot id, 656 B written."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(7)
+    kv = torch.randn((n, 512), device=dev, generator=g).to(torch.bfloat16)
+    kpe = torch.randn((n, 64), device=dev, generator=g).to(torch.bfloat16)
+    nslots = cache.shape[0] * cache.shape[1]
+    slots = torch.randperm(nslots, device=dev, generator=g)[:n].to(torch.int64)
+    P = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def call():
+        return lib.mla_cache_write(P(kv), kv.stride(0), P(kpe), kpe.stride(0), P(slots), n, P(cache),
+                                   cache.shape[0], cache.shape[1], s_ptr)
+    for _ in range(2):
+        assert call() == 0
+    e0, e1 = ev.create(reps), ev.create(reps)
+    for i in range(reps):
+        arm(e0[i], e1[i])
+        assert call() == 0
+    torch.cuda.synchronize()
+    t = float(np.mean([ev.elapsed_ms(e0[i], e1[i]) for i in range(reps)])) * 1e-3
+    ev.destroy(e0 + e1)
+    alg = n * (1024 + 128 + 8 + MLA_ENTRY_BYTES)
+    gbps = alg / t / 1e9
+    return {"tokens": n, "avg_launch_us": round(t * 1e6, 3),
+            "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "alg_bytes_per_launch": alg}}
 
 
 def mla_cpu_baseline(cache, q_nope, q_pe, slots, out, lse, sm_scale, min_seconds):
