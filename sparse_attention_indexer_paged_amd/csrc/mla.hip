@@ -740,7 +740,7 @@ extern "C" int sparse_mla_decode(const void* q_nope, const void* q_pe, int32_t r
   const MlaPlan p = mla_plan(rows, heads, k);
   const size_t need = mla_workspace(rows, heads, p);
   if (need > 0 && (!workspace || workspace_bytes < need || !aligned16(workspace))) return SAI_EWORKSPACE;
-  if (p.grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  if (p.grid > 0x7FFFFFFF || (p.nsplit > 1 && (int64_t)rows * heads > 0x7FFFFFFF)) return SAI_EUNSUPPORTED;
   float* ws_o = need ? reinterpret_cast<float*>(workspace) : nullptr;
   float* ws_ml = need ? ws_o + (size_t)rows * heads * p.nsplit * kMlaKv : nullptr;
   launch(p.wide ? sparse_mla_decode_wide_kernel : sparse_mla_decode_kernel, dim3((unsigned)p.grid),
