@@ -31,7 +31,7 @@ using namespace sai;
 #define SAI_DECODE_WAVES 2048
 #endif
 #ifndef SAI_DECODE_DEPTH
-#define SAI_DECODE_DEPTH 2
+#define SAI_DECODE_DEPTH 1
 #endif
 #ifndef SAI_DECODE_CAP
 #define SAI_DECODE_CAP 8
@@ -43,7 +43,9 @@ using namespace sai;
 namespace {
 
 // Decode launch shape: waves of the persistent grid (8 per CU), blocks in
-// the per-wave register ring (DEPTH-1 blocks in flight while one is scored),
+// the per-wave register ring (DEPTH-1 blocks in flight while one is scored;
+// at 1 each wave loads a block and scores it, and the eight waves of a CU
+// keep more K in flight than its miss queue takes, with fewer registers),
 // the most units scored per straight-line group, and the floats of each
 // wave's LDS result stage.
 constexpr int kDecodeWaves = SAI_DECODE_WAVES;
