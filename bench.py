@@ -52,6 +52,7 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_c
 MLA_PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_mla_decode_b64_h128_counters.txt")
 COPY_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
+GRAPH_STEPS = 8                  # steps captured per hipGraph for graph_ms_per_step
 MLA_HEADS = 128                  # query heads of one sparse MLA decode row
 MLA_FLOPS_PER_SLOT = 2 * (576 + 512)   # per (row, head, valid slot): q.k over 576, p.v over 512
 MLA_ENTRY_BYTES = 656
@@ -559,23 +560,24 @@ def main():
     try:
         if args.no_graph:
             raise RuntimeError("disabled by --no-graph")
+        # one graph holds GRAPH_STEPS consecutive steps (rotating the cache
+        # pools like the timed loop), so a replay's launch cost is shared
         side = torch.cuda.Stream()
         gcalls = launches(ctypes.c_void_p(side.cuda_stream))
-        graphs = []
-        for p in range(npools):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=side):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            for j in range(GRAPH_STEPS):
                 for _, fn in gcalls:
-                    assert fn(p) == 0
-            graphs.append(g)
-        for i in range(args.warmup):
-            graphs[i % len(graphs)].replay()
+                    assert fn(j) == 0
+        for _ in range(max(1, args.warmup // GRAPH_STEPS)):
+            g.replay()
         torch.cuda.synchronize()
+        reps = max(1, K // GRAPH_STEPS)
         tg = time.perf_counter()
-        for i in range(K):
-            graphs[i % len(graphs)].replay()
+        for _ in range(reps):
+            g.replay()
         torch.cuda.synchronize()
-        graph_ms = (time.perf_counter() - tg) * 1e3 / K
+        graph_ms = (time.perf_counter() - tg) * 1e3 / (reps * GRAPH_STEPS)
     except Exception as exc:  # noqa: BLE001
         print(f"graph replay skipped: {exc}", file=sys.stderr)
 
