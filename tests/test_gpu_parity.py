@@ -495,6 +495,42 @@ def test_decode_pipeline_graph_capture_replays_match_eager():
             assert torch.equal(a, b)
 
 
+def test_wide_row_pipeline_graph_capture_replays_match_eager():
+    """Rows wider than one top-k segment (segment pass, candidate lists in
+    the workspace, merge pass) captured in a hipGraph: every replay equals
+    the eager result, with eager work between replays."""
+    _say("hipGraph capture of the decode pipeline, 40960-column rows (segments + merge)")
+    wl = synth.custom(4, 2, [40000, 20000, 3000, 17000], num_blocks=1500, bt_width=640, seed=47)
+    g = GpuWorkload(wl)
+    q = g.q_fp8.view(4, 2, 64, 128)
+    eager = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+    torch.cuda.synchronize()
+    logits, idx, _ = eager
+    rl = torch.from_numpy(np.repeat(wl.ctx, 2) - 2 + np.tile(np.arange(2), 4) + 1).to(torch.int32)
+    assert np.array_equal(idx.cpu().numpy(), O.topk_rows(logits.cpu().numpy(), rl.numpy(), 2048))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)   # warm-up on side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+    for rep in range(3):
+        for t in out:
+            t.fill_(-7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        eager2 = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
+        torch.cuda.synchronize()
+        for a, b in zip(eager2, eager):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000])
 def test_topk_every_row_width_path(width):
     """Row widths on both sides of each register-resident size and the
