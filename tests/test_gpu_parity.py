@@ -531,6 +531,48 @@ def test_wide_row_pipeline_graph_capture_replays_match_eager():
             assert torch.equal(a, b)
 
 
+def test_prefill_pipeline_graph_capture_replays_match_eager():
+    """gather -> mqa_logits -> top-k with slot ids (3072 rows, so the top-k
+    takes its many-row shapes) captured in a hipGraph: every replay equals
+    the eager result, with eager work between replays."""
+    _say("hipGraph capture of the prefill pipeline, 2000 + 1072 tokens")
+    wl = synth.custom(2, 0, [2000, 1072], num_blocks=60, bt_width=32, seed=53)
+    g = GpuWorkload(wl)
+    total, width = wl.total_tokens, 2048
+
+    def run():
+        kv, ks = sai.gather_indexer_k(g.pool, g.block_table, g.cu, total)
+        logits, row_len, row_req = sai.mqa_logits(g.q_fp8, g.w_eff, kv, ks, g.cu, width)
+        idx, slots = sai.topk_rows_slots(logits, row_len, row_req, g.block_table, 2048)
+        return kv, ks, logits, idx, slots
+
+    eager = run()
+    torch.cuda.synchronize()
+    assert np.array_equal(eager[3].cpu().numpy(),
+                          O.topk_rows(eager[2].cpu().numpy(), np.r_[1:2001, 1:1073].astype(np.int32), 2048))
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()   # warm-up on side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        out = run()
+    for rep in range(3):
+        for t in out:
+            t.fill_(0xA5 if t.dtype == torch.uint8 else -7)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(out, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        eager2 = run()
+        torch.cuda.synchronize()
+        for a, b in zip(eager2, eager):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000])
 def test_topk_every_row_width_path(width):
     """Row widths on both sides of each register-resident size and the
