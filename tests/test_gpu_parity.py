@@ -573,6 +573,65 @@ def test_prefill_pipeline_graph_capture_replays_match_eager():
             assert torch.equal(a, b)
 
 
+def test_producers_graph_capture_replays_match_eager():
+    """The q quantiser, the indexer K-cache writer and the MLA cache writer
+    captured in one hipGraph: every replay writes the bytes the eager calls
+    wrote (skipped slots included), with eager work between replays."""
+    _say("hipGraph capture of the producers: q quant, K-cache write, MLA cache write")
+    rng = np.random.default_rng(59)
+    n = 300
+    q = bf16_tensor(synth.f32_to_bf16_bits(rng.standard_normal((n, 64, 128)).astype(np.float32)))
+    wt = torch.from_numpy((rng.standard_normal((n, 64)) / 64).astype(np.float32)).to(DEV)
+    k = bf16_tensor(synth.f32_to_bf16_bits(rng.standard_normal((n, 128)).astype(np.float32)))
+    kv = bf16_tensor(synth.f32_to_bf16_bits(rng.standard_normal((n, 576)).astype(np.float32)))
+    slot_np = rng.permutation(20 * 64)[:n].astype(np.int64)
+    slot_np[::37] = -1
+    slot = torch.from_numpy(slot_np).to(DEV)
+    icache = torch.zeros((20, 8448), dtype=torch.uint8, device=DEV)
+    mcache = torch.zeros((20, 64, 656), dtype=torch.uint8, device=DEV)
+    qf = torch.empty((n, 64, 128), dtype=torch.uint8, device=DEV)
+    weff = torch.empty((n, 64), dtype=torch.float32, device=DEV)
+    qs = torch.empty((n,), dtype=torch.float32, device=DEV)
+    outs = (qf, weff, qs, icache, mcache)
+
+    def run():
+        sai.indexer_q_quant(q, wt, qf, weff, qs)
+        sai.indexer_k_cache_write(k, slot, icache)
+        sai.mla_cache_write(kv[:, :512], kv[:, 512:], slot, mcache)
+
+    def reset():
+        qf.fill_(0xA5)
+        weff.fill_(-7)
+        qs.fill_(-7)
+        icache.zero_()
+        mcache.zero_()
+
+    run()
+    torch.cuda.synchronize()
+    eager = [t.clone() for t in outs]
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s):
+        run()   # warm-up on side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run()
+    for rep in range(3):
+        reset()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b), f"replay {rep} differs"
+        reset()
+        run()
+        torch.cuda.synchronize()
+        for a, b in zip(outs, eager):
+            assert torch.equal(a, b)
+
+
 @pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000])
 def test_topk_every_row_width_path(width):
     """Row widths on both sides of each register-resident size and the
