@@ -34,7 +34,7 @@ using namespace sai;
 #define SAI_DECODE_DEPTH 1
 #endif
 #ifndef SAI_DECODE_CAP
-#define SAI_DECODE_CAP 8
+#define SAI_DECODE_CAP 4
 #endif
 #ifndef SAI_DECODE_STAGE
 #define SAI_DECODE_STAGE 2048
