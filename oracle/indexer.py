@@ -341,17 +341,23 @@ def topk_rows(logits, row_len, k):
     ROCm/ATOM PR #1094 (Technical Details) selects a sparse top-k per query
     and hands it on in a 2-D index buffer.  Column s < row_len[r] is ranked by
     the key (-L[r, s], s): larger logit first, lower index first among equal
-    logits (-0.0 == +0.0).  The first min(k, n) are written in ascending
-    column order, then -1 padding.  Returns int32 [rows, k].
+    logits (-0.0 == +0.0).  A NaN ranks after every number (-inf included)
+    and NaNs tie with each other (the pages print no rule for NaN; this is
+    the ranking the library documents for the NaN logits of blocks outside
+    the pool).  The first min(k, n) are written in ascending column order,
+    then -1 padding.  Returns int32 [rows, k].
     """
     logits = np.asarray(logits)
     R, W = logits.shape
     out = np.full((R, k), -1, dtype=np.int32)
     for r in range(R):
         n = int(min(max(int(row_len[r]), 0), W))
-        vals = logits[r, :n].astype(np.float64) + 0.0      # -0.0 -> +0.0
+        with np.errstate(invalid="ignore"):                 # signalling NaNs widen quietly
+            vals = logits[r, :n].astype(np.float64) + 0.0  # -0.0 -> +0.0
+        nan = np.isnan(vals)
         idx = np.arange(n)
-        order = np.lexsort((idx, -vals))                    # by -value, then index
+        # by NaN last, then -value, then index
+        order = np.lexsort((idx, -np.where(nan, 0.0, vals), nan))
         sel = np.sort(order[:min(k, n)])
         out[r, :sel.size] = sel
     return out
@@ -363,13 +369,24 @@ def topk_to_global_slots(topk_idx, row_req, block_table):
     ROCm/ATOM PR #1094 (Technical Details) converts the request-local top-k
     indices into global paged KV indices for sparse MLA decode; with 64-token
     blocks, local index i of request b lives in slot
-    block_table[b][i // 64] * 64 + i % 64.  -1 stays -1.
+    block_table[b][i // 64] * 64 + i % 64.  -1 (padding: no token) stays -1.
+    An index the table does not map also gives -1: a row whose request is
+    not a row of the table, an index whose block lies past the table's
+    width, or a negative table entry (the table's own "no block" marker).
     """
     topk_idx = np.asarray(topk_idx)
+    table_all = np.asarray(block_table, dtype=np.int64)
+    n_req, n_cols = table_all.shape
     out = np.full(topk_idx.shape, -1, dtype=np.int32)
     for r in range(topk_idx.shape[0]):
-        table = np.asarray(block_table[int(row_req[r])], dtype=np.int64)
+        b = int(row_req[r])
+        if b < 0 or b >= n_req:
+            continue
         i = topk_idx[r].astype(np.int64)
-        ok = i >= 0
-        out[r, ok] = (table[i[ok] // BLOCK] * BLOCK + i[ok] % BLOCK).astype(np.int32)
+        col = np.where(i >= 0, i // BLOCK, n_cols)
+        mapped = col < n_cols
+        blk = np.full(i.shape, -1, dtype=np.int64)
+        blk[mapped] = table_all[b, col[mapped]]
+        ok = mapped & (blk >= 0)
+        out[r, ok] = (blk[ok] * BLOCK + i[ok] % BLOCK).astype(np.int32)
     return out

@@ -546,3 +546,39 @@ def test_slot_round_trip():
             blk, off = sl // 64, sl % 64
             assert np.array_equal(pool[blk, off * 128:(off + 1) * 128], kv[cu[r] + i])
             assert pool[blk, 8192 + 4 * off:8192 + 4 * off + 4].view(np.float32)[0] == ks[cu[r] + i]
+
+
+def test_slot_map_hand_values_and_unmapped_indices():
+    """Slot ids worked by hand from the map block_table[b][i // 64] * 64 + i % 64
+    (ROCm/ATOM PR #1094, Technical Details), and -1 for every index the table
+    does not map: padding, a negative table entry, a column past the table and
+    a request that is not a row of the table (negative or too large)."""
+    bt = np.array([[5, 9, -1], [2, 0, 7]], np.int32)
+    idx = np.array([[0, 63, 64, 127, -1, 128, 191, 192],
+                    [0, 1, 64, 130, 191, -1, -1, -1],
+                    [0, 1, 2, 3, 4, 5, 6, 7],
+                    [0, 1, 2, 3, 4, 5, 6, 7]], np.int32)
+    req = np.array([0, 1, 5, -1], np.int32)
+    got = O.topk_to_global_slots(idx, req, bt)
+    # row 0: block 5 -> 320.., block 9 -> 576.., entry -1 and column 3 (past the table) -> -1
+    assert got[0].tolist() == [320, 383, 576, 639, -1, -1, -1, -1]
+    # row 1: block 2 -> 128, 129; block 0 -> 0; block 7 -> 448 + 2 = 450, 448 + 63 = 511
+    assert got[1].tolist() == [128, 129, 0, 450, 511, -1, -1, -1]
+    assert got[2].tolist() == [-1] * 8
+    assert got[3].tolist() == [-1] * 8
+    assert got.dtype == np.int32
+
+
+def test_topk_nan_ranks_below_every_number_and_ties_by_index():
+    """NaN (either sign, any payload) ranks after -inf; NaNs tie, so the
+    lower index wins among them.  Worked by hand on a 7-column row."""
+    bits = np.array([0x3F800000, 0x7FC00000, 0xFF800000, 0xFFC00001, 0x40000000,
+                     0x7F800001, 0xBF800000], np.uint32)        # 1, NaN, -inf, -NaN, 2, NaN, -1
+    L = bits.view(np.float32)[None, :]
+    for k, want in [(2, [0, 4]), (4, [0, 2, 4, 6]), (5, [0, 1, 2, 4, 6]), (6, [0, 1, 2, 3, 4, 6]),
+                    (7, [0, 1, 2, 3, 4, 5, 6])]:
+        got = O.topk_rows(L, np.array([7]), k)[0]
+        assert got.tolist() == want, (k, got)
+    # only NaNs: the lowest indices
+    N = np.full((1, 10), np.nan, np.float32)
+    assert O.topk_rows(N, np.array([10]), 3)[0].tolist() == [0, 1, 2]
