@@ -129,8 +129,12 @@ class Workload:
         return (x * np.float32(DIM ** -0.5 * HEADS ** -0.5)).astype(np.float32)
 
     def poisoned_pool(self):
-        """uint8 [num_blocks, 8448], every byte poison."""
-        return np.tile(poison_block(), (self.num_blocks, 1))
+        """uint8 [num_blocks, 8448], every byte poison (the bytes of
+        ``poison_block`` in every block)."""
+        pool = np.empty((self.num_blocks, BLOCK_BYTES), dtype=np.uint8)
+        pool[:, :BLOCK * DIM] = POISON_CODE
+        pool[:, BLOCK * DIM:] = np.tile(POISON_SCALE_BYTES, BLOCK)[None, :]
+        return pool
 
 
 def _assign_blocks(rng, ctx, num_blocks, bt_width):
