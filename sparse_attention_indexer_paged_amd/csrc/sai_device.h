@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "sai.h"
+#include "sai_profile.h"
 
 namespace sai {
 
@@ -49,11 +50,14 @@ __device__ __forceinline__ float fp8_scale(float amax) {
 }
 
 // Order-preserving float -> uint32 key (larger float, larger key).  -0.0 is
-// folded onto +0.0 so the two tie.
+// folded onto +0.0 so the two tie.  Every NaN (either sign, any payload)
+// gets key 0, below -inf (key 0x007FFFFF): NaNs rank last and tie with each
+// other, so ties among them go to the lower index like any other tie.
 __device__ __forceinline__ uint32_t f32_order_key(float f) {
   uint32_t u = __float_as_uint(f);
   if (u == 0x80000000u) u = 0u;
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return (u & 0x7FFFFFFFu) > 0x7F800000u ? 0u : k;
 }
 
 // ---------------------------------------------------------------- wave ops

@@ -316,14 +316,18 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   int32_t col[CIN ? VPT : 1];
   float v[CIN ? 1 : VPT];
   // Every load is issued unconditionally from an address clamped into the
-  // row's stride (or, for the merge, into the row's candidate block), not
-  // into its length, so all of a thread's loads are in flight together and
-  // positions past the length are masked afterwards.  With EARLY (few
-  // workgroups, so latency-bound) they go out before the row length has
-  // arrived; otherwise after it, so that rows which need no selection
-  // (length <= k) skip them.  (A runtime choice would join the two orders,
-  // and the wait-count pass drains all loads at such a join.)
-  auto load_row = [&]() {
+  // row (or, for the merge, into the row's candidate block), so all of a
+  // thread's loads are in flight together and positions past the length are
+  // masked afterwards.  With EARLY (few workgroups, so latency-bound) they
+  // go out before the row length has arrived and are clamped to the stride;
+  // otherwise after it, clamped to the length rounded up to 4 columns (a
+  // causal prefill row then reads only its visible part: positions past it
+  // re-read the row's last 16 bytes, a line already on its way), and rows
+  // which need no selection (length <= k) skip them.  (A runtime choice
+  // would join the two orders, and the wait-count pass drains all loads at
+  // such a join.)  `lim` is the number of columns that may be read, >= 1,
+  // a multiple of 4 for VEC.
+  auto load_row = [&](int64_t lim) {
     if (CIN) {
       const int nc = nseg * k;
       const uint32_t* kp = c_key + (int64_t)r * nc;
@@ -350,17 +354,17 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   #pragma unroll
       for (int e = 0; e < VPT; e += 4) {
         if (VEC) {  // stride is a multiple of 4
-          const int64_t p = min(cbase + base + e, stride - 4);
+          const int64_t p = min(cbase + base + e, lim - 4);
           const float4 f = *reinterpret_cast<const float4*>(x0 + p);
           v[e] = f.x; v[e + 1] = f.y; v[e + 2] = f.z; v[e + 3] = f.w;
         } else {
   #pragma unroll
-          for (int i = 0; i < 4; ++i) v[e + i] = x0[min(cbase + base + e + i, stride - 1)];
+          for (int i = 0; i < 4; ++i) v[e + i] = x0[min(cbase + base + e + i, lim - 1)];
         }
       }
     }
   };
-  if constexpr (EARLY) load_row();
+  if constexpr (EARLY) load_row(stride);
   // read after the row's loads are issued: a scalar load ahead of them
   // would make their address computation wait for it
   const int len = (int)min((int64_t)max(row_len[r], 0), stride);
@@ -446,7 +450,8 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   };
   if constexpr (!EARLY) {
     if (done_early()) return;
-    load_row();
+    // len > k >= 1 here; for VEC the stride is a multiple of 4
+    load_row(VEC ? min(stride, ((int64_t)len + 3) & ~(int64_t)3) : (int64_t)len);
   }
   int n;  // positions of this workgroup
   if (CIN) {

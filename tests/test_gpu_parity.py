@@ -235,6 +235,68 @@ def test_topk_adversarial_wide_rows(k):
     assert np.array_equal(got.cpu().numpy(), want)
 
 
+def _nan_rows(W):
+    """Rows with NaNs of both signs and several payloads among numbers."""
+    rng = np.random.default_rng(W + 1)
+    nan_bits = np.array([0x7FC00000, 0xFFC00000, 0x7F800001, 0xFFFFFFFF, 0x7FFFFFFF], np.uint32)
+    rows = []
+    r = rng.standard_normal(W).astype(np.float32)
+    m = rng.random(W) < 0.1
+    r[m] = nan_bits[rng.integers(0, 5, m.sum())].view(np.float32)
+    rows.append(r)                                             # 10 % NaN among numbers
+    rows.append(np.full(W, np.nan, np.float32))                # all NaN
+    r = np.full(W, np.nan, np.float32)
+    r[rng.choice(W, 1500, replace=False)] = rng.standard_normal(1500)
+    rows.append(r)                                             # fewer numbers than k: NaNs fill up
+    r = np.full(W, -np.inf, np.float32)
+    r[::3] = nan_bits[1].view(np.float32)
+    r[1::97] = 0.5
+    rows.append(r)                                             # NaN, -inf and a few numbers
+    L = np.stack(rows)
+    lens = np.array([W, W, W, W], np.int32)
+    return L, lens
+
+
+@pytest.mark.parametrize("width", [9000, 40000, 140000])
+def test_topk_nan_ranks_last(width):
+    """NaN ranks below -inf and NaNs tie by index on every selection path
+    (one pass, segments + merge, streaming), as the oracle ranks them."""
+    _say(f"topk_rows: NaN rows, width {width}")
+    L, lens = _nan_rows(width)
+    for k in (2048, 37):
+        got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
+        assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, k)), k
+
+
+def test_decode_block_outside_pool_gives_nan_logits_ranked_last():
+    """A block-table entry past the pool makes that block's visible columns
+    NaN; the decode top-k ranks them last and the slot ids follow the table."""
+    _say("decode pipeline: a block id outside the pool")
+    wl = synth.custom(2, 1, [3000, 2500], num_blocks=100, bt_width=50, seed=31)
+    g = GpuWorkload(wl)
+    bt = wl.block_table.copy()
+    bt[0, 7] = wl.num_blocks + 5
+    bt[1, 10] = -3
+    q = g.q_fp8.view(wl.batch, 1, 64, 128)
+    logits, idx, slots = sai.decode_indexer(q, g.w_eff, g.pool, torch.from_numpy(bt).to(DEV), g.ctx)
+    torch.cuda.synchronize()
+    gl = logits.cpu().numpy()
+    assert np.isnan(gl[0, 7 * 64:8 * 64]).all() and np.isnan(gl[1, 640:704]).all()
+    o = OracleWorkload(wl)
+    ref = O.paged_mqa_logits(o.q_codes.reshape(2, 1, 64, 128), o.w_eff, o.pool, wl.block_table,
+                             wl.ctx, 1, wl.width)
+    ok = np.ones(gl.shape, bool)
+    ok[0, 7 * 64:8 * 64] = False
+    ok[1, 640:704] = False
+    assert_logits_close(np.where(ok, gl, 0.0), np.where(ok, ref, 0.0), "outside-pool decode")
+    lim, req = O.decode_limits(wl.ctx, 1)
+    want = O.topk_rows(gl, lim, 2048)
+    assert np.array_equal(idx.cpu().numpy(), want)
+    assert not np.isin(np.arange(448, 512), want[0]).any()
+    assert not np.isin(np.arange(640, 704), want[1]).any()
+    assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, req, bt))
+
+
 @pytest.mark.parametrize("width,k", [(140000, 2048), (300000, 100)])
 def test_topk_widest_rows(width, k):
     """Rows past the two-pass limit (streaming kernel) and a small k whose
@@ -288,6 +350,7 @@ def test_slots_edge_cases():
     req = np.array([0, 1, 5], np.int32)
     got = sai.topk_to_global_slots(torch.from_numpy(idx).to(DEV), torch.from_numpy(req).to(DEV),
                                    torch.from_numpy(bt).to(DEV)).cpu().numpy()
+    assert np.array_equal(got, O.topk_to_global_slots(idx, req, bt))
     assert got[0].tolist() == [320, 383, 576, 639, -1, -1, -1, -1]
     assert got[1].tolist() == [128, 129, 0, 450, 511, -1, -1, -1]
     assert got[2].tolist() == [-1] * 8
@@ -319,6 +382,7 @@ def test_topk_rows_slots_matches_the_two_calls(width):
     idx, slots = sai.topk_rows_slots(T(L), T(lens), T(req), T(bt), k)
     sep = sai.topk_to_global_slots(idx, T(req), T(bt))
     assert np.array_equal(idx.cpu().numpy(), want)
+    assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, req, bt))
     assert torch.equal(slots, sep)
     assert (slots[6] == -1).all()
 
@@ -655,13 +719,7 @@ def test_slots_wide_table_elementwise_path():
     req = np.array([0, 2, 1, 7], np.int32)
     got = sai.topk_to_global_slots(torch.from_numpy(idx).to(DEV), torch.from_numpy(req).to(DEV),
                                    torch.from_numpy(bt).to(DEV)).cpu().numpy()
-    want = np.full_like(idx, -1)
-    for r in range(3):
-        b = req[r]
-        blk = bt[b][np.maximum(idx[r], 0) // 64]
-        ok = (idx[r] >= 0) & (blk >= 0)
-        want[r, ok] = blk[ok] * 64 + idx[r][ok] % 64
-    assert np.array_equal(got, want)
+    assert np.array_equal(got, O.topk_to_global_slots(idx, req, bt))
 
 
 # ---------------------------------------------------------------- past 4 GiB
