@@ -124,16 +124,37 @@ def build_inputs(torch, sai, wl, dev, npools):
     return pools, q_fp8, w_eff
 
 
-def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
-    """Time the oracle (as it stands) on a bounded sample of the workload and
-    check the GPU's logits / top-k on those rows."""
-    import oracle as O
-    from sparse_attention_indexer_paged_amd import synth
+def host_info():
+    """Threads the oracle's BLAS runs on (the only multi-threaded part of
+    the oracle; the rest is single-threaded numpy), the CPUs this process may
+    use and the host CPU model."""
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:  # noqa: BLE001
         threads = 1
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        usable = os.cpu_count()
+    return {"cores": threads, "host_cpus": os.cpu_count(), "usable_cpus": usable, "cpu_model": model}
+
+
+def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
+    """Time the oracle (as it stands) on a bounded sample of the workload and
+    check the GPU's logits / top-k on those rows."""
+    import oracle as O
+    from sparse_attention_indexer_paged_amd import synth
+    host = host_info()
     pool = wl.poisoned_pool()
     for b in sample_requests:
         O.k_cache_write(synth.bf16_bits_to_f32(wl.k_request(b)), wl.slots_request(b), pool)
@@ -159,7 +180,7 @@ def cpu_baseline(wl, sample_requests, gpu_logits, min_seconds):
     return {
         "value": round(reps * len(rows) / el, 2),
         "unit": "query-tokens/s",
-        "cores": threads,
+        **host,
         "kind": "oracle",
         "sample": (f"{len(rows)} of {wl.rows} query rows (requests {sample_requests[0]}.."
                    f"{sample_requests[-1]}, {int(wl.ctx[sample_requests].sum())} keys) x {reps} "
@@ -260,11 +281,7 @@ def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
     """Oracle throughput on a sample of prefill rows spread over the request."""
     import oracle as O
     from sparse_attention_indexer_paged_amd import synth
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    host = host_info()
     pool = wl.poisoned_pool()
     for b in range(wl.batch):
         O.k_cache_write(synth.bf16_bits_to_f32(wl.k_request(b)), wl.slots_request(b), pool)
@@ -288,7 +305,7 @@ def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
     ok = bool(np.all(np.abs(g[fin] - ref[rows][fin]) <= 1e-4 + 1e-3 * np.abs(ref[rows][fin]))
               and np.all(np.isneginf(g[~fin])))
     return {
-        "value": round(reps * len(rows) / el, 2), "unit": "query-tokens/s", "cores": threads,
+        "value": round(reps * len(rows) / el, 2), "unit": "query-tokens/s", **host,
         "kind": "oracle",
         "sample": f"{len(rows)} of {wl.rows} prefill rows spread over the batch x {reps} passes of "
                   f"gather+logits+top-2048+slot ids, {el:.1f} s, numpy/OpenBLAS fp64",
@@ -446,15 +463,11 @@ def mla_cpu_baseline(cache, q_nope, q_pe, slots, out, lse, sm_scale, min_seconds
     ok = bool(np.all(np.abs(got - ref) <= 2.0 ** -8 * ref_abs + 1e-30)
               and np.all(np.abs(got_lse[fin] - ref_lse[fin]) <= 1e-4 + 1e-5 * np.abs(ref_lse[fin]))
               and np.all(np.isneginf(got_lse[~fin])))
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # noqa: BLE001
-        threads = 1
+    host = host_info()
     return {
         "value": round(reps * len(pick) / el, 3),
         "unit": "query-rows/s",
-        "cores": threads,
+        **host,
         "kind": "oracle",
         "sample": (f"{len(pick)} of {rows} rows x {MLA_HEADS} heads x {reps} passes over their "
                    f"{int((sl >= 0).sum())} selected slots, {el:.1f} s, numpy fp64"),

@@ -10,7 +10,10 @@
  * Conventions shared by every entry point
  * ---------------------------------------
  *  - Pointers are DEVICE pointers owned by the caller; the library never
- *    allocates, frees or keeps them, and holds no state between calls.
+ *    allocates, frees or keeps them, and the entry points of this header
+ *    hold no state between calls.  (The one piece of state in the library
+ *    is the profiling aid of sai_profile.h: a per-thread event pair that the
+ *    calling thread's next launch consumes.  It changes no result.)
  *    (Preallocated outputs written in place, as the review of
  *    cp_gather_indexer_k_quant_cache in vLLM PR #25869 asks for.)
  *  - Scalars are host values.  Validation reads host scalars only: no call
@@ -57,19 +60,6 @@ extern "C" {
 
 /* Human-readable name of a status code (static storage). */
 const char* sai_status_string(int status);
-
-/*
- * sai_time_next_launch -- profiling aid (not an operation of the pages).
- * Arms a pair of events (created by the caller with hipEventCreate*) for the
- * next kernel that the calling thread launches through any entry point
- * below: that launch carries them in its own dispatch, so
- * hipEventElapsedTime(start, stop) is the kernel's execution time without
- * the marker packets a separate hipEventRecord adds to the stream.  The pair
- * is used once; entry points that launch several kernels time the first.
- * Both NULL disarms.  SAI_EINVAL if exactly one is NULL.  Per thread; no
- * device work.
- */
-int sai_time_next_launch(hipEvent_t start, hipEvent_t stop);
 
 /*
  * indexer_k_cache_write -- quantise K rows to fp8 and scatter them into the
@@ -237,8 +227,11 @@ int mqa_logits_chunked(const void* q_fp8, const float* weights, const void* k_fp
  *
  * Row r ranks its columns s < n_r = clamp(row_len[r], 0, logits_stride) by
  * (larger logit, then lower index); -0.0 and +0.0 are equal.  It writes the
- * min(k, n_r) winners in ascending column order, then -1 up to k.  NaN
- * inside a row is outside the contract.
+ * min(k, n_r) winners in ascending column order, then -1 up to k.  A NaN
+ * (either sign, any payload) ranks below every number, -inf included, and
+ * NaNs tie with each other, so they are taken only when a row has fewer
+ * than k other columns, lowest index first (paged_mqa_logits writes NaN
+ * for blocks outside the pool).
  *
  *   logits   [rows, logits_stride] fp32
  *   row_len  [rows] int32 (device)

@@ -1,6 +1,8 @@
-"""The C-ABI library loads, exports every symbol include/sai.h declares, and its
-host-side validation rejects bad arguments without touching a GPU."""
+"""The C-ABI library loads, exports every symbol the headers under include/
+declare, and its host-side validation rejects bad arguments without touching a
+GPU."""
 import ctypes
+import glob
 import os
 import re
 import subprocess
@@ -10,13 +12,13 @@ import pytest
 from sparse_attention_indexer_paged_amd import binding
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-HEADER = os.path.join(ROOT, "include", "sai.h")
+HEADERS = sorted(glob.glob(os.path.join(ROOT, "include", "*.h")))
 
 SAI_OK, SAI_EINVAL, SAI_EUNSUPPORTED, SAI_EWORKSPACE = 0, -1, -2, -3
 
 
 def declared_functions():
-    text = open(HEADER).read()
+    text = "\n".join(open(h).read() for h in HEADERS)
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\**\s+\**(\w+)\s*\(", text, flags=re.M)))
 
