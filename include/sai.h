@@ -57,6 +57,10 @@ extern "C" {
 #define SAI_EUNSUPPORTED (-2) /* shape outside what the kernels are built for */
 #define SAI_EWORKSPACE (-3)   /* workspace missing or too small */
 #define SAI_ELAUNCH (-4)      /* the HIP runtime rejected a launch */
+#define SAI_ESCRATCH (-5)     /* needs more than the built-in scratch buffer (allocation-free entry) */
+
+/* bytes of the built-in device scratch buffer of the allocation-free entry */
+#define SAI_NOALLOC_SCRATCH_BYTES (16u << 20)
 
 /* Human-readable name of a status code (static storage). */
 const char* sai_status_string(int status);
@@ -280,6 +284,31 @@ int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* r
                     const int32_t* row_req, const int32_t* block_table, int64_t bt_stride,
                     int32_t batch, int32_t rows, int32_t k, int32_t* out_idx, int32_t* out_slots,
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * topk_rows_slots_noalloc -- topk_rows_slots for callers that cannot
+ * allocate device memory (code under hipGraph capture, tight serving loops,
+ * harnesses that forbid hipMalloc): no workspace argument, and no call to
+ * hipMalloc, hipFree or any allocating routine.
+ *
+ * Same arguments (minus the workspace), outputs and errors as
+ * topk_rows_slots.  Rows wider than 16384 columns keep their segment
+ * candidates in a buffer built into the library: a file-scope device array
+ * of SAI_NOALLOC_SCRATCH_BYTES (16 MiB) that each device holds from the
+ * library's load until the process ends.  A problem whose
+ * topk_workspace_bytes(rows, logits_stride, k) exceeds that returns
+ * SAI_ESCRATCH and launches nothing (e.g. 256 rows of 65536 columns at
+ * k = 2048 fit exactly; 257 do not).  The first call on a device resolves
+ * that device's array address (hipGetSymbolAddress, with the stream's
+ * device made current for the lookup); the address is then kept.  Every
+ * call on a device shares its one array, so calls that overlap on the same
+ * device (other streams, other threads) race and must be serialised by the
+ * caller; nothing needs clearing between calls.
+ */
+int topk_rows_slots_noalloc(const float* logits, int64_t logits_stride, const int32_t* row_len,
+                            const int32_t* row_req, const int32_t* block_table, int64_t bt_stride,
+                            int32_t batch, int32_t rows, int32_t k, int32_t* out_idx,
+                            int32_t* out_slots, hipStream_t stream);
 
 /*
  * mla_cache_write -- write tokens into the fp8 MLA cache that sparse MLA

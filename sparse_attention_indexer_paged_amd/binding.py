@@ -48,6 +48,8 @@ SIGNATURES = {
                              _c_void_p],
     "topk_rows_slots": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32, _i32,
                         _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
+    "topk_rows_slots_noalloc": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _i32,
+                                _i32, _c_void_p, _c_void_p, _c_void_p],
     "mla_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _i32,
                         _c_void_p],
     "sparse_mla_workspace_bytes": [_i32, _i32, _i32],
@@ -394,6 +396,30 @@ def topk_rows_slots(logits, row_len, row_req, block_table, k=TOPK_MAX, out=None,
                                   rows, k, _ptr(out), _ptr(slots), _ptr(workspace),
                                   workspace.numel() if workspace is not None else 0, _stream()),
            "topk_rows_slots")
+    return out, slots
+
+
+def topk_rows_slots_noalloc(logits, row_len, row_req, block_table, k=TOPK_MAX, out=None, slots=None):
+    """topk_rows_slots through the allocation-free entry point (segment
+    candidates in the library's built-in device buffer).  Pass ``out`` and
+    ``slots`` to allocate nothing at all; otherwise they are allocated here,
+    outside the C call."""
+    _need(logits, torch.float32, "logits", 2)
+    _need(row_len, torch.int32, "row_len", 1)
+    _need(row_req, torch.int32, "row_req", 1)
+    _need(block_table, torch.int32, "block_table", 2)
+    rows = logits.shape[0]
+    if row_len.shape[0] != rows or row_req.shape[0] != rows:
+        raise ValueError("row_len and row_req need one entry per row")
+    dev = logits.device
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev) if out is None else out
+    slots = torch.empty((rows, k), dtype=torch.int32, device=dev) if slots is None else slots
+    _out(out, torch.int32, "out", (rows, k))
+    _out(slots, torch.int32, "slots", (rows, k))
+    _check(load().topk_rows_slots_noalloc(_ptr(logits), logits.stride(0), _ptr(row_len), _ptr(row_req),
+                                          _ptr(block_table), block_table.stride(0), block_table.shape[0],
+                                          rows, k, _ptr(out), _ptr(slots), _stream()),
+           "topk_rows_slots_noalloc")
     return out, slots
 
 

@@ -14,6 +14,7 @@ extern "C" const char* sai_status_string(int status) {
     case SAI_EUNSUPPORTED: return "SAI_EUNSUPPORTED: unsupported shape";
     case SAI_EWORKSPACE: return "SAI_EWORKSPACE: workspace missing or too small";
     case SAI_ELAUNCH: return "SAI_ELAUNCH: kernel launch failed";
+    case SAI_ESCRATCH: return "SAI_ESCRATCH: problem needs more than the built-in scratch buffer";
     default: return "SAI: unknown status";
   }
 }

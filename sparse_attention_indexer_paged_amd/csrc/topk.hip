@@ -18,6 +18,7 @@
 // with an exact radix select as the fallback.  Rows too wide for the
 // segment-and-merge plan take topk_row_kernel, which streams the row from
 // L2 for each of three radix rounds (11, 11, 10 key bits).
+#include <atomic>
 #include <type_traits>
 
 #include "sai_device.h"
@@ -855,4 +856,61 @@ extern "C" int topk_rows_slots(const float* logits, int64_t logits_stride, const
   // rows too wide for the fused kernels: map the indices afterwards
   return topk_to_global_slots(out_idx, row_req, block_table, bt_stride, batch, rows, k, out_slots,
                               stream);
+}
+
+// ------------------------------------------------- allocation-free variant
+// topk_rows_slots_noalloc keeps the segment candidates of wide rows in this
+// file-scope device array instead of a caller workspace.  In host code the
+// name `scratch` is a host-side stand-in, not a device address: the address
+// is resolved per device with hipGetSymbolAddress (with that device
+// current) and only the resolved pointer is passed to kernels.  Each device
+// holds its own copy until the process ends; every call on a device shares
+// it, so calls that overlap on one device race.  The passes overwrite every
+// candidate slot they later read, so nothing needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[SAI_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream`, resolved on
+// the first call for that device (two threads racing here store the same
+// address).
+int scratch_for_stream(hipStream_t stream, void** out) {
+  int dev = -1, cur = -1;
+  if (hipStreamGetDevice(stream, &dev) != hipSuccess || hipGetDevice(&cur) != hipSuccess)
+    return SAI_ELAUNCH;
+  if (dev < 0 || dev >= kMaxDevices) return SAI_EUNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p == nullptr) {
+    if (dev != cur && hipSetDevice(dev) != hipSuccess) return SAI_ELAUNCH;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur && hipSetDevice(cur) != hipSuccess) return SAI_ELAUNCH;
+    if (e != hipSuccess || p == nullptr) return SAI_ELAUNCH;
+    g_scratch_ptr[dev].store(p, std::memory_order_release);
+  }
+  *out = p;
+  return SAI_OK;
+}
+
+}  // namespace
+
+extern "C" int topk_rows_slots_noalloc(const float* logits, int64_t logits_stride,
+                                       const int32_t* row_len, const int32_t* row_req,
+                                       const int32_t* block_table, int64_t bt_stride, int32_t batch,
+                                       int32_t rows, int32_t k, int32_t* out_idx, int32_t* out_slots,
+                                       hipStream_t stream) {
+  if (rows < 0 || batch < 0 || bt_stride < 0 || logits_stride < 0) return SAI_EINVAL;
+  if (k < 1 || k > SAI_TOPK_MAX) return SAI_EUNSUPPORTED;
+  if (rows == 0) return SAI_OK;
+  const size_t need = topk_workspace_bytes(rows, logits_stride, k);
+  if (need > (size_t)SAI_NOALLOC_SCRATCH_BYTES) return SAI_ESCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const int st = scratch_for_stream(stream, &ws);
+    if (st != SAI_OK) return st;
+  }
+  return topk_rows_slots(logits, logits_stride, row_len, row_req, block_table, bt_stride, batch, rows,
+                         k, out_idx, out_slots, ws, need, stream);
 }

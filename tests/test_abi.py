@@ -36,7 +36,8 @@ def test_header_declares_the_boundary():
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
         "gather_indexer_k",
         "paged_mqa_logits", "paged_mqa_logits_visible", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
-        "topk_to_global_slots", "topk_rows_slots", "mla_cache_write", "sparse_mla_workspace_bytes",
+        "topk_to_global_slots", "topk_rows_slots", "topk_rows_slots_noalloc", "mla_cache_write",
+        "sparse_mla_workspace_bytes",
         "sparse_mla_decode"])
 
 
@@ -101,6 +102,24 @@ def test_topk_rows_slots_host_validation(lib):
     assert lib.topk_rows_slots(fake, 256, fake, fake, fake, 4, 2, 3, 0, fake, fake, nul, 0, nul) == SAI_EUNSUPPORTED
     assert lib.topk_rows_slots(fake, 65536, fake, fake, fake, 4, 2, 3, 2048, fake, fake, nul, 0, nul) == SAI_EWORKSPACE
     assert lib.topk_rows_slots(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul, 0, nul) == SAI_OK
+
+
+def test_topk_rows_slots_noalloc_host_validation(lib):
+    """The allocation-free entry rejects problems past its built-in buffer
+    (16 MiB of segment candidates) and bad arguments before touching any
+    device."""
+    fake = ctypes.c_void_p(4096)
+    nul = ctypes.c_void_p(0)
+    f = lib.topk_rows_slots_noalloc
+    assert binding.topk_workspace_bytes(256, 65536, 2048) == 16 << 20
+    assert f(fake, 65536, fake, fake, fake, 1024, 256, 257, 2048, fake, fake, nul) == -5   # SAI_ESCRATCH
+    assert f(fake, 131072, fake, fake, fake, 2048, 32, 129, 2048, fake, fake, nul) == -5   # 128 fit
+    assert binding.status_string(-5).startswith("SAI_ESCRATCH")
+    assert f(fake, 65536, fake, fake, fake, 1024, 256, 3, 0, fake, fake, nul) == SAI_EUNSUPPORTED
+    assert f(fake, 65536, fake, fake, fake, 1024, 256, 3, 2049, fake, fake, nul) == SAI_EUNSUPPORTED
+    assert f(fake, 65536, fake, fake, fake, 1024, 256, -3, 2048, fake, fake, nul) == SAI_EINVAL
+    assert f(fake, -1, fake, fake, fake, 1024, 256, 3, 2048, fake, fake, nul) == SAI_EINVAL
+    assert f(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul) == SAI_OK
 
 
 def test_topk_missing_workspace_is_rejected(lib):
