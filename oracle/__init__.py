@@ -15,7 +15,8 @@ Pages:
     per-request context lengths, fp32 dequantisation, -inf "clean logits".
   * prhub summary of vLLM PR #47090 (FlashMLA FP8 KV cache + BF16 query),
     key source excerpt of ``_fused_norm_rope_kernel`` -> the amax/448 dynamic
-    fp8 quantiser with its FLT_MIN floor.
+    fp8 quantiser with its FLT_MIN floor, and the rotated pair (r1, r2)
+    stored at positions 2i, 2i + 1 (the fused producers' rotation).
   * ROCm/ATOM PR #1094 "Support DSv3.2 with sglang-ATOM plugin and sglang sparse
     MLA", Technical Details -> request-local top-k -> global paged KV indices,
     the 2-D top-k index buffer.
@@ -25,6 +26,7 @@ Parity status: every function here is pinned by tests/test_oracle_pins.py.
 from .indexer import (  # noqa: F401
     BLOCK, HEADS, DIM, BLOCK_BYTES, FLT_MIN, INV_448,
     e4m3fn_table, fp8_encode, quantize_rows, quantize_q,
+    rope_rotate, quantize_q_rope, k_rope_cache_write,
     k_cache_write, gather_indexer_k, paged_mqa_logits, mqa_logits, mqa_logits_chunked,
     topk_rows, topk_to_global_slots, decode_limits,
 )

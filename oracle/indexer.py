@@ -123,6 +123,91 @@ def quantize_q(q, w):
 
 
 # --------------------------------------------------------------------------
+# rotary position embedding (fused producers)
+# --------------------------------------------------------------------------
+def rope_rotate(x, positions, cos_table, sin_table, rope_dim):
+    """Rotate the first ``rope_dim`` values of every row of x by its token's
+    position, in float32.
+
+    The pages show the rotated pair being stored as ``r1`` at position 2i and
+    ``r2`` at position 2i + 1 (prhub summary of vLLM PR #47090, key source
+    excerpt of ``_fused_norm_rope_kernel``, MLA_CACHE_DS_MLA branch); they do
+    not print the rotation or its tables.  Reading taken: pair i of a row is
+    (x[2i], x[2i+1]) for 2i + 1 < rope_dim, the angle's cosine and sine are
+    row ``positions[t]`` of the caller's tables (column i), and
+        r1 = fl32(fl32(x1 * cos) - fl32(x2 * sin))
+        r2 = fl32(fl32(x2 * cos) + fl32(x1 * sin))
+    with every product and sum rounded to float32 on its own (no fused
+    multiply-add).  Values at or past rope_dim are unchanged.
+
+    x: float32 [T, ..., L] (the rotation acts on the last axis of every
+    row); positions: int [T]; cos_table, sin_table: float32 [P, rope_dim/2].
+    Returns float32 of x's shape.  The caller checks 0 <= positions < P.
+    """
+    x = np.array(x, dtype=np.float32, copy=True)
+    half = rope_dim // 2
+    if half == 0:
+        return x
+    pos = np.asarray(positions, dtype=np.int64)
+    c = np.asarray(cos_table, dtype=np.float32)[pos, :half]     # [T, half]
+    sn = np.asarray(sin_table, dtype=np.float32)[pos, :half]
+    shape = (x.shape[0],) + (1,) * (x.ndim - 2) + (half,)
+    c, sn = c.reshape(shape), sn.reshape(shape)
+    x1 = x[..., 0:2 * half:2].copy()
+    x2 = x[..., 1:2 * half:2].copy()
+    x[..., 0:2 * half:2] = (x1 * c).astype(np.float32) - (x2 * sn).astype(np.float32)
+    x[..., 1:2 * half:2] = (x2 * c).astype(np.float32) + (x1 * sn).astype(np.float32)
+    return x
+
+
+def quantize_q_rope(q, positions, cos_table, sin_table, rope_dim, w):
+    """Fused query producer: rotate the first rope_dim values of every head
+    of every query token (``rope_rotate``), then ``quantize_q``.
+
+    A token whose position is outside [0, P) gets NaN codes (0x7F), a NaN
+    scale and NaN folded weights (the library's signal for a caller error).
+    Returns (q_codes uint8 [T, H, D], w_eff float32 [T, H], q_scale float32 [T]).
+    """
+    q = np.asarray(q, dtype=np.float32)
+    pos = np.asarray(positions, dtype=np.int64)
+    P = np.asarray(cos_table).shape[0]
+    ok = (pos >= 0) & (pos < P)
+    rot = q.copy()
+    if ok.any():
+        rot[ok] = rope_rotate(q[ok], pos[ok], cos_table, sin_table, rope_dim)
+    codes, w_eff, scale = quantize_q(rot, w)
+    codes[~ok] = 0x7F
+    w_eff[~ok] = np.nan
+    scale[~ok] = np.nan
+    return codes, w_eff, scale
+
+
+def k_rope_cache_write(k, positions, cos_table, sin_table, rope_dim, slot_mapping, cache):
+    """Fused K producer: rotate the first rope_dim values of every K row
+    (``rope_rotate``), quantise it and store it in the paged indexer cache
+    (``k_cache_write``), in place.  A negative slot is skipped; a token whose
+    position is outside [0, P) is stored as NaN codes (0x7F) and a NaN scale.
+    """
+    k = np.asarray(k, dtype=np.float32)
+    pos = np.asarray(positions, dtype=np.int64)
+    P = np.asarray(cos_table).shape[0]
+    ok = (pos >= 0) & (pos < P)
+    rot = k.copy()
+    if ok.any():
+        rot[ok] = rope_rotate(k[ok], pos[ok], cos_table, sin_table, rope_dim)
+    k_cache_write(rot, slot_mapping, cache)
+    slots = np.asarray(slot_mapping, dtype=np.int64)
+    bad = (~ok) & (slots >= 0)
+    if bad.any():
+        blk, off = slots[bad] // BLOCK, slots[bad] % BLOCK
+        values = cache[:, :VALUE_BYTES].reshape(-1, BLOCK, DIM)
+        scales = cache[:, VALUE_BYTES:BLOCK_BYTES].view(np.float32)
+        values[blk, off] = 0x7F
+        scales[blk, off] = np.nan
+    return cache
+
+
+# --------------------------------------------------------------------------
 # paged cache
 # --------------------------------------------------------------------------
 def _block_values(cache, blk):
