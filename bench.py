@@ -27,7 +27,10 @@ Decode workloads add a second measured object, "sparse_mla_decode": sparse
 MLA decode (128 heads, fp8 MLA cache with the pool's block count) over the
 global slot ids the last indexer step produced, timed after the indexer's
 timed region with its own roofline (bf16 MFMA peak), and the oracle's decode
-on three sampled rows as its CPU baseline and parity check (--no-mla skips it).
+on three sampled rows as its CPU baseline and parity check (--no-mla skips it),
+and a third, "fused_producers": the rotary + fp8 quantiser + cache write (K)
+and rotary + quantiser + weight fold (q) kernels timed on their own with their
+HBM rooflines (--no-producers skips it).
 """
 import argparse
 import ctypes
@@ -429,6 +432,71 @@ def mla_cache_write_leg(torch, lib, cache, dev, ev, arm, s_ptr, n=65536, reps=10
                          "alg_bytes_per_launch": alg}}
 
 
+PRODUCER_ROPE_DIM = 64
+
+
+def producer_leg(torch, lib, dev, ev, arm, s_ptr, n_k=65536, n_q=4096, reps=10):
+    """The fused producers timed on their own (dispatch-carried events),
+    after the indexer's timed region, into a cache of their own: the K
+    writer rotates, quantises and scatters n_k bf16 K rows to random slots
+    of a 2048-block cache; the query producer rotates and quantises n_q query
+    rows and folds their scales into the head weights.  Both are byte movers:
+    HBM roofline on their algorithmic bytes (K: 256 B in, 8 B position, 8 B
+    slot, the position's cos and sin rows, 132 B out per token; q: 16 KB in,
+    8 B position, cos and sin rows, 256 B weights in, 8 KB codes + 256 B
+    folded weights + 4 B scale out per row)."""
+    g = torch.Generator(device=dev)
+    g.manual_seed(11)
+    half = PRODUCER_ROPE_DIM // 2
+    P = 1 << 17
+    f = 10000.0 ** (-2.0 * torch.arange(half, device=dev, dtype=torch.float64) / PRODUCER_ROPE_DIM)
+    ang = torch.arange(P, device=dev, dtype=torch.float64)[:, None] * f[None, :]
+    cos, sin = torch.cos(ang).float().contiguous(), torch.sin(ang).float().contiguous()
+    nb = 2048
+    cache = torch.zeros((nb, 8448), dtype=torch.uint8, device=dev)
+    k = torch.randn((n_k, 128), device=dev, generator=g).to(torch.bfloat16)
+    kpos = torch.randint(0, P, (n_k,), device=dev, generator=g)
+    slots = torch.randperm(nb * 64, device=dev, generator=g)[:n_k].to(torch.int64)
+    q = torch.randn((n_q, 64, 128), device=dev, generator=g).to(torch.bfloat16)
+    qpos = torch.randint(0, P, (n_q,), device=dev, generator=g)
+    w = torch.randn((n_q, 64), device=dev, generator=g).float()
+    qf = torch.empty((n_q, 64, 128), dtype=torch.uint8, device=dev)
+    weff = torch.empty((n_q, 64), dtype=torch.float32, device=dev)
+    qs = torch.empty((n_q,), dtype=torch.float32, device=dev)
+    P_ = lambda x: ctypes.c_void_p(x.data_ptr())  # noqa: E731
+
+    def kcall():
+        return lib.indexer_k_rope_cache_write(P_(k), k.stride(0), P_(kpos), P_(cos), P_(sin), P,
+                                              PRODUCER_ROPE_DIM, P_(slots), n_k, P_(cache), nb, s_ptr)
+
+    def qcall():
+        return lib.indexer_q_rope_quant(P_(q), P_(qpos), P_(cos), P_(sin), P, PRODUCER_ROPE_DIM, P_(w), n_q,
+                                        P_(qf), P_(weff), P_(qs), s_ptr)
+
+    res = {}
+    table_row = 2 * half * 4
+    for name, call, units, per in (("indexer_k_rope_cache_write", kcall, n_k, 256 + 8 + 8 + table_row + 132),
+                                   ("indexer_q_rope_quant", qcall, n_q,
+                                    16384 + 8 + table_row + 256 + 8192 + 256 + 4)):
+        for _ in range(2):
+            assert call() == 0
+        e0, e1 = ev.create(reps), ev.create(reps)
+        for i in range(reps):
+            arm(e0[i], e1[i])
+            assert call() == 0
+        torch.cuda.synchronize()
+        t = float(np.mean([ev.elapsed_ms(e0[i], e1[i]) for i in range(reps)])) * 1e-3
+        ev.destroy(e0 + e1)
+        alg = units * per
+        gbps = alg / t / 1e9
+        res[name] = {"units": units, "rope_dim": PRODUCER_ROPE_DIM, "avg_launch_us": round(t * 1e6, 3),
+                     "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                  "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                                  "alg_bytes_per_launch": alg}}
+    del cache, k, q
+    return res
+
+
 def mla_cpu_baseline(cache, q_nope, q_pe, slots, out, lse, sm_scale, min_seconds):
     """The oracle's sparse MLA decode on three sampled rows (their entries
     copied to the host), timed, and the GPU's out / lse on those rows checked
@@ -498,6 +566,8 @@ def main():
     ap.add_argument("--no-mla", action="store_true",
                     help="skip the sparse MLA decode leg over this step's slot ids")
     ap.add_argument("--mla-steps", type=int, default=50)
+    ap.add_argument("--no-producers", action="store_true",
+                    help="skip the fused-producer leg (rotary + fp8 quantiser + cache write / weight fold)")
     ap.add_argument("--profile-copy", action="store_true",
                     help="after timing, copy 256 MiB device-to-device once (a known-size "
                          "transfer that calibrates rocprofv3 FETCH_SIZE/WRITE_SIZE)")
@@ -630,6 +700,10 @@ def main():
         mla = mla_leg(torch, lib, wl, t["slots"], dev, args.mla_steps, ev, arm, s_ptr,
                       0.0 if args.no_cpu_baseline else min(args.cpu_seconds, 5.0))
 
+    producers = None
+    if not args.no_producers and not prefill:
+        producers = producer_leg(torch, lib, dev, ev, arm, s_ptr)
+
     if args.profile_copy:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device=dev).fill_(1)
         dst = torch.empty_like(src)
@@ -704,6 +778,7 @@ def main():
         "parity_sampled_rows": parity_ok,
         "cpu_baseline": cpu,
         "sparse_mla_decode": mla,
+        "fused_producers": producers,
     }
     print(json.dumps(out), flush=True)
 

@@ -106,6 +106,53 @@ int indexer_q_quant(const void* q_bf16, const float* weights, int64_t rows,
                     void* q_fp8, float* w_eff, float* q_scale, hipStream_t stream);
 
 /*
+ * Fused producers.  The rotary embedding, the fp8 quantiser and the write
+ * of its result in one kernel each: the indexer's analogue of the kernel
+ * that rotates, quantises and stores MLA cache rows in one pass
+ * (_fused_norm_rope_kernel, prhub summary of vLLM PR #47090, key source
+ * excerpt).  The pages show that kernel storing the rotated pair r1, r2 at
+ * positions 2i and 2i + 1 but print neither the rotation nor its tables;
+ * the reading this library takes: for a row with token position
+ * p = positions[t] and each pair i < rope_dim / 2,
+ *   x[2i]     <- fl32(fl32(x[2i] * cos[p][i]) - fl32(x[2i+1] * sin[p][i]))
+ *   x[2i + 1] <- fl32(fl32(x[2i+1] * cos[p][i]) + fl32(x[2i] * sin[p][i]))
+ * in float32 without fused multiply-add (so the codes are reproducible bit
+ * for bit); values at and past rope_dim are kept.  The quantiser then sees
+ * the rotated values.
+ *
+ *   positions             int64, one per K token / query row (device)
+ *   cos_table, sin_table  [table_rows, rope_dim / 2] fp32 (device); row p
+ *                         holds position p's angles
+ *   rope_dim              even, 0..128 (0: no rotation, the plain call)
+ * A position outside [0, table_rows) gives NaN: NaN codes (0x7F) and a NaN
+ * scale in the K cache, NaN codes, scale and folded weights for a query row
+ * (never an out-of-bounds read).  SAI_EINVAL for an odd or out-of-range
+ * rope_dim, a negative table_rows, or missing positions or tables when
+ * rope_dim > 0.
+ */
+
+/*
+ * indexer_k_rope_cache_write -- rotate the first rope_dim values of each K
+ * row, then indexer_k_cache_write's quantiser and layout.  Other arguments,
+ * skipping rules and errors as for indexer_k_cache_write.
+ */
+int indexer_k_rope_cache_write(const void* k_bf16, int64_t k_row_stride, const int64_t* positions,
+                               const float* cos_table, const float* sin_table, int64_t table_rows,
+                               int32_t rope_dim, const int64_t* slot_mapping, int64_t n,
+                               void* kv_cache, int64_t num_blocks, hipStream_t stream);
+
+/*
+ * indexer_q_rope_quant -- rotate the first rope_dim values of every head of
+ * each query row, then indexer_q_quant (one scale per token over all 64x128
+ * rotated values, folded into that token's head weights).  Other arguments
+ * and errors as for indexer_q_quant.
+ */
+int indexer_q_rope_quant(const void* q_bf16, const int64_t* positions, const float* cos_table,
+                         const float* sin_table, int64_t table_rows, int32_t rope_dim,
+                         const float* weights, int64_t rows, void* q_fp8, float* w_eff,
+                         float* q_scale, hipStream_t stream);
+
+/*
  * gather_indexer_k -- paged -> contiguous copy of K codes and scales for
  * prefill (vLLM PR #25869, review of cp_gather_indexer_k_quant_cache):
  * request b owns output rows [cu[b], cu[b+1]); token t < cu[b+1]-cu[b]

@@ -31,6 +31,10 @@ SIGNATURES = {
     "sai_time_next_launch": [_c_void_p, _c_void_p],
     "indexer_k_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
     "indexer_q_quant": [_c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
+    "indexer_k_rope_cache_write": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,
+                                   _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
+    "indexer_q_rope_quant": [_c_void_p, _c_void_p, _c_void_p, _c_void_p, _i64, _i32, _c_void_p, _i64,
+                             _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "gather_indexer_k": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32, _i64, _c_void_p,
                          _c_void_p, _c_void_p],
     "paged_mqa_logits": [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32,
@@ -146,6 +150,72 @@ def indexer_k_cache_write(k_bf16, slot_mapping, kv_cache):
                                         k_bf16.shape[0], _ptr(kv_cache), kv_cache.shape[0],
                                         _stream()), "indexer_k_cache_write")
     return kv_cache
+
+
+def _rope_tables(cos_table, sin_table, rope_dim):
+    _need(cos_table, torch.float32, "cos_table", 2)
+    _need(sin_table, torch.float32, "sin_table", 2)
+    if cos_table.shape != sin_table.shape:
+        raise ValueError("cos_table and sin_table must have the same shape [positions, rope_dim/2]")
+    rope_dim = 2 * cos_table.shape[1] if rope_dim is None else int(rope_dim)
+    if rope_dim > 2 * cos_table.shape[1]:
+        raise ValueError("the tables hold fewer than rope_dim/2 columns")
+    if cos_table.shape[1] != rope_dim // 2:
+        raise ValueError("the kernels index the tables with rope_dim/2 columns per row")
+    return rope_dim
+
+
+def indexer_k_rope_cache_write(k_bf16, positions, cos_table, sin_table, slot_mapping, kv_cache,
+                               rope_dim=None):
+    """Fused K producer: rotate the first rope_dim values of each K row [n, 128]
+    bf16 by its position (positions [n] int64; cos/sin tables [P, rope_dim/2]
+    fp32), quantise to fp8 and write into the paged cache in place.  K rows
+    may be strided (the C call takes the row stride)."""
+    _need_rows(k_bf16, torch.bfloat16, "k_bf16")
+    _need(positions, torch.int64, "positions", 1)
+    _need(slot_mapping, torch.int64, "slot_mapping", 1)
+    _need(kv_cache, torch.uint8, "kv_cache", 2)
+    rope_dim = _rope_tables(cos_table, sin_table, rope_dim)
+    n = k_bf16.shape[0]
+    if k_bf16.shape[1] != DIM or kv_cache.shape[1] != BLOCK_BYTES:
+        raise ValueError("k_bf16 must be [n,128] and kv_cache [num_blocks, 8448]")
+    if slot_mapping.shape[0] != n or positions.shape[0] != n:
+        raise ValueError("slot_mapping and positions need one entry per K row")
+    if n == 0:
+        return kv_cache
+    _check(load().indexer_k_rope_cache_write(_ptr(k_bf16), k_bf16.stride(0), _ptr(positions),
+                                             _ptr(cos_table), _ptr(sin_table), cos_table.shape[0],
+                                             rope_dim, _ptr(slot_mapping), n, _ptr(kv_cache),
+                                             kv_cache.shape[0], _stream()),
+           "indexer_k_rope_cache_write")
+    return kv_cache
+
+
+def indexer_q_rope_quant(q_bf16, positions, cos_table, sin_table, weights, rope_dim=None, q_fp8=None,
+                         w_eff=None, q_scale=None):
+    """Fused query producer: rotate the first rope_dim values of every head of
+    each query row q [T,64,128] bf16 by its position (positions [T] int64),
+    then quantise as indexer_q_quant -> (q_fp8, w_eff, q_scale)."""
+    _need(q_bf16, torch.bfloat16, "q_bf16", 3)
+    _need(positions, torch.int64, "positions", 1)
+    _need(weights, torch.float32, "weights", 2)
+    rope_dim = _rope_tables(cos_table, sin_table, rope_dim)
+    T = q_bf16.shape[0]
+    if tuple(q_bf16.shape[1:]) != (HEADS, DIM) or tuple(weights.shape) != (T, HEADS):
+        raise ValueError("q_bf16 must be [T,64,128] and weights [T,64]")
+    if positions.shape[0] != T:
+        raise ValueError("positions needs one entry per query row")
+    dev = q_bf16.device
+    q_fp8 = torch.empty((T, HEADS, DIM), dtype=torch.uint8, device=dev) if q_fp8 is None else q_fp8
+    w_eff = torch.empty((T, HEADS), dtype=torch.float32, device=dev) if w_eff is None else w_eff
+    q_scale = torch.empty((T,), dtype=torch.float32, device=dev) if q_scale is None else q_scale
+    _out(q_fp8, torch.uint8, "q_fp8", (T, HEADS, DIM))
+    _out(w_eff, torch.float32, "w_eff", (T, HEADS))
+    _out(q_scale, torch.float32, "q_scale", (T,))
+    _check(load().indexer_q_rope_quant(_ptr(q_bf16), _ptr(positions), _ptr(cos_table), _ptr(sin_table),
+                                       cos_table.shape[0], rope_dim, _ptr(weights), T, _ptr(q_fp8),
+                                       _ptr(w_eff), _ptr(q_scale), _stream()), "indexer_q_rope_quant")
+    return q_fp8, w_eff, q_scale
 
 
 MLA_ENTRY_BYTES = 656

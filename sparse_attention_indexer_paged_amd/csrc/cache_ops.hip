@@ -31,20 +31,48 @@ static inline int launch_status() {
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
 
+// ---------------------------------------------------------------- rotation
+// Rotates the pair (x1, x2) by the angle whose cosine and sine are (c, s):
+// r1 = x1 c - x2 s, r2 = x2 c + x1 s, every product and sum rounded to
+// float32 on its own (no fused multiply-add), so the codes the quantiser
+// makes of the result are reproducible bit for bit.
+__device__ __forceinline__ void rope_pair(float& x1, float& x2, float c, float s) {
+#pragma clang fp contract(off)
+  const float a = x1 * c, b = x2 * s, d = x2 * c, e = x1 * s;
+  x1 = a - b;
+  x2 = d + e;
+}
+
+// Rotary tables of the fused producers: cos/sin [rows, half] fp32, row p =
+// token position p; pair j of a row (values 2j, 2j + 1) uses column j.
+struct Rope {
+  const int64_t* pos;
+  const float* cos_t;
+  const float* sin_t;
+  int64_t rows;
+  int half;  // rope_dim / 2
+};
+
 // ---------------------------------------------------------------- K1
-// 16 lanes per token row: lane i of the group holds values [8i, 8i+8).
-// One 256-thread workgroup writes 16 tokens.
+// 16 lanes per token row: lane i of the group holds values [8i, 8i+8), i.e.
+// rotary pairs 4i .. 4i+3.  One 256-thread workgroup writes 16 tokens.
+// With ROPE the first 2*half values are rotated by the token's position
+// before the quantiser sees them; a position outside the table writes NaN
+// codes and a NaN scale.
+template <bool ROPE>
 __global__ __launch_bounds__(256) void k_cache_write_kernel(
     const uint16_t* __restrict__ k, int64_t row_stride, const int64_t* __restrict__ slots,
-    int64_t n, uint8_t* __restrict__ cache, int64_t num_blocks) {
+    int64_t n, uint8_t* __restrict__ cache, int64_t num_blocks, Rope rope) {
   const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
   const int sub = threadIdx.x & 15;
   const bool live = tok < n;
   uint4 raw = make_uint4(0, 0, 0, 0);
   int64_t slot = -1;
+  int64_t p = 0;
   if (live) {
     raw = *reinterpret_cast<const uint4*>(k + tok * row_stride + sub * 8);
     slot = slots[tok];
+    if (ROPE) p = rope.pos[tok];
   }
   float x[8];
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
@@ -53,17 +81,33 @@ __global__ __launch_bounds__(256) void k_cache_write_kernel(
     x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
     x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
   }
+  bool pos_ok = true;
+  if constexpr (ROPE) {
+    pos_ok = p >= 0 && p < rope.rows;
+    if (live && pos_ok) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int j = 4 * sub + i;
+        if (j < rope.half)
+          rope_pair(x[2 * i], x[2 * i + 1], rope.cos_t[p * rope.half + j], rope.sin_t[p * rope.half + j]);
+      }
+    }
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
-  const float scale = fp8_scale(amax);
+  float scale = fp8_scale(amax);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
   for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(x[i] / scale) << (8 * i);
 #pragma unroll
   for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(x[4 + i] / scale) << (8 * i);
+  if (!pos_ok) {
+    lo = hi = 0x7F7F7F7Fu;
+    scale = __uint_as_float(0x7FC00000u);
+  }
   if (!live || slot < 0 || slot >= num_blocks * kBlock) return;
   uint8_t* blk = cache + (slot / kBlock) * kBlockBytes;
   const int off = (int)(slot % kBlock);
@@ -81,18 +125,58 @@ extern "C" int indexer_k_cache_write(const void* k_bf16, int64_t k_row_stride,
     return SAI_EINVAL;
   const int64_t grid = (n + 15) / 16;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  launch(k_cache_write_kernel, dim3((unsigned)grid), dim3(256), 0, stream,
-                     (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n,
-                     (uint8_t*)kv_cache, num_blocks);
+  launch(k_cache_write_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+         (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n, (uint8_t*)kv_cache, num_blocks,
+         Rope{nullptr, nullptr, nullptr, 0, 0});
+  return launch_status();
+}
+
+// Host checks shared by the two fused producers: rope_dim even in [0, 128];
+// tables and positions present when something is rotated.
+static int check_rope(const int64_t* positions, const float* cos_t, const float* sin_t,
+                      int64_t table_rows, int32_t rope_dim) {
+  if (rope_dim < 0 || rope_dim > kDim || (rope_dim & 1) || table_rows < 0) return SAI_EINVAL;
+  if (rope_dim > 0 && (!positions || !cos_t || !sin_t)) return SAI_EINVAL;
+  if (table_rows > (int64_t)1 << 40) return SAI_EUNSUPPORTED;
+  return SAI_OK;
+}
+
+extern "C" int indexer_k_rope_cache_write(const void* k_bf16, int64_t k_row_stride,
+                                          const int64_t* positions, const float* cos_table,
+                                          const float* sin_table, int64_t table_rows,
+                                          int32_t rope_dim, const int64_t* slot_mapping, int64_t n,
+                                          void* kv_cache, int64_t num_blocks, hipStream_t stream) {
+  if (n < 0 || num_blocks < 0) return SAI_EINVAL;
+  const int rc = check_rope(positions, cos_table, sin_table, table_rows, rope_dim);
+  if (rc != SAI_OK) return rc;
+  if (n == 0) return SAI_OK;
+  if (k_row_stride < kDim || (k_row_stride & 7)) return SAI_EINVAL;
+  if (!k_bf16 || !slot_mapping || !kv_cache || !aligned16(k_bf16) || !aligned16(kv_cache))
+    return SAI_EINVAL;
+  const int64_t grid = (n + 15) / 16;
+  if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  if (rope_dim == 0)
+    launch(k_cache_write_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+           (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n, (uint8_t*)kv_cache, num_blocks,
+           Rope{nullptr, nullptr, nullptr, 0, 0});
+  else
+    launch(k_cache_write_kernel<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+           (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n, (uint8_t*)kv_cache, num_blocks,
+           Rope{positions, cos_table, sin_table, table_rows, rope_dim / 2});
   return launch_status();
 }
 
 // ---------------------------------------------------------------- q producer
 // One 256-thread workgroup per query token (64 heads x 128 = 8192 values):
-// thread t owns values [32t, 32t+32) as four 16-byte loads.
+// thread t owns values [32t, 32t+32) as four 16-byte loads, i.e. head t/4,
+// in-head values 32 (t % 4) .. +31 (rotary pairs 16 (t % 4) .. +15).  With
+// ROPE every head's first 2*half values are rotated by the token's position
+// before the token's scale is taken; a position outside the table gives
+// NaN codes, scale and weights.
+template <bool ROPE>
 __global__ __launch_bounds__(256) void q_quant_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ wts, uint8_t* __restrict__ q8,
-    float* __restrict__ w_eff, float* __restrict__ q_scale) {
+    float* __restrict__ w_eff, float* __restrict__ q_scale, Rope rope) {
   __shared__ float s_amax[4];
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
@@ -108,6 +192,19 @@ __global__ __launch_bounds__(256) void q_quant_kernel(
       x[v * 8 + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   }
+  bool pos_ok = true;
+  if constexpr (ROPE) {
+    const int64_t p = rope.pos[row];
+    pos_ok = p >= 0 && p < rope.rows;
+    if (pos_ok) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int j = 16 * (t & 3) + i;
+        if (j < rope.half)
+          rope_pair(x[2 * i], x[2 * i + 1], rope.cos_t[p * rope.half + j], rope.sin_t[p * rope.half + j]);
+      }
+    }
+  }
   float amax = 0.0f;
 #pragma unroll
   for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(x[i]));
@@ -115,15 +212,16 @@ __global__ __launch_bounds__(256) void q_quant_kernel(
   if ((t & 63) == 0) s_amax[t >> 6] = amax;
   __syncthreads();
   amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
-  const float scale = fp8_scale(amax);
+  float scale = fp8_scale(amax);
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    uint32_t p = 0;
+    uint32_t pk = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) p |= f32_to_e4m3fn(x[4 * i + j] / scale) << (8 * j);
-    packed[i] = p;
+    for (int j = 0; j < 4; ++j) pk |= f32_to_e4m3fn(x[4 * i + j] / scale) << (8 * j);
+    packed[i] = pos_ok ? pk : 0x7F7F7F7Fu;
   }
+  if (!pos_ok) scale = __uint_as_float(0x7FC00000u);
   uint8_t* dst = q8 + row * (kHeads * kDim) + t * 32;
   *reinterpret_cast<uint4*>(dst) = make_uint4(packed[0], packed[1], packed[2], packed[3]);
   *reinterpret_cast<uint4*>(dst + 16) = make_uint4(packed[4], packed[5], packed[6], packed[7]);
@@ -138,8 +236,32 @@ extern "C" int indexer_q_quant(const void* q_bf16, const float* weights, int64_t
   if (!q_bf16 || !weights || !q_fp8 || !w_eff || !aligned16(q_bf16) || !aligned16(q_fp8))
     return SAI_EINVAL;
   if (rows > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
-  launch(q_quant_kernel, dim3((unsigned)rows), dim3(256), 0, stream,
-                     (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale);
+  launch(q_quant_kernel<false>, dim3((unsigned)rows), dim3(256), 0, stream,
+         (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale,
+         Rope{nullptr, nullptr, nullptr, 0, 0});
+  return launch_status();
+}
+
+extern "C" int indexer_q_rope_quant(const void* q_bf16, const int64_t* positions,
+                                    const float* cos_table, const float* sin_table,
+                                    int64_t table_rows, int32_t rope_dim, const float* weights,
+                                    int64_t rows, void* q_fp8, float* w_eff, float* q_scale,
+                                    hipStream_t stream) {
+  if (rows < 0) return SAI_EINVAL;
+  const int rc = check_rope(positions, cos_table, sin_table, table_rows, rope_dim);
+  if (rc != SAI_OK) return rc;
+  if (rows == 0) return SAI_OK;
+  if (!q_bf16 || !weights || !q_fp8 || !w_eff || !aligned16(q_bf16) || !aligned16(q_fp8))
+    return SAI_EINVAL;
+  if (rows > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
+  if (rope_dim == 0)
+    launch(q_quant_kernel<false>, dim3((unsigned)rows), dim3(256), 0, stream,
+           (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale,
+           Rope{nullptr, nullptr, nullptr, 0, 0});
+  else
+    launch(q_quant_kernel<true>, dim3((unsigned)rows), dim3(256), 0, stream,
+           (const uint16_t*)q_bf16, weights, (uint8_t*)q_fp8, w_eff, q_scale,
+           Rope{positions, cos_table, sin_table, table_rows, rope_dim / 2});
   return launch_status();
 }
 

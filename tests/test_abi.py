@@ -34,6 +34,7 @@ def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted([
         "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
+        "indexer_k_rope_cache_write", "indexer_q_rope_quant",
         "gather_indexer_k",
         "paged_mqa_logits", "paged_mqa_logits_visible", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
         "topk_to_global_slots", "topk_rows_slots", "topk_rows_slots_noalloc", "mla_cache_write",
@@ -120,6 +121,24 @@ def test_topk_rows_slots_noalloc_host_validation(lib):
     assert f(fake, 65536, fake, fake, fake, 1024, 256, -3, 2048, fake, fake, nul) == SAI_EINVAL
     assert f(fake, -1, fake, fake, fake, 1024, 256, 3, 2048, fake, fake, nul) == SAI_EINVAL
     assert f(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul) == SAI_OK
+
+
+def test_fused_producer_host_checks(lib):
+    """rope_dim must be even and at most 128, tables and positions present
+    when rotating; no device work."""
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    k = lib.indexer_k_rope_cache_write
+    assert k(fake, 128, fake, fake, fake, 10, 63, fake, 3, fake, 4, nul) == SAI_EINVAL    # odd
+    assert k(fake, 128, fake, fake, fake, 10, 130, fake, 3, fake, 4, nul) == SAI_EINVAL   # > 128
+    assert k(fake, 128, nul, fake, fake, 10, 64, fake, 3, fake, 4, nul) == SAI_EINVAL     # positions
+    assert k(fake, 128, fake, nul, fake, 10, 64, fake, 3, fake, 4, nul) == SAI_EINVAL     # cos
+    assert k(fake, 128, fake, fake, fake, -1, 64, fake, 3, fake, 4, nul) == SAI_EINVAL    # table rows
+    assert k(fake, 100, fake, fake, fake, 10, 64, fake, 3, fake, 4, nul) == SAI_EINVAL    # stride
+    assert k(fake, 128, fake, fake, fake, 10, 64, fake, 0, fake, 4, nul) == SAI_OK        # n == 0
+    q = lib.indexer_q_rope_quant
+    assert q(fake, fake, fake, fake, 10, 3, fake, 2, fake, fake, fake, nul) == SAI_EINVAL
+    assert q(fake, fake, fake, nul, 10, 64, fake, 2, fake, fake, fake, nul) == SAI_EINVAL
+    assert q(fake, fake, fake, fake, 10, 64, fake, 0, fake, fake, fake, nul) == SAI_OK
 
 
 def test_topk_missing_workspace_is_rejected(lib):
