@@ -14,7 +14,7 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(HERE, "libsai.so")
 
-SOURCES = ["cache_ops.hip", "logits.hip", "topk.hip", "mla.hip"]
+SOURCES = ["cache_ops.hip", "logits.hip", "prefill.hip", "topk.hip", "mla.hip"]
 OBJDIR = os.path.join(HERE, "_build")
 
 FLAGS = [
@@ -34,6 +34,7 @@ FLAGS = [
 # copies).
 PER_FILE = {
     "logits.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
+    "prefill.hip": ["-fno-honor-nans", "-mllvm", "-amdgpu-mfma-vgpr-form"],
 }
 
 
