@@ -21,7 +21,9 @@ against the CPU oracle on sampled rows, the oracle's own throughput on
 the host cores (cpu_baseline), and two reference points taken after the
 timed region: the bandwidth of a plain 1 GiB device copy on the same box and
 the dominant kernel's time when it re-reads one pool (hot_dominant_us, much
-of its K then comes from the memory-side cache).
+of its K then comes from the memory-side cache).  "topk" gives the top-k
+entry's time on the same timed steps (a sai_time_span pair from its first
+kernel's start to its last kernel's end) with its HBM roofline.
 
 Decode workloads add a second measured object, "sparse_mla_decode": sparse
 MLA decode (128 heads, fp8 MLA cache with the pool's block count) over the
@@ -226,7 +228,7 @@ def decode_pipeline(torch, sai, lib, wl, dev, npools, visible=False):
     alg_bytes = k_bytes + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW) + int(written.sum()) * 4
     lim = np.repeat(ctx_np, nn) - nn + np.tile(np.arange(nn), wl.batch) + 1
     flops = float(np.clip(lim, 0, None).sum()) * 64 * 128 * 2
-    return t, launches, 0, dict(bound="hbm", alg_bytes=alg_bytes, k_bytes=k_bytes, flops=flops)
+    return t, launches, 0, dict(bound="hbm", alg_bytes=alg_bytes, k_bytes=k_bytes, flops=flops, row_len=lim)
 
 
 def prefill_limits(wl):
@@ -277,7 +279,8 @@ def prefill_pipeline(torch, sai, lib, wl, dev, npools):
         ]
     flops = float(prefill_limits(wl).sum()) * 64 * 128 * 2
     alg_bytes = total * 132 + rows * (Q_BYTES_PER_ROW + W_BYTES_PER_ROW + width * 4)
-    return t, launches, 1, dict(bound="mfma", alg_bytes=alg_bytes, k_bytes=total * 132, flops=flops)
+    return t, launches, 1, dict(bound="mfma", alg_bytes=alg_bytes, k_bytes=total * 132, flops=flops,
+                                row_len=prefill_limits(wl))
 
 
 def cpu_baseline_prefill(wl, gpu_logits, min_seconds, nrows=64):
@@ -620,7 +623,13 @@ def main():
     arm = lib.sai_time_next_launch
     before = [fn for _, fn in calls[:dom]]
     dom_fn = calls[dom][1]
-    after = [fn for _, fn in calls[dom + 1:]]
+    # the top-k entry (one or two kernels) is timed on the same steps with a
+    # span: its first kernel's start to its last kernel's end
+    tk = [j for j, (name, _) in enumerate(calls) if name == "topk_rows_slots"][0]
+    after = [(j == tk, fn) for j, (_, fn) in enumerate(calls) if j > dom]
+    k0, k1 = ev.create(len(timed)), ev.create(len(timed))
+    span = lib.sai_time_span
+    nul = ctypes.c_void_p(0)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
@@ -629,14 +638,22 @@ def main():
         if i % every == 0:
             arm(e0[i // every], e1[i // every])
             dom_fn(i)
+            for is_tk, fn in after:
+                if is_tk:
+                    span(k0[i // every], k1[i // every])
+                    fn(i)
+                    span(nul, nul)
+                else:
+                    fn(i)
         else:
             dom_fn(i)
-        for fn in after:
-            fn(i)
+            for _, fn in after:
+                fn(i)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     t_dom = np.array([ev.elapsed_ms(e0[j], e1[j]) for j in range(len(timed))])
-    ev.destroy(e0 + e1)
+    t_tk = np.array([ev.elapsed_ms(k0[j], k1[j]) for j in range(len(timed))])
+    ev.destroy(e0 + e1 + k0 + k1)
 
     # hipGraph replay of the same step (reported alongside; not the headline value)
     graph_ms = None
@@ -726,6 +743,19 @@ def main():
     roof.update({"kernel": dom_name, "alg_bytes_per_launch": work["alg_bytes"],
                  "flops_per_launch": work["flops"], "avg_launch_us": round(t_dom_s * 1e6, 3)})
 
+    # top-k entry: algorithmic bytes = each row's visible logits read, its
+    # length and request read, the k indices and k slot ids written, and the
+    # block-table entries of its visible keys
+    vis = np.minimum(np.clip(work["row_len"], 0, None), width)
+    tk_bytes = int(vis.sum()) * 4 + rows * 8 + rows * 2048 * 8 + int(((vis + 63) // 64).sum()) * 4
+    tk_s = float(t_tk.mean()) * 1e-3
+    tk_gbps = tk_bytes / tk_s / 1e9
+    topk = {"entry": "topk_rows_slots", "avg_us": round(tk_s * 1e6, 3),
+            "us_p10_p50_p90": [round(float(np.percentile(t_tk, p)) * 1e3, 3) for p in (10, 50, 90)],
+            "roofline": {"bound": "hbm", "achieved": round(tk_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(tk_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "alg_bytes_per_launch": tk_bytes}}
+
     ms_per_step = elapsed * 1e3 / K
     value = rows * K / elapsed
 
@@ -777,6 +807,7 @@ def main():
         "graph_ms_per_step": None if graph_ms is None else round(graph_ms, 5),
         "parity_sampled_rows": parity_ok,
         "cpu_baseline": cpu,
+        "topk": topk,
         "sparse_mla_decode": mla,
         "fused_producers": producers,
     }

@@ -15,6 +15,14 @@
  * calls, and it changes no result.  No device work.
  *
  * Returns SAI_OK, or SAI_EINVAL if exactly one event is NULL.
+ *
+ * sai_time_span arms a pair that spans several kernels: the next launch
+ * carries start, and every launch until the thread disarms the span (both
+ * NULL, here or through sai_time_next_launch) carries stop, so after
+ * arm -> calls -> disarm, hipEventElapsedTime(start, stop) runs from the
+ * first kernel's start to the last kernel's end, gaps between them
+ * included (the way to time an entry point that launches several
+ * kernels).  Same per-thread state and return codes as above.
  */
 #ifndef SAI_PROFILE_H
 #define SAI_PROFILE_H
@@ -26,6 +34,7 @@ extern "C" {
 #endif
 
 int sai_time_next_launch(hipEvent_t start, hipEvent_t stop);
+int sai_time_span(hipEvent_t start, hipEvent_t stop);
 
 #ifdef __cplusplus
 }

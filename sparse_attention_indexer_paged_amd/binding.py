@@ -29,6 +29,7 @@ _i64 = ctypes.c_int64
 SIGNATURES = {
     "sai_status_string": [ctypes.c_int],
     "sai_time_next_launch": [_c_void_p, _c_void_p],
+    "sai_time_span": [_c_void_p, _c_void_p],
     "indexer_k_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p],
     "indexer_q_quant": [_c_void_p, _c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _c_void_p],
     "indexer_k_rope_cache_write": [_c_void_p, _i64, _c_void_p, _c_void_p, _c_void_p, _i64, _i32,

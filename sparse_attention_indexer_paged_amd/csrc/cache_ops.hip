@@ -21,7 +21,13 @@ extern "C" const char* sai_status_string(int status) {
 
 extern "C" int sai_time_next_launch(hipEvent_t start, hipEvent_t stop) {
   if ((start == nullptr) != (stop == nullptr)) return SAI_EINVAL;
-  g_launch_timing = LaunchTiming{start, stop};
+  g_launch_timing = LaunchTiming{start, stop, false};
+  return SAI_OK;
+}
+
+extern "C" int sai_time_span(hipEvent_t start, hipEvent_t stop) {
+  if ((start == nullptr) != (stop == nullptr)) return SAI_EINVAL;
+  g_launch_timing = LaunchTiming{start, stop, start != nullptr};
   return SAI_OK;
 }
 

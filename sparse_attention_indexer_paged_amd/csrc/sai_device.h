@@ -105,17 +105,23 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int* scratch, int* to
 // start/stop event pair (sai_time_next_launch), its next launch carries the
 // pair in its own dispatch, so their elapsed time is that kernel's execution
 // alone; a separate hipEventRecord would add marker packets to the stream.
+// A span (sai_time_span) stays armed until the caller disarms it: its first
+// launch carries start and every launch carries stop, so the pair ends with
+// the last kernel of the calls made meanwhile.
 struct LaunchTiming {
   hipEvent_t start = nullptr;
   hipEvent_t stop = nullptr;
+  bool span = false;
 };
 inline thread_local LaunchTiming g_launch_timing;
 
 template <typename F, typename... Args>
 inline void launch(F kernel, dim3 grid, dim3 block, uint32_t lds, hipStream_t s, Args... args) {
-  const LaunchTiming t = g_launch_timing;
-  g_launch_timing = LaunchTiming{};
-  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, t.start, t.stop, 0u, args...);
+  LaunchTiming& t = g_launch_timing;
+  const hipEvent_t start = t.start, stop = t.stop;
+  if (t.span) t.start = nullptr;
+  else t = LaunchTiming{};
+  hipExtLaunchKernelGGL(kernel, grid, block, lds, s, start, stop, 0u, args...);
 }
 
 }  // namespace sai

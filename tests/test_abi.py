@@ -33,7 +33,7 @@ def lib():
 def test_header_declares_the_boundary():
     names = declared_functions()
     assert names == sorted([
-        "sai_status_string", "sai_time_next_launch", "indexer_k_cache_write", "indexer_q_quant",
+        "sai_status_string", "sai_time_next_launch", "sai_time_span", "indexer_k_cache_write", "indexer_q_quant",
         "indexer_k_rope_cache_write", "indexer_q_rope_quant",
         "gather_indexer_k",
         "paged_mqa_logits", "paged_mqa_logits_visible", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
@@ -154,6 +154,9 @@ def test_time_next_launch_host_checks(lib):
     assert lib.sai_time_next_launch(fake, nul) == SAI_EINVAL
     assert lib.sai_time_next_launch(nul, fake) == SAI_EINVAL
     assert lib.sai_time_next_launch(nul, nul) == SAI_OK
+    assert lib.sai_time_span(fake, nul) == SAI_EINVAL
+    assert lib.sai_time_span(nul, fake) == SAI_EINVAL
+    assert lib.sai_time_span(nul, nul) == SAI_OK
 
 
 def test_mla_cache_write_host_checks(lib):
