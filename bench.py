@@ -55,6 +55,17 @@ Q_BYTES_PER_ROW = 64 * 128       # fp8 query codes
 W_BYTES_PER_ROW = 64 * 4         # fp32 head weights
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_counters.txt")
 MLA_PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_mla_decode_b64_h128_counters.txt")
+# committed PMC traffic summaries per (workload, kernel), each keyed by the
+# hash of the sources the kernel is built from
+DECODE_SOURCES = ("logits.hip", "score_mfma.h", "sai_device.h")
+PREFILL_SOURCES = ("prefill.hip", "score_mfma.h", "sai_device.h")
+TOPK_SOURCES = ("topk.hip", "sai_device.h")
+MLA_SOURCES = ("mla.hip", "sai_device.h")
+PREFILL_COUNTERS = {"prefill_8192": os.path.join(ROOT, "profiles", "mqa_logits_prefill_8192_counters.txt")}
+TOPK_COUNTERS = {
+    "decode_b64_ctx4k-16k": os.path.join(ROOT, "profiles", "topk_rows_slots_decode_b64_counters.txt"),
+    "prefill_8192": os.path.join(ROOT, "profiles", "topk_rows_slots_prefill_8192_counters.txt"),
+}
 COPY_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
 GRAPH_STEPS = 8                  # steps captured per hipGraph for graph_ms_per_step
@@ -96,12 +107,12 @@ class HipEvents:
             self.hip.hipEventDestroy(e)
 
 
-def kernel_source_hash(files=("logits.hip", "sai_device.h")):
+def kernel_source_hash(files=DECODE_SOURCES):
     from sparse_attention_indexer_paged_amd.profile_summary import source_hash
     return source_hash(files)
 
 
-def counter_traffic(path=PROFILE_COUNTERS, files=("logits.hip", "sai_device.h")):
+def counter_traffic(path=PROFILE_COUNTERS, files=DECODE_SOURCES):
     """HBM bytes per launch of a kernel from a committed rocprofv3 PMC
     summary, or None if absent or taken on different kernel source."""
     if not os.path.exists(path):
@@ -388,7 +399,7 @@ def mla_leg(torch, lib, wl, slots, dev, steps, ev, arm, s_ptr, cpu_seconds):
         "splits_workspace_bytes": ws_bytes,
         "roofline": {"bound": "mfma", "achieved": round(achieved, 1), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(achieved / BF16_PEAK_TFLOPS, 4),
-                     "traffic": (counter_traffic(MLA_PROFILE_COUNTERS, ("mla.hip", "sai_device.h"))
+                     "traffic": (counter_traffic(MLA_PROFILE_COUNTERS, MLA_SOURCES)
                                  if wl.name.startswith("decode_b64") else None),
                      "flops_per_launch": flops, "alg_bytes_per_launch": alg_bytes,
                      "alg_gbps": round(alg_bytes / t_kernel / 1e9, 1)},
@@ -738,8 +749,10 @@ def main():
                 "traffic": counter_traffic() if args.config == 1 and not args.visible_logits else None}
     else:
         achieved = work["flops"] / t_dom_s / 1e12
+        pf = PREFILL_COUNTERS.get(wl.name)
         roof = {"bound": "mfma", "achieved": round(achieved, 1), "peak": FP8_PEAK_TFLOPS,
-                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4), "traffic": None}
+                "unit": "TFLOP/s", "frac": round(achieved / FP8_PEAK_TFLOPS, 4),
+                "traffic": counter_traffic(pf, PREFILL_SOURCES) if pf else None}
     roof.update({"kernel": dom_name, "alg_bytes_per_launch": work["alg_bytes"],
                  "flops_per_launch": work["flops"], "avg_launch_us": round(t_dom_s * 1e6, 3)})
 
@@ -753,7 +766,9 @@ def main():
     topk = {"entry": "topk_rows_slots", "avg_us": round(tk_s * 1e6, 3),
             "us_p10_p50_p90": [round(float(np.percentile(t_tk, p)) * 1e3, 3) for p in (10, 50, 90)],
             "roofline": {"bound": "hbm", "achieved": round(tk_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
-                         "frac": round(tk_gbps / HBM_PEAK_GBPS, 4), "traffic": None,
+                         "frac": round(tk_gbps / HBM_PEAK_GBPS, 4),
+                         "traffic": (counter_traffic(TOPK_COUNTERS[wl.name], TOPK_SOURCES)
+                                     if wl.name in TOPK_COUNTERS and not args.visible_logits else None),
                          "alg_bytes_per_launch": tk_bytes}}
 
     ms_per_step = elapsed * 1e3 / K

@@ -5,8 +5,11 @@
   HBM traffic:    python -m sparse_attention_indexer_paged_amd.profile_summary traffic \\
                       --fetch <fetch ..._counter_collection.csv> --write <write ..._counter_collection.csv> \\
                       --kernel paged_logits_kernel --copy-bytes 268435456 \\
-                      [--sources logits.hip,sai_device.h] \\
+                      [--sources logits.hip,score_mfma.h,sai_device.h] \\
                       --command "<both rocprofv3 commands>" --out <txt>
+  counters:       python -m sparse_attention_indexer_paged_amd.profile_summary counters \\
+                      --csv <..._counter_collection.csv> --kernel prefill_logits_kernel \\
+                      --command "<rocprofv3 command>" --out <txt>
 
 FETCH_SIZE / WRITE_SIZE are in KiB per dispatch.  They are scaled by what the
 same counters read for a plain device-to-device copy of --copy-bytes bytes
@@ -87,6 +90,50 @@ def traffic(args):
     print("\n".join(lines))
 
 
+def counters(args):
+    """Per-dispatch means of every counter collected for one kernel, with
+    derived ratios when their counters are present: non-MFMA VALU
+    instructions per MFMA (SQ_INSTS_VALU counts MFMAs too), the clock
+    (GRBM_GUI_ACTIVE summed over the XCDs, over the dispatch duration), and
+    the share of the SIMDs' cycles the MFMA pipe was busy."""
+    disp = {}
+    dur = {}
+    name = None
+    for row in csv.DictReader(open(args.csv)):
+        if args.kernel not in row["Kernel_Name"]:
+            continue
+        name = row["Kernel_Name"]
+        key = row["Dispatch_Id"]
+        d = disp.setdefault(key, {})
+        d[row["Counter_Name"]] = d.get(row["Counter_Name"], 0.0) + float(row["Counter_Value"])
+        if row.get("Start_Timestamp") and row.get("End_Timestamp"):
+            dur[key] = (float(row["End_Timestamp"]) - float(row["Start_Timestamp"])) * 1e-9
+    if not disp:
+        raise SystemExit(f"no dispatch of {args.kernel!r}")
+    names = sorted({c for d in disp.values() for c in d})
+    mean = {c: statistics.mean(d[c] for d in disp.values() if c in d) for c in names}
+    lines = [f"# rocprofv3 counters of {name} (mean per dispatch over {len(disp)} dispatches)",
+             f"command: {args.command}"]
+    lines += [f"{c}: {mean[c]:.0f}" for c in names]
+    if dur:
+        lines.append(f"dispatch_duration_us (under the counter run): {statistics.mean(dur.values()) * 1e6:.1f}")
+    if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean and mean["SQ_INSTS_MFMA"] > 0:
+        lines.append(f"non_mfma_valu_per_mfma: {(mean['SQ_INSTS_VALU'] - mean['SQ_INSTS_MFMA']) / mean['SQ_INSTS_MFMA']:.2f}")
+    if "GRBM_GUI_ACTIVE" in mean:
+        cyc = mean["GRBM_GUI_ACTIVE"] / args.xcds
+        lines.append(f"gpu_cycles_per_xcd: {cyc:.0f}")
+        if dur:
+            lines.append(f"clock_ghz: {cyc / statistics.mean(dur.values()) / 1e9:.2f}")
+        simds = args.cus * 4
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in mean:
+            lines.append(f"mfma_busy_share: {mean['SQ_VALU_MFMA_BUSY_CYCLES'] / simds / cyc:.3f}")
+        if "SQ_INSTS_VALU" in mean and "SQ_INSTS_MFMA" in mean:
+            valu = mean["SQ_INSTS_VALU"] - mean["SQ_INSTS_MFMA"]
+            lines.append(f"valu_issue_share (4 cycles per wave64 instruction): {valu * 4 / simds / cyc:.3f}")
+    open(args.out, "w").write("\n".join(lines) + "\n")
+    print("\n".join(lines))
+
+
 def stats(args):
     rows = list(csv.DictReader(open(args.csv)))
     lines = [f"# rocprofv3 kernel statistics", f"command: {args.command}",
@@ -109,7 +156,7 @@ def main():
     t.add_argument("--kernel", default="paged_logits_kernel")
     t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--copy-bytes", type=int, default=256 << 20)
-    t.add_argument("--sources", default="logits.hip,sai_device.h",
+    t.add_argument("--sources", default="logits.hip,score_mfma.h,sai_device.h",
                    help="kernel sources (csrc/) whose hash the summary records")
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
@@ -117,8 +164,15 @@ def main():
     s.add_argument("--csv", required=True)
     s.add_argument("--command", required=True)
     s.add_argument("--out", required=True)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--kernel", required=True)
+    c.add_argument("--xcds", type=int, default=8)
+    c.add_argument("--cus", type=int, default=256)
+    c.add_argument("--command", required=True)
+    c.add_argument("--out", required=True)
     args = ap.parse_args()
-    traffic(args) if args.cmd == "traffic" else stats(args)
+    {"traffic": traffic, "stats": stats, "counters": counters}[args.cmd](args)
 
 
 if __name__ == "__main__":
