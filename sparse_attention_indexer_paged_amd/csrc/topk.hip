@@ -15,7 +15,10 @@
 // of wider rows) keeps each thread's keys in registers from the single read
 // to the output and finds T from a sample, a histogram over the sampled
 // value range and a brute-force rank of the few keys in the threshold bin,
-// with an exact radix select as the fallback.  Rows too wide for the
+// with an exact radix select as the fallback.  On the 1024-thread shapes
+// the keys at or above the sample's bound (about 1.3 k of the row) are
+// first compacted into LDS in position order, so the later phases handle 4
+// keys per thread instead of 8-16.  Rows too wide for the
 // segment-and-merge plan take topk_row_kernel, which streams the row from
 // L2 for each of three radix rounds (11, 11, 10 key bits).
 #include <atomic>
@@ -171,6 +174,7 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 constexpr int kSegCols = 16384;              // columns per segment of a wide row
 constexpr int kManyWgs = SAI_TOPK_MANY_WGS;  // from this many workgroups on, use small ones
 constexpr int kCandMax = 64;               // threshold-bin keys resolved by brute force
+constexpr int kCompCap = 4096;             // keys at or above the sampled bound kept in LDS
 // Launches of at most this many workgroups are latency-bound: their rows'
 // loads go out before the row lengths are known (a few wasted reads of rows
 // that need no selection are cheaper than the extra round trip).
@@ -283,6 +287,8 @@ __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t
 //  2. Keys >= key_lo are counted in 2048 bins spread linearly over
 //     [key_lo, key_hi] (keys above key_hi go to the top bin); the bin
 //     holding the k-th largest key typically holds a few keys.
+//     (With kComp the keys >= key_lo are compacted into LDS first and this
+//     and the following phases run on them.)
 //  3. Those keys (at most kCandMax) are copied to LDS and every wave ranks
 //     them by brute force in registers, which gives T exactly.
 // If the bound was too high or the bin too full (heavy ties, odd
@@ -301,8 +307,18 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     SlotMap sm) {
   constexpr int kWaves = NT / 64, SEG = VPT * NT;
   static_assert(!COUT || SEG == kSegCols, "a segment pass covers exactly one segment");
+  // Compaction (see below) on the 1024-thread shapes with at least 8 keys
+  // per thread: CPER = 4 compacted keys per thread, kCompCap in all.  (On
+  // the many-workgroup 512-thread shapes it measured even or slower: 8192
+  // rows of <= 8192 even, the 4-segment MTP pass 52 -> 64 us, its extra
+  // registers costing a wave per SIMD.)
+  constexpr int CPER = kCompCap / NT;
+  constexpr bool kComp = !CIN && NT == 1024 && VPT >= 2 * CPER;
   __shared__ __align__(16) int s_h0[kBins];
   __shared__ __align__(16) int s_h1[kBins];
+  __shared__ uint32_t s_ck[kComp ? kCompCap : 1];  // compacted keys
+  uint16_t* const s_cp = reinterpret_cast<uint16_t*>(s_h0);  // their positions (s_h0 is free then)
+  static_assert(kCompCap * 2 <= kBins * 4, "positions fit the first histogram");
   __shared__ uint32_t s_cand[kCandMax];
   __shared__ int s_wsum[kWaves];
   __shared__ uint32_t s_misc[2];  // [0] threshold-bin keys, [1] largest sampled key
@@ -541,21 +557,84 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   // 2. linear bins over the logit values [v_lo, v_hi] (a finite, non-empty
   // range: anything else goes straight to the radix select)
   bool fast = isfinite(v_lo) && isfinite(range) && range > 0.0f && isfinite(scale);
+
+  // 2a. Only keys >= key_lo can win while the bound holds, about 1.3 k of the
+  // row.  With kComp they are compacted, in ascending position order, into
+  // LDS (keys in s_ck, positions in s_cp), and the histogram, candidate and
+  // output phases run on each thread's CPER compacted keys instead of its
+  // VPT register keys.  The register keys stay live for the radix
+  // fallback, which then also writes the output.
+  bool comp = false;
+  uint32_t ckey[kComp ? CPER : 1];
+  int32_t ccol[kComp ? CPER : 1];
+  if constexpr (kComp) {
+    if (fast) {
+      int cnt = 0;
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) cnt += (key[e] != 0u && key[e] >= key_lo);
+      const int incl = wave_scan_dpp(cnt);
+      if (lane == 63) s_wsum[wid] = incl;
+      __syncthreads();
+      int off = incl - cnt, total = 0;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const int sw = s_wsum[w];
+        off += w < wid ? sw : 0;
+        total += sw;
+      }
+      comp = total >= k && total <= kCompCap;
+      if (comp) {
+#pragma unroll
+        for (int e = 0; e < VPT; ++e) {
+          if (key[e] != 0u && key[e] >= key_lo) {
+            s_ck[off] = key[e];
+            s_cp[off] = (uint16_t)(base + e);
+            ++off;
+          }
+        }
+      }
+      __syncthreads();  // the compacted list; every wave has read s_wsum
+      if (comp) {
+#pragma unroll
+        for (int j = 0; j < CPER; ++j) {
+          const int i = tid * CPER + j;
+          ckey[j] = i < total ? s_ck[i] : 0u;
+          ccol[j] = i < total ? (int32_t)(cbase + s_cp[i]) : -1;
+        }
+      }
+    }
+  }
   BinPick p1 = {0, 0, false};
   if (fast) {
+    if (comp) {
 #pragma unroll
-    for (int e = 0; e < VPT; ++e)
-      if (key[e] != 0u && key[e] >= key_lo) atomicAdd(&s_h1[fbin(key[e])], 1);
+      for (int j = 0; j < (kComp ? CPER : 1); ++j)
+        if (ckey[j] != 0u) atomicAdd(&s_h1[fbin(ckey[j])], 1);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPT; ++e)
+        if (key[e] != 0u && key[e] >= key_lo) atomicAdd(&s_h1[fbin(key[e])], 1);
+    }
     __syncthreads();
     p1 = pick(s_h1, k, B11{});
     fast = p1.found;
   }
   if (fast) {
+    if (comp) {
 #pragma unroll
-    for (int e = 0; e < VPT; ++e) {
-      if (key[e] != 0u && key[e] >= key_lo && fbin(key[e]) == p1.bin) {
-        const uint32_t sl = atomicAdd(&s_misc[0], 1u);
-        if (sl < (uint32_t)kCandMax) s_cand[sl] = key[e];
+      for (int j = 0; j < (kComp ? CPER : 1); ++j) {
+        if (ckey[j] != 0u && fbin(ckey[j]) == p1.bin) {
+          const uint32_t sl = atomicAdd(&s_misc[0], 1u);
+          if (sl < (uint32_t)kCandMax) s_cand[sl] = ckey[j];
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < VPT; ++e) {
+        if (key[e] != 0u && key[e] >= key_lo && fbin(key[e]) == p1.bin) {
+          const uint32_t sl = atomicAdd(&s_misc[0], 1u);
+          if (sl < (uint32_t)kCandMax) s_cand[sl] = key[e];
+        }
       }
     }
     __syncthreads();
@@ -624,45 +703,62 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     round(hb, 0, 0x3FFu, 0u, B10{});
     T = prefix;
     need = nd;
+    comp = false;  // the output comes from the register keys
   }
 
   // ordered output; counts packed as (equal << 12) | above (above-T totals
-  // stay below k <= 2048, equal totals below 2^19)
-  int ngt = 0, neq = 0;
+  // stay below k <= 2048, equal totals below 2^19).  The keys are either the
+  // compacted list (thread t holds its ascending slice) or the register keys
+  // (thread t holds positions [t*VPT, (t+1)*VPT)): either way thread order is
+  // position order.
+  auto place = [&](auto cnt_tag, auto key_at, auto col_at) {
+    constexpr int CNT = decltype(cnt_tag)::value;
+    int ngt = 0, neq = 0;
 #pragma unroll
-  for (int e = 0; e < VPT; ++e) {
-    const bool in = key[e] != 0u;
-    ngt += (in && key[e] > T);
-    neq += (in && key[e] == T);
-  }
-  const int packed = ngt | (neq << 12);
-  const int inc = wave_scan_dpp(packed);
-  if (lane == 63) s_wsum[wid] = inc;
-  __syncthreads();
-  int ex = inc - packed;
+    for (int e = 0; e < CNT; ++e) {
+      const uint32_t ke = key_at(e);
+      const bool in = ke != 0u;
+      ngt += (in && ke > T);
+      neq += (in && ke == T);
+    }
+    const int packed = ngt | (neq << 12);
+    const int inc = wave_scan_dpp(packed);
+    if (lane == 63) s_wsum[wid] = inc;
+    __syncthreads();
+    int ex = inc - packed;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
-  int gt_b = ex & 0xFFF, eq_b = ex >> 12;
-  int tot = 0;
+    for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
+    int gt_b = ex & 0xFFF, eq_b = ex >> 12;
+    int tot = 0;
 #pragma unroll
-  for (int w = 0; w < kWaves; ++w) tot += s_wsum[w];
-  const int nwin = min(k, (tot & 0xFFF) + min(tot >> 12, need));  // k unless the row is short
+    for (int w = 0; w < kWaves; ++w) tot += s_wsum[w];
 #pragma unroll
-  for (int e = 0; e < VPT; ++e) {
-    if (key[e] != 0u) {
-      int pos = -1;
-      if (key[e] > T) {
-        pos = gt_b + min(eq_b, need);
-        ++gt_b;
-      } else if (key[e] == T) {
-        if (eq_b < need) pos = gt_b + eq_b;
-        ++eq_b;
-      }
-      if ((unsigned)pos < (unsigned)k) {
-        s_h0[pos] = column(e);
-        if (COUT) s_h1[pos] = (int)key[e];
+    for (int e = 0; e < CNT; ++e) {
+      const uint32_t ke = key_at(e);
+      if (ke != 0u) {
+        int pos = -1;
+        if (ke > T) {
+          pos = gt_b + min(eq_b, need);
+          ++gt_b;
+        } else if (ke == T) {
+          if (eq_b < need) pos = gt_b + eq_b;
+          ++eq_b;
+        }
+        if ((unsigned)pos < (unsigned)k) {
+          s_h0[pos] = col_at(e);
+          if (COUT) s_h1[pos] = (int)ke;
+        }
       }
     }
+    return min(k, (tot & 0xFFF) + min(tot >> 12, need));  // k unless the row is short
+  };
+  int nwin;
+  if (comp) {
+    nwin = place(std::integral_constant<int, (kComp ? CPER : 1)>{}, [&](int j) { return ckey[j]; },
+                 [&](int j) { return ccol[j]; });
+  } else {
+    nwin = place(std::integral_constant<int, VPT>{}, [&](int e) { return key[e]; },
+                 [&](int e) { return column(e); });
   }
   if constexpr (EARLY) store_bt();
   __syncthreads();
