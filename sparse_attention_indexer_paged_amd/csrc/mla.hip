@@ -92,9 +92,9 @@ extern "C" int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const
 //   out[t,h] = sum_j softmax(s)_j kv_j,  lse[t,h] = log sum_j exp(s_j),
 // kv_j the dequantised latent (code * tile scale), kpe_j the stored RoPE part.
 //
-// Two kernels share the staging below: the 64-head (wide) kernel, described
-// at its definition, for head counts in groups of 64, and the 16-head
-// (narrow) kernel described here for the rest.
+// Two kernels share the gather below: the 64-head (wide) kernel, described
+// at its definition (it stages chunks as bf16), for head counts in groups of
+// 64, and the 16-head (narrow) kernel described here for the rest.
 //
 // Narrow: workgroup = one query row x 16 heads x one split of the slot list,
 // 4 waves.  Slots go through in chunks of 32: the chunk's entries are gathered one
@@ -112,6 +112,7 @@ extern "C" int mla_cache_write(const void* kv_bf16, int64_t kv_row_stride, const
 
 typedef __bf16 v8bf16 __attribute__((ext_vector_type(8)));
 typedef __bf16 v2bf16 __attribute__((ext_vector_type(2)));
+typedef __bf16 v4bf16 __attribute__((ext_vector_type(4)));
 
 constexpr int kMlaHg = 16;     // heads per workgroup (narrow kernel) and per wave (wide)
 constexpr int kMlaWideHeads = 64;  // heads per workgroup of the wide kernel
@@ -304,32 +305,6 @@ __device__ __forceinline__ MlaStage8 mla_gather8(const uint8_t* __restrict__ cac
   return st;
 }
 
-__device__ __forceinline__ void mla_stage8_to_lds(MlaChunkLds& sm, const MlaStage8& st) {
-  const int t = threadIdx.x;
-  const int tg = t >> 6, dp = t & 63;
-  uint2 c[4];  // invalid tokens staged as zeros (see mla_stage_to_lds)
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const bool v = (st.vmask >> (4 * tg + i)) & 1u;
-    c[i] = v ? st.c[i] : make_uint2(0u, 0u);
-    *reinterpret_cast<uint2*>(&sm.km[4 * tg + i][8 * dp]) = c[i];
-  }
-  uint32_t lo[4], hi[4];
-  tr4x4(c[0].x, c[1].x, c[2].x, c[3].x, lo);
-  tr4x4(c[0].y, c[1].y, c[2].y, c[3].y, hi);
-  *reinterpret_cast<uint4*>(&sm.vt[tg][8 * dp]) = make_uint4(lo[0], lo[1], lo[2], lo[3]);
-  *reinterpret_cast<uint4*>(&sm.vt[tg][8 * dp + 4]) = make_uint4(hi[0], hi[1], hi[2], hi[3]);
-  if (t < 256) {
-    *reinterpret_cast<uint4*>(&sm.pe[t >> 3][8 * (t & 7)]) = st.tail;
-  } else if (t < 256 + kMlaChunk) {
-    const int j = t - 256;
-    sm.sct[0][j] = st.valid ? __uint_as_float(st.tail.x) : 0.0f;
-    sm.sct[1][j] = st.valid ? __uint_as_float(st.tail.y) : 0.0f;
-    sm.sct[2][j] = st.valid ? __uint_as_float(st.tail.z) : 0.0f;
-    sm.sct[3][j] = st.valid ? __uint_as_float(st.tail.w) : 0.0f;
-    sm.valid[j] = st.valid;
-  }
-}
 
 __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
     const uint16_t* __restrict__ q_nope, const uint16_t* __restrict__ q_pe, int heads,
@@ -472,6 +447,60 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
   }
 }
 
+// The wide kernel stages each chunk as bf16, converted once per workgroup
+// (every fp8 code is a bf16 value), in one [slot][dim] layout read two ways:
+// the Q.K^T operands are 16-byte row reads (8 dims of one slot), and the P.V
+// operands come through ds_read_b64_tr_b16, which hands lane n of a 16-lane
+// group element n of four rows (4 slots of one dim).  16-byte chunk c of
+// slot r sits at c ^ mla_swz(r): eight consecutive slots then put one chunk
+// in eight different 16-byte bank groups (the row reads take 8 lanes a
+// cycle) and four consecutive slots put a 32-byte chunk pair in four
+// different 32-byte groups (the transposing reads take 16 lanes a cycle).
+__device__ __forceinline__ int mla_swz(int r) { return ((r & 3) << 1) | ((r >> 2) & 1); }
+
+struct alignas(16) MlaChunkBf {
+  uint4 kv[kMlaChunk][kMlaKv / 8];    // latent values, bf16, swizzled chunks
+  uint4 pe[kMlaChunk][kMlaRope / 8];  // RoPE values, bf16, swizzled chunks
+  float sct[4][kMlaChunk];            // tile scales, [tile][token]
+  int valid[kMlaChunk];
+};
+
+// mla_gather8's registers -> a bf16 chunk (invalid tokens as zero codes and
+// scales, see mla_stage_to_lds).
+__device__ __forceinline__ void mla_stage8_to_lds_bf(MlaChunkBf& sm, const MlaStage8& st) {
+  const int t = threadIdx.x;
+  const int tg = t >> 6, dp = t & 63;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * tg + i;
+    const bool v = (st.vmask >> r) & 1u;
+    const v8bf16 b = fp8x8_to_bf16(v ? st.c[i] : make_uint2(0u, 0u));
+    uint4 u;
+    __builtin_memcpy(&u, &b, 16);
+    sm.kv[r][dp ^ mla_swz(r)] = u;
+  }
+  if (t < 256) {
+    const int r = t >> 3;
+    sm.pe[r][(t & 7) ^ mla_swz(r)] = st.tail;
+  } else if (t < 256 + kMlaChunk) {
+    const int j = t - 256;
+    sm.sct[0][j] = st.valid ? __uint_as_float(st.tail.x) : 0.0f;
+    sm.sct[1][j] = st.valid ? __uint_as_float(st.tail.y) : 0.0f;
+    sm.sct[2][j] = st.valid ? __uint_as_float(st.tail.z) : 0.0f;
+    sm.sct[3][j] = st.valid ? __uint_as_float(st.tail.w) : 0.0f;
+    sm.valid[j] = st.valid;
+  }
+}
+
+typedef short v4s16 __attribute__((ext_vector_type(4)));
+
+// 4 bf16 of one dim for four consecutive slots (ds_read_b64_tr_b16), from a
+// byte address inside the LDS chunk.
+__device__ __forceinline__ v4s16 lds_tr4(const uint8_t* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s16*)(const_cast<uint8_t*>(p)));
+}
+
 // 64 heads per workgroup in eight waves: wave w takes heads 16(w%4)..+15
 // and latent tiles 2(w/4), 2(w/4)+1 (value dims 256(w/4)..+255) plus RoPE
 // step w/4.  The two waves of a head block add their partial scores through
@@ -481,9 +510,10 @@ __global__ __launch_bounds__(256) void sparse_mla_decode_kernel(
 // Scores are formed transposed, S^T = K Q^T: lane (g, n) then holds head n
 // for tokens 4g..4g+3 and 16+4g..16+4g+3, which are exactly the eight
 // tokens it supplies as the A operand of P.V when the B operand (V) is read
-// from slabs g and 4+g.  The softmax state of head n is therefore per lane;
-// the running max is shared by the four lanes of a head (two shuffles a
-// chunk) and the running sum is reduced once at the end.  O is rescaled
+// with two transposing reads of slots 4g..4g+3 and 16+4g..16+4g+3.  The
+// softmax state of head n is therefore per lane; the running max is shared
+// by the four lanes of a head (two shuffles a chunk) and the running sum is
+// reduced once at the end.  O is rescaled
 // only when a head's max grows by more than 2^8 (until then the weights
 // 2^(s - m) stay below 2^8, harmless in bf16 and fp32).
 __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
@@ -492,7 +522,7 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     const int32_t* __restrict__ slots, int k, float sm_log2, int nsplit, int split_len, int rows,
     float* __restrict__ out, float* __restrict__ lse, float* __restrict__ ws_o,
     float* __restrict__ ws_ml) {
-  __shared__ MlaChunkLds buf[3];
+  __shared__ MlaChunkBf buf[3];
   __shared__ v4f xs[2][4][2][2][64];  // partial scores [chunk parity][head block][tile half][token half][lane]
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int g = lane >> 4, n = lane & 15;
@@ -532,13 +562,27 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     int id = mla_load_id(srow, base0, lim);
     MlaStage8 st = mla_gather8(cache, id, base0, lim, num_slots, (uint32_t)block_size, block_stride);
     id = mla_load_id(srow, base0 + kMlaChunk, lim);
-    mla_stage8_to_lds(buf[0], st);
+    mla_stage8_to_lds_bf(buf[0], st);
     st = mla_gather8(cache, id, base0 + kMlaChunk, lim, num_slots, (uint32_t)block_size, block_stride);
     id = mla_load_id(srow, base0 + 2 * kMlaChunk, lim);
     __syncthreads();
+    // per-lane byte offsets inside a chunk (the rest of each address is a
+    // compile-time constant): Q.K^T rows n and 16+n, 16-byte chunks 4s+g
+    // (s even: qk0, odd: qk1) of a 32-dim step; P.V rows 4g+r (and 16+4g+r),
+    // n = 4r+q reading 8 bytes of dims 16d + 4q of its row, for d % 4 = 0..3
+    const int sw = mla_swz(n);
+    const uint32_t qk0 = (uint32_t)(n * kMlaKv * 2 + ((g ^ sw) << 4));
+    const uint32_t qk1 = (uint32_t)(n * kMlaKv * 2 + (((4 + g) ^ sw) << 4));
+    const int pr = n >> 2, pq = n & 3;
+    const int psw = (pr << 1) | (g & 1);  // mla_swz(4g + pr) = mla_swz(16 + 4g + pr)
+    uint32_t pvo[4];
+#pragma unroll
+    for (int d4 = 0; d4 < 4; ++d4)
+      pvo[d4] = (uint32_t)((4 * g + pr) * kMlaKv * 2 + (((2 * d4 + (pq >> 1)) ^ psw) << 4) + 8 * (pq & 1));
     int cur = 0, nxt = 1;  // buffers of chunks c and c+1 (three rotate)
     for (int c = 0; c < nchunks; ++c) {
-      const MlaChunkLds& b = buf[cur];
+      const MlaChunkBf& b = buf[cur];
+      const uint8_t* kvb = reinterpret_cast<const uint8_t*>(&b.kv[0][0]);
       // partial S^T over this wave's two tiles (each scaled) and RoPE step,
       // tokens n (acc 0) and 16+n (acc 1)
       v4f s0 = zero, s1 = zero;
@@ -548,18 +592,19 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
         v4f a0 = zero, a1 = zero;
 #pragma unroll
         for (int st4 = 0; st4 < 4; ++st4) {
-          const int col = w * kMlaTile + 32 * st4 + 8 * g;
-          const uint2 c0 = *reinterpret_cast<const uint2*>(&b.km[n][col]);
-          const uint2 c1 = *reinterpret_cast<const uint2*>(&b.km[16 + n][col]);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c0), qa[4 * w2 + st4], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fp8x8_to_bf16(c1), qa[4 * w2 + st4], a1, 0, 0, 0);
+          // chunk 16w + 4 st4 + g: bits 3+ are constant, bits 0-2 come from the lane
+          const uint8_t* rp = kvb + (st4 & 1 ? qk1 : qk0) + ((16 * w + 8 * (st4 >> 1)) << 4);
+          const uint4 c0 = *reinterpret_cast<const uint4*>(rp);
+          const uint4 c1 = *reinterpret_cast<const uint4*>(rp + 16 * kMlaKv * 2);
+          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c0), qa[4 * w2 + st4], a0, 0, 0, 0);
+          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c1), qa[4 * w2 + st4], a1, 0, 0, 0);
         }
         s0 += a0 * *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
         s1 += a1 * *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
       }
       {
-        const uint4 p0 = *reinterpret_cast<const uint4*>(&b.pe[n][32 * dh + 8 * g]);
-        const uint4 p1 = *reinterpret_cast<const uint4*>(&b.pe[16 + n][32 * dh + 8 * g]);
+        const uint4 p0 = b.pe[n][(4 * dh + g) ^ sw];
+        const uint4 p1 = b.pe[16 + n][(4 * dh + g) ^ sw];
         s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp, s0, 0, 0, 0);
         s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp, s1, 0, 0, 0);
       }
@@ -573,7 +618,7 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
       // it, the partial scores and chunk c+1 are visible.  The partial
       // scores alternate between two arrays for the same reason.  Past the
       // end these touch only valid addresses and are never read.
-      mla_stage8_to_lds(buf[nxt], st);
+      mla_stage8_to_lds_bf(buf[nxt], st);
       st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
                       block_stride);
       id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
@@ -624,9 +669,14 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
                            (__bf16)(pv[6] * t1[2]), (__bf16)(pv[7] * t1[3])};
 #pragma unroll
         for (int d = 0; d < kMlaTile / 16; ++d) {
-          const int dim = w * kMlaTile + 16 * d + n;
-          const uint2 cv = make_uint2(b.vt[g][dim], b.vt[4 + g][dim]);
-          o[w2 * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, fp8x8_to_bf16(cv), o[w2 * 8 + d], 0, 0, 0);
+          // dims 128w + 16d .. +15: 16-byte chunks 16w + 2d + (0, 1); the
+          // lane's chunk index XOR its row's swizzle is pvo[d % 4] + 8 (d / 4)
+          const uint8_t* vp = kvb + pvo[d & 3] + ((16 * w + 8 * (d >> 2)) << 4);
+          const v4s16 lo = lds_tr4(vp);                        // slots 4g .. 4g+3
+          const v4s16 hi = lds_tr4(vp + 16 * kMlaKv * 2);      // slots 16+4g .. 16+4g+3
+          const v8bf16 vb = __builtin_shufflevector(__builtin_bit_cast(v4bf16, lo), __builtin_bit_cast(v4bf16, hi),
+                                                    0, 1, 2, 3, 4, 5, 6, 7);
+          o[w2 * 8 + d] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa, vb, o[w2 * 8 + d], 0, 0, 0);
         }
       }
       cur = nxt;
