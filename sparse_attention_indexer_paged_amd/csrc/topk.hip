@@ -707,58 +707,74 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   }
 
   // ordered output; counts packed as (equal << 12) | above (above-T totals
-  // stay below k <= 2048, equal totals below 2^19).  The keys are either the
-  // compacted list (thread t holds its ascending slice) or the register keys
-  // (thread t holds positions [t*VPT, (t+1)*VPT)): either way thread order is
-  // position order.
-  auto place = [&](auto cnt_tag, auto key_at, auto col_at) {
-    constexpr int CNT = decltype(cnt_tag)::value;
-    int ngt = 0, neq = 0;
+  // stay below k <= 2048, equal totals below 2^19).  The keys are the
+  // register keys (thread t holds positions [t*VPT, (t+1)*VPT)) or, with
+  // comp, the compacted list (thread t holds its ascending slice): either
+  // way thread order is position order.
+  int ngt = 0, neq = 0;
+  if (comp) {
 #pragma unroll
-    for (int e = 0; e < CNT; ++e) {
-      const uint32_t ke = key_at(e);
-      const bool in = ke != 0u;
-      ngt += (in && ke > T);
-      neq += (in && ke == T);
+    for (int j = 0; j < (kComp ? CPER : 1); ++j) {
+      const bool in = ckey[j] != 0u;
+      ngt += (in && ckey[j] > T);
+      neq += (in && ckey[j] == T);
     }
-    const int packed = ngt | (neq << 12);
-    const int inc = wave_scan_dpp(packed);
-    if (lane == 63) s_wsum[wid] = inc;
-    __syncthreads();
-    int ex = inc - packed;
+  } else {
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
-    int gt_b = ex & 0xFFF, eq_b = ex >> 12;
-    int tot = 0;
+    for (int e = 0; e < VPT; ++e) {
+      const bool in = key[e] != 0u;
+      ngt += (in && key[e] > T);
+      neq += (in && key[e] == T);
+    }
+  }
+  const int packed = ngt | (neq << 12);
+  const int inc = wave_scan_dpp(packed);
+  if (lane == 63) s_wsum[wid] = inc;
+  __syncthreads();
+  int ex = inc - packed;
 #pragma unroll
-    for (int w = 0; w < kWaves; ++w) tot += s_wsum[w];
+  for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
+  int gt_b = ex & 0xFFF, eq_b = ex >> 12;
+  int tot = 0;
 #pragma unroll
-    for (int e = 0; e < CNT; ++e) {
-      const uint32_t ke = key_at(e);
-      if (ke != 0u) {
+  for (int w = 0; w < kWaves; ++w) tot += s_wsum[w];
+  const int nwin = min(k, (tot & 0xFFF) + min(tot >> 12, need));  // k unless the row is short
+  if (comp) {
+#pragma unroll
+    for (int j = 0; j < (kComp ? CPER : 1); ++j) {
+      if (ckey[j] != 0u) {
         int pos = -1;
-        if (ke > T) {
+        if (ckey[j] > T) {
           pos = gt_b + min(eq_b, need);
           ++gt_b;
-        } else if (ke == T) {
+        } else if (ckey[j] == T) {
           if (eq_b < need) pos = gt_b + eq_b;
           ++eq_b;
         }
         if ((unsigned)pos < (unsigned)k) {
-          s_h0[pos] = col_at(e);
-          if (COUT) s_h1[pos] = (int)ke;
+          s_h0[pos] = ccol[j];
+          if (COUT) s_h1[pos] = (int)ckey[j];
         }
       }
     }
-    return min(k, (tot & 0xFFF) + min(tot >> 12, need));  // k unless the row is short
-  };
-  int nwin;
-  if (comp) {
-    nwin = place(std::integral_constant<int, (kComp ? CPER : 1)>{}, [&](int j) { return ckey[j]; },
-                 [&](int j) { return ccol[j]; });
   } else {
-    nwin = place(std::integral_constant<int, VPT>{}, [&](int e) { return key[e]; },
-                 [&](int e) { return column(e); });
+#pragma unroll
+    for (int e = 0; e < VPT; ++e) {
+      if (key[e] != 0u) {
+        int pos = -1;
+        if (key[e] > T) {
+          pos = gt_b + min(eq_b, need);
+          ++gt_b;
+        } else if (key[e] == T) {
+          if (eq_b < need) pos = gt_b + eq_b;
+          ++eq_b;
+        }
+        if ((unsigned)pos < (unsigned)k) {
+          s_h0[pos] = column(e);
+          if (COUT) s_h1[pos] = (int)key[e];
+        }
+      }
+    }
   }
   if constexpr (EARLY) store_bt();
   __syncthreads();
