@@ -294,10 +294,15 @@ __device__ __forceinline__ MlaStage8 mla_gather8(const uint8_t* __restrict__ cac
     return (int64_t)(((uint64_t)(uint32_t)__shfl(hi, j) << 32) | (uint32_t)__shfl(lo, j));
   };
   MlaStage8 st;
-  const int tg = t >> 6, dp = t & 63;
+  const int tg = __builtin_amdgcn_readfirstlane(t >> 6), dp = t & 63;
+  // the four code tokens of a wave are the same for all its lanes: their
+  // offsets come through scalar lane reads, not lane shuffles
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    st.c[i] = *reinterpret_cast<const uint2*>(cache + off_of(4 * tg + i) + 8 * dp);
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t ol = (uint32_t)__builtin_amdgcn_readlane(lo, 4 * tg + i);
+    const uint32_t oh = (uint32_t)__builtin_amdgcn_readlane(hi, 4 * tg + i);
+    st.c[i] = *reinterpret_cast<const uint2*>(cache + (int64_t)(((uint64_t)oh << 32) | ol) + 8 * dp);
+  }
   const int64_t tail = t < 256 ? off_of((t >> 3) & 31) + kMlaRopeOff + 16 * (t & 7) : off + kMlaScaleOff;
   st.tail = *reinterpret_cast<const uint4*>(cache + tail);
   st.valid = ok;
