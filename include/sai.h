@@ -333,6 +333,48 @@ int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* r
                     void* workspace, size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * paged_mqa_topk_slots -- one decode step of the indexer: paged_mqa_logits
+ * followed by topk_rows_slots, with the logits kernel handing the selection
+ * each row's histogram of its logits (the fused logits -> top-k step beside
+ * the "clean logits" of vLLM PR #36250, review thread: the selection starts
+ * at the bin that holds the k-th largest logit instead of finding it from a
+ * sample of the logits).
+ *
+ * Outputs are exactly those of the two calls: logits, row_len_out and
+ * row_req_out as paged_mqa_logits writes them (both required here), out_idx
+ * and out_slots as topk_rows_slots writes them from those logits (k indices
+ * per row).  Arguments as for the two calls, plus
+ *   hist        [rows, 1024] int32 device buffer, rows = batch * next_n, or
+ *               NULL.  It must be all zero before the first call; every call
+ *               that uses it adds the counts in the logits kernel and sets
+ *               them back to zero in the selection, so it is zero again
+ *               after the call.  Used when paged_mqa_topk_hist_bytes(rows,
+ *               logits_stride) is non-zero (rows of at most 16384 columns,
+ *               fewer than 512 rows); otherwise, and when NULL, the step runs
+ *               the two calls unchanged and leaves hist untouched.
+ *   hist_bytes  its size; SAI_EWORKSPACE if it is used and smaller than
+ *               paged_mqa_topk_hist_bytes(rows, logits_stride).
+ *   workspace   as for topk_rows_slots (needed only for rows wider than
+ *               16384 columns, which never use hist).
+ * Errors: those of both calls, all checked before anything is launched.
+ * A histogram that is not zero before the call changes no result (the
+ * selection checks its bound as it checks a sampled one), only the time.
+ * On 64 rows of at most 16384 keys the step measured 2 us slower than the
+ * two plain calls: counting adds more to the logits kernel than starting
+ * from the histogram saves in the selection.
+ */
+int paged_mqa_topk_slots(const void* q_fp8, const float* weights, const void* kv_cache,
+                         int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                         const int32_t* context_lens, int32_t batch, int32_t next_n, float* logits,
+                         int64_t logits_stride, int32_t* row_len_out, int32_t* row_req_out, int32_t k,
+                         int32_t* out_idx, int32_t* out_slots, int32_t* hist, size_t hist_bytes,
+                         void* workspace, size_t workspace_bytes, hipStream_t stream);
+
+/* Bytes of paged_mqa_topk_slots' hist for this shape; 0 when the shape
+ * does not use one (rows <= 0, logits_stride <= 0 or > 16384, rows >= 512). */
+size_t paged_mqa_topk_hist_bytes(int32_t rows, int64_t logits_stride);
+
+/*
  * topk_rows_slots_noalloc -- topk_rows_slots for callers that cannot
  * allocate device memory (code under hipGraph capture, tight serving loops,
  * harnesses that forbid hipMalloc): no workspace argument, and no call to

@@ -58,11 +58,15 @@ SIGNATURES = {
     "mla_cache_write": [_c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i64, _i32,
                         _c_void_p],
     "sparse_mla_workspace_bytes": [_i32, _i32, _i32],
+    "paged_mqa_topk_hist_bytes": [_i32, _i64],
+    "paged_mqa_topk_slots": [_c_void_p, _c_void_p, _c_void_p, _i64, _c_void_p, _i64, _c_void_p, _i32, _i32,
+                             _c_void_p, _i64, _c_void_p, _c_void_p, _i32, _c_void_p, _c_void_p, _c_void_p,
+                             ctypes.c_size_t, _c_void_p, ctypes.c_size_t, _c_void_p],
     "sparse_mla_decode": [_c_void_p, _c_void_p, _i32, _i32, _c_void_p, _i64, _i32, _c_void_p, _i32,
                           ctypes.c_float, _c_void_p, _c_void_p, _c_void_p, ctypes.c_size_t, _c_void_p],
 }
 _RESTYPE = {"sai_status_string": ctypes.c_char_p, "topk_workspace_bytes": ctypes.c_size_t,
-            "sparse_mla_workspace_bytes": ctypes.c_size_t}
+            "sparse_mla_workspace_bytes": ctypes.c_size_t, "paged_mqa_topk_hist_bytes": ctypes.c_size_t}
 
 _lib = None
 
@@ -492,6 +496,59 @@ def topk_rows_slots_noalloc(logits, row_len, row_req, block_table, k=TOPK_MAX, o
                                           rows, k, _ptr(out), _ptr(slots), _stream()),
            "topk_rows_slots_noalloc")
     return out, slots
+
+
+def paged_mqa_topk_hist_bytes(rows, logits_stride):
+    return load().paged_mqa_topk_hist_bytes(rows, logits_stride)
+
+
+def paged_mqa_topk_slots(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None,
+                         hist=None, logits=None, row_len=None, row_req=None, out=None, slots=None,
+                         workspace=None):
+    """One decode step through the fused entry: the logits kernel also counts
+    each row's logits into ``hist`` (int32 [rows, 1024], zero on entry and
+    left zero) and the selection starts from those counts.  Returns (logits,
+    row_len, row_req, idx, slots).  ``hist`` is allocated zeroed here when
+    the shape uses one and none is passed; keep and pass it back to allocate
+    nothing per step."""
+    _need(q_fp8, torch.uint8, "q_fp8", 4)
+    _need(weights, torch.float32, "weights", 2)
+    _need(kv_cache, torch.uint8, "kv_cache", 2)
+    _need(block_table, torch.int32, "block_table", 2)
+    _need(context_lens, torch.int32, "context_lens", 1)
+    B, next_n = q_fp8.shape[0], q_fp8.shape[1]
+    if tuple(q_fp8.shape[2:]) != (HEADS, DIM) or tuple(weights.shape) != (B * next_n, HEADS):
+        raise ValueError("q_fp8 must be [B,next_n,64,128] and weights [B*next_n,64]")
+    if context_lens.shape[0] != B or block_table.shape[0] != B:
+        raise ValueError("context_lens and block_table need one row per request")
+    rows = B * next_n
+    width = block_table.shape[1] * BLOCK if width is None else width
+    dev = q_fp8.device
+    logits = torch.empty((rows, width), dtype=torch.float32, device=dev) if logits is None else logits
+    row_len = torch.empty((rows,), dtype=torch.int32, device=dev) if row_len is None else row_len
+    row_req = torch.empty((rows,), dtype=torch.int32, device=dev) if row_req is None else row_req
+    out = torch.empty((rows, k), dtype=torch.int32, device=dev) if out is None else out
+    slots = torch.empty((rows, k), dtype=torch.int32, device=dev) if slots is None else slots
+    _out(logits, torch.float32, "logits", (rows, width))
+    _out(row_len, torch.int32, "row_len", (rows,))
+    _out(row_req, torch.int32, "row_req", (rows,))
+    _out(out, torch.int32, "out", (rows, k))
+    _out(slots, torch.int32, "slots", (rows, k))
+    hist_bytes = paged_mqa_topk_hist_bytes(rows, width) if rows else 0
+    if hist is None and hist_bytes:
+        hist = torch.zeros((rows, 1024), dtype=torch.int32, device=dev)
+    if hist is not None:
+        _need(hist, torch.int32, "hist")
+    ws_bytes = 0 if hist_bytes else (topk_workspace_bytes(rows, width, k) if rows else 0)
+    if ws_bytes and workspace is None:
+        workspace = torch.empty((ws_bytes,), dtype=torch.uint8, device=dev)
+    _check(load().paged_mqa_topk_slots(
+        _ptr(q_fp8), _ptr(weights), _ptr(kv_cache), kv_cache.shape[0], _ptr(block_table),
+        block_table.stride(0), _ptr(context_lens), B, next_n, _ptr(logits), logits.stride(0),
+        _ptr(row_len), _ptr(row_req), k, _ptr(out), _ptr(slots), _ptr(hist),
+        hist.numel() * 4 if hist is not None else 0, _ptr(workspace),
+        workspace.numel() if workspace is not None else 0, _stream()), "paged_mqa_topk_slots")
+    return logits, row_len, row_req, out, slots
 
 
 def decode_indexer(q_fp8, weights, kv_cache, block_table, context_lens, k=TOPK_MAX, width=None,

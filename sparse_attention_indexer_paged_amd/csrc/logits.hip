@@ -23,6 +23,7 @@
 // one coalesced 256-byte store per row.
 #include <algorithm>
 
+#include "indexer_internal.h"
 #include "score_mfma.h"
 
 using namespace sai;
@@ -110,11 +111,13 @@ __device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], 
 // 16-byte word of q instead), which lets the in-order vmcnt accounting
 // leave the DEPTH-1 prefetched blocks in flight while one is scored.  No
 // global store sits in the loop, so no K load ever queues behind one.
-template <int NN, int DEPTH, int NS>
+// With HIST every visible logit of row r also counts into bin (order key >>
+// 22) of the wave's LDS histogram hist[r * kHistBins ..] (an LDS atomic).
+template <int NN, int DEPTH, int NS, bool HIST>
 __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, int64_t num_blocks,
                                             const uint8_t* __restrict__ dummy, int myblk,
                                             const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                            int ctx, float* st, int slots) {
+                                            int ctx, float* st, int slots, int* hist) {
   const int lane = threadIdx.x & 63;
   KFrag buf[DEPTH];
   bool okb[DEPTH];
@@ -138,21 +141,26 @@ __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, i
     for (int r = 0; r < NN; ++r) {
       const float sc = score_row(cur, qa[r], wf[r]);
       const float v = select_f(okb[i % DEPTH], sc * cur.s, kNaNBits);
-      st[(r * slots + i) * kBlock + lane] = select_f(col < ctx - NN + r + 1, v, kNegInfBits);
+      const bool vis = col < ctx - NN + r + 1;
+      st[(r * slots + i) * kBlock + lane] = select_f(vis, v, kNegInfBits);
+      if constexpr (HIST) {
+        if (vis) atomicAdd(&hist[r * kHistBins + (f32_order_key(v) >> (32 - kHistBits))], 1);
+      }
     }
   }
 }
 
 // Calls score_group with NS == n (1 <= n <= NS; n is wave-uniform).
-template <int NN, int DEPTH, int NS>
+template <int NN, int DEPTH, int NS, bool HIST>
 __device__ __forceinline__ void dispatch_group(int n, const uint8_t* __restrict__ cache, int64_t num_blocks,
                                                const uint8_t* __restrict__ dummy, int myblk,
                                                const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                               int ctx, float* st, int slots) {
+                                               int ctx, float* st, int slots, int* hist) {
   if (n == NS || NS == 1) {
-    score_group<NN, DEPTH, NS>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots);
+    score_group<NN, DEPTH, NS, HIST>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots, hist);
   } else if constexpr (NS > 1) {
-    dispatch_group<NN, DEPTH, NS - 1>(n, cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots);
+    dispatch_group<NN, DEPTH, NS - 1, HIST>(n, cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots,
+                                            hist);
   }
 }
 
@@ -166,13 +174,19 @@ __device__ __forceinline__ void dispatch_group(int n, const uint8_t* __restrict_
 // request, stages the logits in its LDS slice and writes them out as
 // contiguous row runs (float4 per lane when rows are 16-byte aligned) once
 // its units are done or the slice is full.
-template <int NN, int DEPTH, int CAP, bool NT>
+//
+// With HIST each wave also counts its visible logits per row into an LDS
+// histogram of the top kHistBits order-key bits and adds it to the row's
+// histogram in `hist` ([rows][kHistBins], device atomics) when it moves to
+// another request and at its end: the counts the top-k's first phase needs,
+// with no global operation inside the K loop.
+template <int NN, int DEPTH, int CAP, bool NT, bool HIST>
 __global__ __launch_bounds__(256) void paged_logits_kernel(
     const uint8_t* __restrict__ q, const float* __restrict__ wts, const uint8_t* __restrict__ cache,
     int64_t num_blocks, const int32_t* __restrict__ bt, int64_t bt_stride,
     const int32_t* __restrict__ ctx_lens, int32_t batch, float* __restrict__ logits,
     int64_t stride, int32_t* __restrict__ row_len_out, int32_t* __restrict__ row_req_out, bool vec,
-    bool clean) {
+    bool clean, int32_t* __restrict__ hist) {
   constexpr int kSlots = kStageFloats / (kBlock * NN);  // staged units per wave
   constexpr int kCap = CAP < kSlots ? CAP : kSlots;      // a group fits the stage
   static_assert(kCap >= 1, "stage too small");
@@ -183,6 +197,29 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   int* s_fill = s_unit + (batch + 1);     // [batch+1] prefix of fill pieces
   int* s_ctx = s_unit + 2 * (batch + 1);  // [batch] clamped context
   int* s_tot = s_unit + 3 * (batch + 1);  // [8] per-wave totals
+  int* s_hist = s_tot + 8 + wid * NN * kHistBins;  // [NN][kHistBins] this wave's histograms (HIST)
+  if constexpr (HIST) {
+#pragma unroll
+    for (int i = 0; i < NN * kHistBins / 256; ++i)
+      reinterpret_cast<int4*>(s_hist)[i * 64 + lane] = make_int4(0, 0, 0, 0);
+  }
+  // adds this wave's histograms of request hb to `hist` and clears them
+  auto flush_hist = [&](int hb) {
+#pragma unroll
+    for (int r = 0; r < NN; ++r) {
+      int* gh = hist + ((int64_t)hb * NN + r) * kHistBins;
+#pragma unroll
+      for (int i = 0; i < kHistBins / 256; ++i) {
+        const int j = (i * 64 + lane) * 4;
+        const int4 h = *reinterpret_cast<const int4*>(s_hist + r * kHistBins + j);
+        if (h.x) __hip_atomic_fetch_add(gh + j, h.x, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (h.y) __hip_atomic_fetch_add(gh + j + 1, h.y, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (h.z) __hip_atomic_fetch_add(gh + j + 2, h.z, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        if (h.w) __hip_atomic_fetch_add(gh + j + 3, h.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        *reinterpret_cast<int4*>(s_hist + r * kHistBins + j) = make_int4(0, 0, 0, 0);
+      }
+    }
+  };
 
   const int maxc = (int)min64(stride, bt_stride * kBlock);
 
@@ -320,6 +357,9 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     const int c0 = u - s_unit[b];
     const int myblk = lane < n ? bt[(int64_t)b * bt_stride + c0 + lane] : -1;
     if (b != qb) {
+      if constexpr (HIST) {
+        if (qb >= 0) flush_hist(qb);
+      }
       qb = b;
 #pragma unroll
       for (int r = 0; r < NN; ++r) {
@@ -327,24 +367,29 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
         load_wfrag(wf[r], wts + ((int64_t)qb * NN + r) * kHeads);
       }
     }
-    dispatch_group<NN, DEPTH, kCap>(n, cache, num_blocks, q, myblk, qa, wf, c0, s_ctx[b],
-                                    stage + (u - sa) * kBlock, kSlots);
+    dispatch_group<NN, DEPTH, kCap, HIST>(n, cache, num_blocks, q, myblk, qa, wf, c0, s_ctx[b],
+                                          stage + (u - sa) * kBlock, kSlots, s_hist);
     u += n;
   }
   if (sa < u1) flush(sa, u1, bs);
+  if constexpr (HIST) {
+    if (qb >= 0) flush_hist(qb);
+  }
 }
 
 template <int NN>
 int launch_paged(const void* q, const float* w, const void* cache, int64_t num_blocks,
                  const int32_t* bt, int64_t bt_stride, const int32_t* ctx, int32_t batch,
-                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, bool clean, hipStream_t s) {
+                 float* logits, int64_t stride, int32_t* rl, int32_t* rr, bool clean, int32_t* hist,
+                 hipStream_t s) {
   if (batch > 4096) return SAI_EUNSUPPORTED;  // LDS prefix arrays
   const int64_t wblocks = (stride + kBlock - 1) / kBlock;
   const int64_t units_max = (int64_t)batch * wblocks;
   const int64_t waves = std::min<int64_t>(kDecodeWaves, std::max<int64_t>(units_max, 1));
   int64_t G = (waves + 3) / 4;
   G = (G + 7) / 8 * 8;
-  const size_t lds = 4 * kStageFloats * sizeof(float) + (size_t)(3 * (batch + 1) + 8) * sizeof(int);
+  const size_t lds = 4 * kStageFloats * sizeof(float) + (size_t)(3 * (batch + 1) + 8) * sizeof(int) +
+                     (hist ? (size_t)4 * NN * kHistBins * sizeof(int) : 0);
   if (lds > 65536) {  // large batches need the device's full per-workgroup LDS
     int dev = 0, max_lds = 0;
     if (hipGetDevice(&dev) != hipSuccess ||
@@ -358,24 +403,30 @@ int launch_paged(const void* q, const float* w, const void* cache, int64_t num_b
   // 16384 columns: step 35.1 -> 34.3 us); larger ones are streamed past the
   // caches (32 x 131072: plain stores cost 1.2 % of the step; 256 x 65536:
   // even).
-  if ((int64_t)batch * NN * stride * (int64_t)sizeof(float) <= kPlainStoreMaxBytes)
-    launch((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap, false>), dim3((unsigned)G), dim3(256), lds, s,
-           (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt, bt_stride, ctx, batch, logits,
-           stride, rl, rr, vec, clean);
-  else
-    launch((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap, true>), dim3((unsigned)G), dim3(256), lds, s,
-           (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt, bt_stride, ctx, batch, logits,
-           stride, rl, rr, vec, clean);
+  const bool plain = (int64_t)batch * NN * stride * (int64_t)sizeof(float) <= kPlainStoreMaxBytes;
+#define SAI_PAGED_LAUNCH(NT_, HIST_)                                                                  \
+  launch((paged_logits_kernel<NN, kDecodeDepth, kDecodeCap, NT_, HIST_>), dim3((unsigned)G), dim3(256), lds, \
+         s, (const uint8_t*)q, w, (const uint8_t*)cache, num_blocks, bt, bt_stride, ctx, batch, logits,   \
+         stride, rl, rr, vec, clean, hist)
+  if (hist) {
+    if (plain) SAI_PAGED_LAUNCH(false, true); else SAI_PAGED_LAUNCH(true, true);
+  } else {
+    if (plain) SAI_PAGED_LAUNCH(false, false); else SAI_PAGED_LAUNCH(true, false);
+  }
+#undef SAI_PAGED_LAUNCH
   return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }
 
 }  // namespace
 
-namespace {
-int paged_entry(const void* q_fp8, const float* weights, const void* kv_cache, int64_t num_blocks,
-                const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
-                int32_t batch, int32_t next_n, float* logits, int64_t logits_stride,
-                int32_t* row_len_out, int32_t* row_req_out, bool clean, hipStream_t stream) {
+
+// The paged logits call behind paged_mqa_logits, paged_mqa_logits_visible
+// and the fused top-k entry (hist: the per-row histograms, or null).
+int sai_paged_logits(const void* q_fp8, const float* weights, const void* kv_cache, int64_t num_blocks,
+                     const int32_t* block_table, int64_t bt_stride, const int32_t* context_lens,
+                     int32_t batch, int32_t next_n, float* logits, int64_t logits_stride,
+                     int32_t* row_len_out, int32_t* row_req_out, bool clean, int32_t* hist,
+                     hipStream_t stream) {
   if (batch < 0 || num_blocks < 0 || bt_stride < 0 || logits_stride < 0) return SAI_EINVAL;
   if (next_n < 1 || next_n > SAI_NEXT_N_MAX) return SAI_EUNSUPPORTED;
   if (batch == 0) return SAI_OK;
@@ -386,21 +437,20 @@ int paged_entry(const void* q_fp8, const float* weights, const void* kv_cache, i
   if ((int64_t)batch * wblocks > 0x7FFFFFFF / 2 || logits_stride > 0x7FFFFFFF - kBlock)
     return SAI_EUNSUPPORTED;
   switch (next_n) {
-    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
-    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
-    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
-    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, stream);
+    case 1: return launch_paged<1>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, hist, stream);
+    case 2: return launch_paged<2>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, hist, stream);
+    case 3: return launch_paged<3>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, hist, stream);
+    default: return launch_paged<4>(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch, logits, logits_stride, row_len_out, row_req_out, clean, hist, stream);
   }
 }
-}  // namespace
 
 extern "C" int paged_mqa_logits(const void* q_fp8, const float* weights, const void* kv_cache,
                                 int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
                                 const int32_t* context_lens, int32_t batch, int32_t next_n,
                                 float* logits, int64_t logits_stride, int32_t* row_len_out,
                                 int32_t* row_req_out, hipStream_t stream) {
-  return paged_entry(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
-                     next_n, logits, logits_stride, row_len_out, row_req_out, true, stream);
+  return sai_paged_logits(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
+                          next_n, logits, logits_stride, row_len_out, row_req_out, true, nullptr, stream);
 }
 
 extern "C" int paged_mqa_logits_visible(const void* q_fp8, const float* weights, const void* kv_cache,
@@ -408,6 +458,6 @@ extern "C" int paged_mqa_logits_visible(const void* q_fp8, const float* weights,
                                         int64_t bt_stride, const int32_t* context_lens, int32_t batch,
                                         int32_t next_n, float* logits, int64_t logits_stride,
                                         int32_t* row_len_out, int32_t* row_req_out, hipStream_t stream) {
-  return paged_entry(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
-                     next_n, logits, logits_stride, row_len_out, row_req_out, false, stream);
+  return sai_paged_logits(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens, batch,
+                          next_n, logits, logits_stride, row_len_out, row_req_out, false, nullptr, stream);
 }

@@ -24,7 +24,7 @@
 #include <atomic>
 #include <type_traits>
 
-#include "sai_device.h"
+#include "indexer_internal.h"
 
 using namespace sai;
 
@@ -299,14 +299,24 @@ __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t
 // every winner its slot (the `need` lowest-index keys equal to T win), so
 // the winners come out in ascending position order; they are staged in LDS
 // and written with coalesced stores.
-template <int NT, int VPT, bool VEC, bool CIN, bool COUT, bool EARLY>
+//
+// HIST (one-pass rows with early loads only): the row's histogram of the top
+// kHistBits order-key bits over its visible columns, counted by the paged
+// logits kernel, is in hist[r * kHistBins ..].  It replaces the sample: the
+// bin holding the k-th largest key gives key_lo exactly (with the count
+// above it) and the linear bins of step 2 span that bin's value range.  The
+// row's histogram is read once and set back to zero for the next call.  A
+// wrong histogram costs speed, never exactness (the bound is checked like a
+// sampled one).
+template <int NT, int VPT, bool VEC, bool CIN, bool COUT, bool EARLY, bool HIST = false>
 __global__ __launch_bounds__(NT) void topk_select_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
     int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
     int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col,
-    SlotMap sm) {
+    SlotMap sm, int32_t* __restrict__ hist) {
   constexpr int kWaves = NT / 64, SEG = VPT * NT;
   static_assert(!COUT || SEG == kSegCols, "a segment pass covers exactly one segment");
+  static_assert(!HIST || (EARLY && !CIN && !COUT && NT >= kHistBins), "histograms: one-pass early rows");
   // Compaction (see below) on the 1024-thread shapes with at least 8 keys
   // per thread: CPER = 4 compacted keys per thread, kCompCap in all.  (On
   // the many-workgroup 512-thread shapes it measured even or slower: 8192
@@ -381,6 +391,12 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
       }
     }
   };
+  // the row's histogram goes out first: waiting for it then waits for no
+  // other load (the wait counter retires loads in order)
+  int32_t hval = 0;
+  if constexpr (HIST) {
+    if (tid < kHistBins) hval = hist[(int64_t)r * kHistBins + tid];
+  }
   if constexpr (EARLY) load_row(stride);
   // read after the row's loads are issued: a scalar load ahead of them
   // would make their address computation wait for it
@@ -429,9 +445,17 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   // Clears the histograms; done while the row's loads are in flight, so
   // this barrier overlaps their latency.
   auto clear_hist = [&]() {
-    for (int i = tid; i < kBins; i += NT) {
-      s_h0[i] = 0;
-      s_h1[i] = 0;
+    if constexpr (HIST) {  // the row's histogram to LDS (loaded first thing), zero for the next call
+      if (tid < kHistBins) {
+        s_h0[tid] = hval;
+        hist[(int64_t)r * kHistBins + tid] = 0;
+      }
+      for (int i = tid; i < kBins; i += NT) s_h1[i] = 0;
+    } else {
+      for (int i = tid; i < kBins; i += NT) {
+        s_h0[i] = 0;
+        s_h1[i] = 0;
+      }
     }
     if (tid < 2) s_misc[tid] = 0u;
     __syncthreads();
@@ -536,19 +560,32 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
     return;
   }
 
-  // 1. sample (the histograms were cleared while the row was loading)
-  if (key[0] != 0u) atomicAdd(&s_h0[key[0] >> 21], 1);
-  const uint32_t wmax = wave_max_dpp(key[0]);
-  if (lane == 63) atomicMax(&s_misc[1], wmax);
-  __syncthreads();
-  const int S = (n + VPT - 1) / VPT;
-  // k*S*13 < 2^25 and n*10 < 2^19: 32-bit arithmetic
-  const int m = min(S, (int)(((uint32_t)k * S * 13u + (uint32_t)n * 10u - 1u) / ((uint32_t)n * 10u)) + 8);
-  const BinPick ps = pick(s_h0, m, B11{}, true);
-  const uint32_t lo_digit = (uint32_t)ps.bin;
-  const uint32_t key_lo = lo_digit << 21;
+  // 1. the lower bound key_lo and the top of the value range of step 2:
+  // from the row's histogram (HIST), else from a sample (the histograms
+  // were cleared while the row was loading)
+  uint32_t lo_digit, key_lo, key_top;  // lo_digit: key_lo's top 11 bits
+  if constexpr (HIST) {
+    const BinPick ph = pick(s_h0, k, std::integral_constant<int, kHistBins>{});
+    // no bin holds the k-th key (a wrong histogram): key_lo above every key,
+    // so the bound fails and the radix select runs unpruned
+    lo_digit = ph.found ? (uint32_t)ph.bin << (kHistBits == 10 ? 1 : 0) : 0u;
+    key_lo = ph.found ? (uint32_t)ph.bin << (32 - kHistBits) : 0xFFFFFFFFu;
+    key_top = ph.found ? key_lo + ((1u << (32 - kHistBits)) - 1u) : 0xFFFFFFFFu;
+  } else {
+    if (key[0] != 0u) atomicAdd(&s_h0[key[0] >> 21], 1);
+    const uint32_t wmax = wave_max_dpp(key[0]);
+    if (lane == 63) atomicMax(&s_misc[1], wmax);
+    __syncthreads();
+    const int S = (n + VPT - 1) / VPT;
+    // k*S*13 < 2^25 and n*10 < 2^19: 32-bit arithmetic
+    const int m = min(S, (int)(((uint32_t)k * S * 13u + (uint32_t)n * 10u - 1u) / ((uint32_t)n * 10u)) + 8);
+    const BinPick ps = pick(s_h0, m, B11{}, true);
+    lo_digit = (uint32_t)ps.bin;
+    key_lo = lo_digit << 21;
+    key_top = max(s_misc[1], key_lo);
+  }
   const float v_lo = order_key_value(key_lo);
-  const float range = order_key_value(max(s_misc[1], key_lo)) - v_lo;
+  const float range = order_key_value(key_top) - v_lo;
   const float scale = 2048.0f / range;
   auto fbin = [&](uint32_t kk) {
     return (int)fminf((order_key_value(kk) - v_lo) * scale, (float)(kBins - 1));
@@ -844,19 +881,19 @@ void launch_sel(bool vec, unsigned grid, const float* logits, int64_t stride, co
     if (grid <= kEarlyLoadWgs) {
       if (vec)
         launch((topk_select_kernel<NT, VPT, true, CIN, COUT, true>), dim3(grid), dim3(NT), dyn, s,
-               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm, nullptr);
       else
         launch((topk_select_kernel<NT, VPT, false, CIN, COUT, true>), dim3(grid), dim3(NT), dyn, s,
-               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+               logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm, nullptr);
       return;
     }
   }
   if (vec)
     launch((topk_select_kernel<NT, VPT, true, CIN, COUT, false>), dim3(grid), dim3(NT), dyn, s,
-           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm, nullptr);
   else
     launch((topk_select_kernel<NT, VPT, false, CIN, COUT, false>), dim3(grid), dim3(NT), dyn, s,
-           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm);
+           logits, stride, row_len, k, nseg, c_key, c_col, out, o_key, o_col, sm, nullptr);
 }
 
 // Launches the shape's instantiation (segment passes exist only for the
@@ -1025,4 +1062,81 @@ extern "C" int topk_rows_slots_noalloc(const float* logits, int64_t logits_strid
   }
   return topk_rows_slots(logits, logits_stride, row_len, row_req, block_table, bt_stride, batch, rows,
                          k, out_idx, out_slots, ws, need, stream);
+}
+
+// ------------------------------------------------------------ fused decode
+namespace {
+
+// The histogram-seeded one-pass selection (1024 threads, early loads).
+void launch_hist_sel(int vpt, bool vec, unsigned rows, const float* logits, int64_t stride,
+                     const int32_t* row_len, int32_t k, int32_t* out, const SlotMap& sm, int32_t* hist,
+                     hipStream_t s) {
+  const size_t dyn = sm.out && sm.bt_stride <= kBtLds ? (size_t)sm.bt_stride * sizeof(int32_t) : 0;
+#define SAI_HIST_CASE(VPT_)                                                                             \
+  if (vpt == VPT_) {                                                                                    \
+    if (vec)                                                                                            \
+      launch((topk_select_kernel<1024, VPT_, true, false, false, true, true>), dim3(rows), dim3(1024), dyn, s, \
+             logits, stride, row_len, k, 1, nullptr, nullptr, out, nullptr, nullptr, sm, hist);         \
+    else                                                                                                \
+      launch((topk_select_kernel<1024, VPT_, false, false, false, true, true>), dim3(rows), dim3(1024), dyn, \
+             s, logits, stride, row_len, k, 1, nullptr, nullptr, out, nullptr, nullptr, sm, hist);      \
+    return;                                                                                             \
+  }
+  SAI_HIST_CASE(4)
+  SAI_HIST_CASE(8)
+  SAI_HIST_CASE(16)
+#undef SAI_HIST_CASE
+}
+
+// Whether a decode step of `rows` rows of width `stride` takes the
+// histogram-seeded selection (and the shape it runs in).
+bool hist_shape(int64_t rows, int64_t stride, Shape* sh) {
+  if (stride > kSegCols || rows >= kManyWgs) return false;
+  *sh = shape_for(stride, rows, 16);
+  return sh->nt == 1024;
+}
+
+}  // namespace
+
+extern "C" size_t paged_mqa_topk_hist_bytes(int32_t rows, int64_t logits_stride) {
+  Shape sh;
+  if (rows <= 0 || logits_stride <= 0 || !hist_shape(rows, logits_stride, &sh)) return 0;
+  return (size_t)rows * kHistBins * sizeof(int32_t);
+}
+
+extern "C" int paged_mqa_topk_slots(const void* q_fp8, const float* weights, const void* kv_cache,
+                                    int64_t num_blocks, const int32_t* block_table, int64_t bt_stride,
+                                    const int32_t* context_lens, int32_t batch, int32_t next_n,
+                                    float* logits, int64_t logits_stride, int32_t* row_len_out,
+                                    int32_t* row_req_out, int32_t k, int32_t* out_idx, int32_t* out_slots,
+                                    int32_t* hist, size_t hist_bytes, void* workspace,
+                                    size_t workspace_bytes, hipStream_t stream) {
+  // everything the selection needs is checked before the logits launch
+  if (batch < 0 || logits_stride < 0 || bt_stride < 0 || num_blocks < 0) return SAI_EINVAL;
+  if (next_n < 1 || next_n > SAI_NEXT_N_MAX || k < 1 || k > SAI_TOPK_MAX) return SAI_EUNSUPPORTED;
+  if (batch == 0) return SAI_OK;
+  const int64_t rows = (int64_t)batch * next_n;
+  if (!logits || !row_len_out || !row_req_out || !out_idx || !out_slots || !block_table) return SAI_EINVAL;
+  if (logits_stride == 0) return SAI_EINVAL;
+  if (logits_stride > 0x7FFFFFFF - 4 * kThreads) return SAI_EUNSUPPORTED;
+  Shape sh;
+  const size_t need_hist = paged_mqa_topk_hist_bytes((int32_t)rows, logits_stride);
+  const bool use_hist = hist != nullptr && need_hist > 0 && hist_shape(rows, logits_stride, &sh);
+  if (use_hist && hist_bytes < need_hist) return SAI_EWORKSPACE;
+  if (!use_hist) {
+    const TopkPlan p = plan_for(logits_stride, k, rows);
+    if (p.nseg > 0 && (!workspace || workspace_bytes < topk_workspace_bytes((int32_t)rows, logits_stride, k)))
+      return SAI_EWORKSPACE;
+  }
+  const int st = sai_paged_logits(q_fp8, weights, kv_cache, num_blocks, block_table, bt_stride, context_lens,
+                                  batch, next_n, logits, logits_stride, row_len_out, row_req_out, true,
+                                  use_hist ? hist : nullptr, stream);
+  if (st != SAI_OK) return st;
+  if (!use_hist)
+    return topk_rows_slots(logits, logits_stride, row_len_out, row_req_out, block_table, bt_stride, batch,
+                           (int32_t)rows, k, out_idx, out_slots, workspace, workspace_bytes, stream);
+  const bool vec = (logits_stride % 4 == 0) && aligned16p(logits);
+  launch_hist_sel(sh.vpt, vec, (unsigned)rows, logits, logits_stride, row_len_out, k, out_idx,
+                  SlotMap{row_req_out, block_table, bt_stride, batch, out_slots}, hist, stream);
+  return hipGetLastError() == hipSuccess ? SAI_OK : SAI_ELAUNCH;
 }

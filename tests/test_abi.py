@@ -39,7 +39,7 @@ def test_header_declares_the_boundary():
         "paged_mqa_logits", "paged_mqa_logits_visible", "mqa_logits", "mqa_logits_chunked", "topk_workspace_bytes", "topk_rows",
         "topk_to_global_slots", "topk_rows_slots", "topk_rows_slots_noalloc", "mla_cache_write",
         "sparse_mla_workspace_bytes",
-        "sparse_mla_decode"])
+        "sparse_mla_decode", "paged_mqa_topk_slots", "paged_mqa_topk_hist_bytes"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -121,6 +121,38 @@ def test_topk_rows_slots_noalloc_host_validation(lib):
     assert f(fake, 65536, fake, fake, fake, 1024, 256, -3, 2048, fake, fake, nul) == SAI_EINVAL
     assert f(fake, -1, fake, fake, fake, 1024, 256, 3, 2048, fake, fake, nul) == SAI_EINVAL
     assert f(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul) == SAI_OK
+
+
+def test_paged_mqa_topk_slots_host_checks(lib):
+    """The fused decode step: which shapes take a histogram, its size, and
+    argument errors returned before any launch."""
+    assert binding.paged_mqa_topk_hist_bytes(128, 4096) == 128 * 1024 * 4
+    assert binding.paged_mqa_topk_hist_bytes(511, 16384) == 511 * 1024 * 4
+    assert binding.paged_mqa_topk_hist_bytes(512, 4096) == 0       # many rows: segmented path
+    assert binding.paged_mqa_topk_hist_bytes(64, 16385) == 0       # wide rows: segmented path
+    assert binding.paged_mqa_topk_hist_bytes(0, 4096) == 0
+    assert binding.paged_mqa_topk_hist_bytes(64, 0) == 0
+    nul, fake = ctypes.c_void_p(0), ctypes.c_void_p(4096)
+    f = lib.paged_mqa_topk_slots
+
+    def call(batch=2, next_n=1, stride=256, k=64, hist=fake, hist_bytes=2 * 4096, logits=fake,
+             row_len=fake, row_req=fake, slots=fake, ws=nul, ws_bytes=0):
+        return f(fake, fake, fake, 10, fake, 4, fake, batch, next_n, logits, stride, row_len, row_req, k,
+                 fake, slots, hist, hist_bytes, ws, ws_bytes, nul)
+
+    assert call(batch=0) == SAI_OK
+    assert call(batch=-1) == SAI_EINVAL
+    assert call(next_n=5) == SAI_EUNSUPPORTED
+    assert call(k=0) == SAI_EUNSUPPORTED
+    assert call(k=2049) == SAI_EUNSUPPORTED
+    assert call(row_len=nul) == SAI_EINVAL          # both row outputs are required here
+    assert call(row_req=nul) == SAI_EINVAL
+    assert call(slots=nul) == SAI_EINVAL
+    assert call(logits=nul) == SAI_EINVAL
+    assert call(stride=0) == SAI_EINVAL
+    assert call(hist_bytes=2 * 4096 - 4) == SAI_EWORKSPACE
+    # rows wider than 16384 columns take the segmented selection, which needs workspace
+    assert call(stride=65536, hist=nul, hist_bytes=0, k=2048) == SAI_EWORKSPACE
 
 
 def test_fused_producer_host_checks(lib):
