@@ -57,9 +57,9 @@ PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "paged_mqa_logits_decode_b64_c
 MLA_PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "sparse_mla_decode_b64_h128_counters.txt")
 # committed PMC traffic summaries per (workload, kernel), each keyed by the
 # hash of the sources the kernel is built from
-DECODE_SOURCES = ("logits.hip", "score_mfma.h", "sai_device.h")
+DECODE_SOURCES = ("logits.hip", "score_mfma.h", "sai_device.h", "indexer_internal.h")
 PREFILL_SOURCES = ("prefill.hip", "score_mfma.h", "sai_device.h")
-TOPK_SOURCES = ("topk.hip", "sai_device.h")
+TOPK_SOURCES = ("topk.hip", "sai_device.h", "indexer_internal.h")
 MLA_SOURCES = ("mla.hip", "sai_device.h")
 PREFILL_COUNTERS = {"prefill_8192": os.path.join(ROOT, "profiles", "mqa_logits_prefill_8192_counters.txt")}
 TOPK_COUNTERS = {

@@ -5,7 +5,7 @@
   HBM traffic:    python -m sparse_attention_indexer_paged_amd.profile_summary traffic \\
                       --fetch <fetch ..._counter_collection.csv> --write <write ..._counter_collection.csv> \\
                       --kernel paged_logits_kernel --copy-bytes 268435456 \\
-                      [--sources logits.hip,score_mfma.h,sai_device.h] \\
+                      [--sources logits.hip,score_mfma.h,sai_device.h,indexer_internal.h] \\
                       --command "<both rocprofv3 commands>" --out <txt>
   counters:       python -m sparse_attention_indexer_paged_amd.profile_summary counters \\
                       --csv <..._counter_collection.csv> --kernel prefill_logits_kernel \\
@@ -156,7 +156,7 @@ def main():
     t.add_argument("--kernel", default="paged_logits_kernel")
     t.add_argument("--copy-kernel", default="copyBuffer")
     t.add_argument("--copy-bytes", type=int, default=256 << 20)
-    t.add_argument("--sources", default="logits.hip,score_mfma.h,sai_device.h",
+    t.add_argument("--sources", default="logits.hip,score_mfma.h,sai_device.h,indexer_internal.h",
                    help="kernel sources (csrc/) whose hash the summary records")
     t.add_argument("--command", required=True)
     t.add_argument("--out", required=True)
