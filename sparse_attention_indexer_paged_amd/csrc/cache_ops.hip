@@ -59,6 +59,36 @@ struct Rope {
   int half;  // rope_dim / 2
 };
 
+// The table entries of pairs j0 .. j0+N-1 of row p (0 <= p < rows), every
+// load issued before any is used: pairs past the row's half re-read its
+// last entry (the caller ignores them), so the loads are unconditional and
+// go out together instead of one round trip per pair.
+// When half is a multiple of 4 (and j0 too) the entries come as 16-byte
+// loads of whole groups of four.
+template <int N>
+__device__ __forceinline__ void rope_load(const Rope& rope, int64_t p, int j0, float (&c)[N], float (&s)[N]) {
+  static_assert(N % 4 == 0, "groups of four pairs");
+  const float* cr = rope.cos_t + p * rope.half;
+  const float* sr = rope.sin_t + p * rope.half;
+  if ((rope.half & 3) == 0) {
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const int j = min(j0 + i, rope.half - 4);
+      const float4 cv = *reinterpret_cast<const float4*>(cr + j);
+      const float4 sv = *reinterpret_cast<const float4*>(sr + j);
+      c[i] = cv.x; c[i + 1] = cv.y; c[i + 2] = cv.z; c[i + 3] = cv.w;
+      s[i] = sv.x; s[i + 1] = sv.y; s[i + 2] = sv.z; s[i + 3] = sv.w;
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const int j = min(j0 + i, rope.half - 1);
+      c[i] = cr[j];
+      s[i] = sr[j];
+    }
+  }
+}
+
 // ---------------------------------------------------------------- K1
 // 16 lanes per token row: lane i of the group holds values [8i, 8i+8), i.e.
 // rotary pairs 4i .. 4i+3.  One 256-thread workgroup writes 16 tokens.
@@ -91,12 +121,11 @@ __global__ __launch_bounds__(256) void k_cache_write_kernel(
   if constexpr (ROPE) {
     pos_ok = p >= 0 && p < rope.rows;
     if (live && pos_ok) {
+      float c[4], sn[4];
+      rope_load<4>(rope, p, 4 * sub, c, sn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int j = 4 * sub + i;
-        if (j < rope.half)
-          rope_pair(x[2 * i], x[2 * i + 1], rope.cos_t[p * rope.half + j], rope.sin_t[p * rope.half + j]);
-      }
+      for (int i = 0; i < 4; ++i)
+        if (4 * sub + i < rope.half) rope_pair(x[2 * i], x[2 * i + 1], c[i], sn[i]);
     }
   }
   float amax = 0.0f;
@@ -184,30 +213,40 @@ __global__ __launch_bounds__(256) void q_quant_kernel(
     const uint16_t* __restrict__ q, const float* __restrict__ wts, uint8_t* __restrict__ q8,
     float* __restrict__ w_eff, float* __restrict__ q_scale, Rope rope) {
   __shared__ float s_amax[4];
+  __shared__ float s_cs[2][ROPE ? 64 : 1];  // the token's cos and sin table row
   const int64_t row = blockIdx.x;
   const int t = threadIdx.x;
   const uint16_t* src = q + row * (kHeads * kDim) + t * 32;
+  uint4 raw[4];
+#pragma unroll
+  for (int v = 0; v < 4; ++v) raw[v] = *reinterpret_cast<const uint4*>(src + v * 8);
+  // The token's table row goes to LDS (threads 0..half-1 load the
+  // cosines, 64..64+half-1 the sines) while the row's loads are in flight.
+  bool pos_ok = true;
+  if constexpr (ROPE) {
+    const int64_t p = rope.pos[row];
+    pos_ok = p >= 0 && p < rope.rows;
+    const int64_t pc = pos_ok ? p : 0;
+    if (t < 64 && t < rope.half) s_cs[0][t] = rope.cos_t[pc * rope.half + t];
+    else if (t >= 64 && t < 128 && t - 64 < rope.half) s_cs[1][t - 64] = rope.sin_t[pc * rope.half + t - 64];
+  }
   float x[32];
 #pragma unroll
   for (int v = 0; v < 4; ++v) {
-    uint4 raw = *reinterpret_cast<const uint4*>(src + v * 8);
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+    const uint32_t w[4] = {raw[v].x, raw[v].y, raw[v].z, raw[v].w};
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       x[v * 8 + 2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
       x[v * 8 + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
     }
   }
-  bool pos_ok = true;
   if constexpr (ROPE) {
-    const int64_t p = rope.pos[row];
-    pos_ok = p >= 0 && p < rope.rows;
+    __syncthreads();  // the table row
     if (pos_ok) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int j = 16 * (t & 3) + i;
-        if (j < rope.half)
-          rope_pair(x[2 * i], x[2 * i + 1], rope.cos_t[p * rope.half + j], rope.sin_t[p * rope.half + j]);
+        if (j < rope.half) rope_pair(x[2 * i], x[2 * i + 1], s_cs[0][j], s_cs[1][j]);
       }
     }
   }
