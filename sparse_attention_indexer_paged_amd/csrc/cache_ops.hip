@@ -134,11 +134,13 @@ __global__ __launch_bounds__(256) void k_cache_write_kernel(
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
   float scale = fp8_scale(amax);
+  float y[8];
+  quotients_by_scale(x, scale, y);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(x[i] / scale) << (8 * i);
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(y[i]) << (8 * i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(x[4 + i] / scale) << (8 * i);
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(y[4 + i]) << (8 * i);
   if (!pos_ok) {
     lo = hi = 0x7F7F7F7Fu;
     scale = __uint_as_float(0x7FC00000u);
@@ -258,12 +260,14 @@ __global__ __launch_bounds__(256) void q_quant_kernel(
   __syncthreads();
   amax = fmaxf(fmaxf(s_amax[0], s_amax[1]), fmaxf(s_amax[2], s_amax[3]));
   float scale = fp8_scale(amax);
+  float y[32];
+  quotients_by_scale(x, scale, y);
   uint32_t packed[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     uint32_t pk = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) pk |= f32_to_e4m3fn(x[4 * i + j] / scale) << (8 * j);
+    for (int j = 0; j < 4; ++j) pk |= f32_to_e4m3fn(y[4 * i + j]) << (8 * j);
     packed[i] = pos_ok ? pk : 0x7F7F7F7Fu;
   }
   if (!pos_ok) scale = __uint_as_float(0x7FC00000u);

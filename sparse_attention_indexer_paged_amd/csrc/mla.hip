@@ -50,11 +50,13 @@ __global__ __launch_bounds__(256) void mla_cache_write_kernel(
 #pragma unroll
   for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
   const float scale = fp8_scale(amax);
+  float y[8];
+  quotients_by_scale(x, scale, y);
   uint32_t lo = 0, hi = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(x[i] / scale) << (8 * i);
+  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(y[i]) << (8 * i);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(x[4 + i] / scale) << (8 * i);
+  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(y[4 + i]) << (8 * i);
   uint8_t* e = cache + (slot / block_size) * block_stride + (slot % block_size) * kMlaEntry;
   *reinterpret_cast<uint2*>(e + lane * 8) = make_uint2(lo, hi);
   if ((lane & 15) == 0) *reinterpret_cast<float*>(e + kMlaScaleOff + 4 * (lane >> 4)) = scale;

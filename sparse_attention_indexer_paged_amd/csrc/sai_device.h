@@ -49,6 +49,34 @@ __device__ __forceinline__ float fp8_scale(float amax) {
   return fmaxf(amax * (1.0f / 448.0f), 1.17549435e-38f);
 }
 
+// y[i] = fl32(x[i] / s), the correctly rounded quotients.  For a scale
+// 2^-93 <= s <= FLT_MAX they come from r = fl32(1 / s) by Markstein's
+// correction (P. Markstein, "Computation of elementary functions on the IBM
+// RISC System/6000 processor", IBM J. Res. Dev. 34(1), 1990): q = fl(x r)
+// is within an ulp of x / s, the residual x - s q is then exact in one fused
+// multiply-add, and fl(q + (x - s q) r) is the correctly rounded quotient.
+// The residual is a multiple of 2^(e - 46) for |x| in [2^e, 2^(e + 1)),
+// exact as long as e >= -103; a smaller x has a quotient below 2^-10 (as
+// s >= 2^-93), which every float32 near it rounds to the same e4m3 code,
+// zero.  The result takes the sign of x, so that a zero keeps its own sign
+// (the correction would turn -0 into +0).  Other scales take the IEEE
+// division.
+template <int N>
+__device__ __forceinline__ void quotients_by_scale(const float (&x)[N], float s, float (&y)[N]) {
+  if (s >= 0x1p-93f && s <= 3.40282347e38f) {
+    const float r = 1.0f / s;
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const float q = x[i] * r;
+      // the sign of x: a zero x gives a zero of its own sign, as x / s does
+      y[i] = __builtin_copysignf(__builtin_fmaf(__builtin_fmaf(-q, s, x[i]), r, q), x[i]);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < N; ++i) y[i] = x[i] / s;
+  }
+}
+
 // Order-preserving float -> uint32 key (larger float, larger key).  -0.0 is
 // folded onto +0.0 so the two tie.  Every NaN (either sign, any payload)
 // gets key 0, below -inf (key 0x007FFFFF): NaNs rank last and tie with each

@@ -53,7 +53,7 @@ def _rows(width, seed, tile=128, limit=None):
     """Rows of `width` bf16 values in tiles of `tile` (one quantiser scale
     each: 128 for the K row and the MLA tile, the whole token for the
     query), one (maximum, value) pair per tile: the maximum, the value with
-    both signs, and small filler values."""
+    both signs, -0 and +0, and small filler values."""
     pairs = _pairs()[:limit]
     rng = np.random.default_rng(seed)
     tiles = width // tile
@@ -64,6 +64,7 @@ def _rows(width, seed, tile=128, limit=None):
         fill = synth.f32_to_bf16_bits((rng.random(tile - 3) * amax / 64).astype(np.float32))
         out[t, :3] = [ab, xb, xb | 0x8000]
         out[t, 3:] = fill | ((rng.random(tile - 3) < 0.5).astype(np.uint16) << 15)
+        out[t, 3:5] = [0x8000, 0x0000]             # -0 and +0 beside nonzero values: codes 0x80, 0x00
         out[t] = out[t][rng.permutation(tile)]
     for t in range(len(pairs), out.shape[0]):      # padding tiles reuse the first pair
         out[t] = out[0]
