@@ -90,65 +90,71 @@ __device__ __forceinline__ void rope_load(const Rope& rope, int64_t p, int j0, f
 }
 
 // ---------------------------------------------------------------- K1
-// 16 lanes per token row: lane i of the group holds values [8i, 8i+8), i.e.
-// rotary pairs 4i .. 4i+3.  One 256-thread workgroup writes 16 tokens.
-// With ROPE the first 2*half values are rotated by the token's position
-// before the quantiser sees them; a position outside the table writes NaN
-// codes and a NaN scale.
+// 8 lanes per token row: lane i of the group holds values [16i, 16i+16)
+// (two 16-byte loads in flight per lane), i.e. rotary pairs 8i .. 8i+7.
+// One 256-thread workgroup writes 32 tokens.  With ROPE the first 2*half
+// values are rotated by the token's position before the quantiser sees
+// them; a position outside the table writes NaN codes and a NaN scale.
 template <bool ROPE>
 __global__ __launch_bounds__(256) void k_cache_write_kernel(
     const uint16_t* __restrict__ k, int64_t row_stride, const int64_t* __restrict__ slots,
     int64_t n, uint8_t* __restrict__ cache, int64_t num_blocks, Rope rope) {
-  const int64_t tok = (int64_t)blockIdx.x * 16 + (threadIdx.x >> 4);
-  const int sub = threadIdx.x & 15;
+  const int64_t tok = (int64_t)blockIdx.x * 32 + (threadIdx.x >> 3);
+  const int sub = threadIdx.x & 7;
   const bool live = tok < n;
-  uint4 raw = make_uint4(0, 0, 0, 0);
+  uint4 raw[2] = {make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)};
   int64_t slot = -1;
   int64_t p = 0;
   if (live) {
-    raw = *reinterpret_cast<const uint4*>(k + tok * row_stride + sub * 8);
+    raw[0] = *reinterpret_cast<const uint4*>(k + tok * row_stride + sub * 16);
+    raw[1] = *reinterpret_cast<const uint4*>(k + tok * row_stride + sub * 16 + 8);
     slot = slots[tok];
     if (ROPE) p = rope.pos[tok];
   }
-  float x[8];
-  const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+  float x[16];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    x[2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
-    x[2 * i + 1] = bf16_to_f32(w[i] >> 16);
+  for (int h = 0; h < 2; ++h) {
+    const uint32_t w[4] = {raw[h].x, raw[h].y, raw[h].z, raw[h].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[8 * h + 2 * i] = bf16_to_f32(w[i] & 0xFFFFu);
+      x[8 * h + 2 * i + 1] = bf16_to_f32(w[i] >> 16);
+    }
   }
   bool pos_ok = true;
   if constexpr (ROPE) {
     pos_ok = p >= 0 && p < rope.rows;
-    if (live && pos_ok) {
-      float c[4], sn[4];
-      rope_load<4>(rope, p, 4 * sub, c, sn);
+    if (live && pos_ok && 8 * sub < rope.half) {
+      float c[8], sn[8];
+      rope_load<8>(rope, p, 8 * sub, c, sn);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        if (4 * sub + i < rope.half) rope_pair(x[2 * i], x[2 * i + 1], c[i], sn[i]);
+      for (int i = 0; i < 8; ++i)
+        if (8 * sub + i < rope.half) rope_pair(x[2 * i], x[2 * i + 1], c[i], sn[i]);
     }
   }
   float amax = 0.0f;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) amax = fmaxf(amax, fabsf(x[i]));
+  for (int i = 0; i < 16; ++i) amax = fmaxf(amax, fabsf(x[i]));
 #pragma unroll
-  for (int o = 8; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 16));
+  for (int o = 4; o > 0; o >>= 1) amax = fmaxf(amax, __shfl_xor(amax, o, 8));
   float scale = fp8_scale(amax);
-  float y[8];
+  float y[16];
   quotients_by_scale(x, scale, y);
-  uint32_t lo = 0, hi = 0;
+  uint32_t pk[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(y[i]) << (8 * i);
+  for (int q = 0; q < 4; ++q) {
+    pk[q] = 0;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(y[4 + i]) << (8 * i);
+    for (int i = 0; i < 4; ++i) pk[q] |= f32_to_e4m3fn(y[4 * q + i]) << (8 * i);
+  }
   if (!pos_ok) {
-    lo = hi = 0x7F7F7F7Fu;
+    pk[0] = pk[1] = pk[2] = pk[3] = 0x7F7F7F7Fu;
     scale = __uint_as_float(0x7FC00000u);
   }
   if (!live || slot < 0 || slot >= num_blocks * kBlock) return;
   uint8_t* blk = cache + (slot / kBlock) * kBlockBytes;
   const int off = (int)(slot % kBlock);
-  *reinterpret_cast<uint2*>(blk + off * kDim + sub * 8) = make_uint2(lo, hi);
+  *reinterpret_cast<uint4*>(blk + off * kDim + sub * 16) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
   if (sub == 0) *reinterpret_cast<float*>(blk + kValueBytes + 4 * off) = scale;
 }
 
@@ -160,7 +166,7 @@ extern "C" int indexer_k_cache_write(const void* k_bf16, int64_t k_row_stride,
   if (k_row_stride < kDim || (k_row_stride & 7)) return SAI_EINVAL;
   if (!k_bf16 || !slot_mapping || !kv_cache || !aligned16(k_bf16) || !aligned16(kv_cache))
     return SAI_EINVAL;
-  const int64_t grid = (n + 15) / 16;
+  const int64_t grid = (n + 31) / 32;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   launch(k_cache_write_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,
          (const uint16_t*)k_bf16, k_row_stride, slot_mapping, n, (uint8_t*)kv_cache, num_blocks,
@@ -190,7 +196,7 @@ extern "C" int indexer_k_rope_cache_write(const void* k_bf16, int64_t k_row_stri
   if (k_row_stride < kDim || (k_row_stride & 7)) return SAI_EINVAL;
   if (!k_bf16 || !slot_mapping || !kv_cache || !aligned16(k_bf16) || !aligned16(kv_cache))
     return SAI_EINVAL;
-  const int64_t grid = (n + 15) / 16;
+  const int64_t grid = (n + 31) / 32;
   if (grid > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   if (rope_dim == 0)
     launch(k_cache_write_kernel<false>, dim3((unsigned)grid), dim3(256), 0, stream,

@@ -34,9 +34,11 @@ __global__ __launch_bounds__(256) void mla_cache_write_kernel(
   const int64_t tok = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   const int lane = threadIdx.x & 63;
   if (tok >= n) return;  // wave-uniform
+  // every load goes out before the slot is known: the values, the RoPE
+  // piece and the slot arrive in one round trip
   const int64_t slot = slots[tok];
-  if (slot < 0 || slot >= num_slots) return;
   const uint4 raw = *reinterpret_cast<const uint4*>(kv + tok * kv_stride + lane * 8);
+  const uint32_t pe = *reinterpret_cast<const uint32_t*>(kpe + tok * kpe_stride + 2 * (lane & 31));
   float x[8];
   const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
 #pragma unroll
@@ -57,12 +59,11 @@ __global__ __launch_bounds__(256) void mla_cache_write_kernel(
   for (int i = 0; i < 4; ++i) lo |= f32_to_e4m3fn(y[i]) << (8 * i);
 #pragma unroll
   for (int i = 0; i < 4; ++i) hi |= f32_to_e4m3fn(y[4 + i]) << (8 * i);
+  if (slot < 0 || slot >= num_slots) return;
   uint8_t* e = cache + (slot / block_size) * block_stride + (slot % block_size) * kMlaEntry;
   *reinterpret_cast<uint2*>(e + lane * 8) = make_uint2(lo, hi);
   if ((lane & 15) == 0) *reinterpret_cast<float*>(e + kMlaScaleOff + 4 * (lane >> 4)) = scale;
-  if (lane < kMlaRope / 2)
-    *reinterpret_cast<uint32_t*>(e + kMlaRopeOff + 4 * lane) =
-        *reinterpret_cast<const uint32_t*>(kpe + tok * kpe_stride + 2 * lane);
+  if (lane < kMlaRope / 2) *reinterpret_cast<uint32_t*>(e + kMlaRopeOff + 4 * lane) = pe;
 }
 
 }  // namespace
