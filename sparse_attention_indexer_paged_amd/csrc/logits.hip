@@ -55,6 +55,7 @@ constexpr int kDecodeDepth = SAI_DECODE_DEPTH;
 constexpr int kDecodeCap = SAI_DECODE_CAP;
 constexpr int kStageFloats = SAI_DECODE_STAGE;
 constexpr int kFillCols = 256;  // -inf fill piece: one float4 per lane
+constexpr int kLateFill = 2;    // fill pieces a wave issues after its first K loads
 constexpr int64_t kPlainStoreMaxBytes = 8 << 20;  // decode logits written with plain stores
 
 
@@ -113,11 +114,11 @@ __device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], 
 // global store sits in the loop, so no K load ever queues behind one.
 // With HIST every visible logit of row r also counts into bin (order key >>
 // 22) of the wave's LDS histogram hist[r * kHistBins ..] (an LDS atomic).
-template <int NN, int DEPTH, int NS, bool HIST>
+template <int NN, int DEPTH, int NS, bool HIST, typename Hook>
 __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, int64_t num_blocks,
                                             const uint8_t* __restrict__ dummy, int myblk,
                                             const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                            int ctx, float* st, int slots, int* hist) {
+                                            int ctx, float* st, int slots, int* hist, Hook& hook) {
   const int lane = threadIdx.x & 63;
   KFrag buf[DEPTH];
   bool okb[DEPTH];
@@ -135,6 +136,7 @@ __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, i
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     if (i + DEPTH - 1 < NS) issue(i + DEPTH - 1);
+    if (i == 0) hook();  // work that can go out while the first block loads
     const KFrag& cur = buf[i % DEPTH];
     const int col = (c0 + i) * kBlock + lane;
 #pragma unroll
@@ -151,16 +153,16 @@ __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, i
 }
 
 // Calls score_group with NS == n (1 <= n <= NS; n is wave-uniform).
-template <int NN, int DEPTH, int NS, bool HIST>
+template <int NN, int DEPTH, int NS, bool HIST, typename Hook>
 __device__ __forceinline__ void dispatch_group(int n, const uint8_t* __restrict__ cache, int64_t num_blocks,
                                                const uint8_t* __restrict__ dummy, int myblk,
                                                const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                               int ctx, float* st, int slots, int* hist) {
+                                               int ctx, float* st, int slots, int* hist, Hook& hook) {
   if (n == NS || NS == 1) {
-    score_group<NN, DEPTH, NS, HIST>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots, hist);
+    score_group<NN, DEPTH, NS, HIST>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots, hist, hook);
   } else if constexpr (NS > 1) {
     dispatch_group<NN, DEPTH, NS - 1, HIST>(n, cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots,
-                                            hist);
+                                            hist, hook);
   }
 }
 
@@ -264,11 +266,6 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   const int w = __builtin_amdgcn_readfirstlane(lg * 4 + wid);
   const int nw = G * 4;
 
-  for (int r = w * 64 + lane; r < batch * NN; r += nw * 64) {
-    const int b = r / NN, j = r - b * NN;
-    if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
-    if (row_req_out) row_req_out[r] = b;
-  }
 
   // last b in [0, batch) with pre[b] <= u (pre non-decreasing, pre[0] = 0
   // <= u; called wave-uniformly): a coarse ballot over every cs-th entry,
@@ -309,31 +306,54 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     }
   };
 
-  // The -inf fill needs only the context lengths, so its stores go out
-  // before the K stream starts and complete while the first loads wait.
+  // Stores that need only the context lengths: the row lengths and
+  // requests, and the -inf fill, split into pieces of kFillCols columns and
+  // shared out like the units.  A wave with at most kLateFill pieces issues
+  // them (and the row lengths) right after its first block's K loads, from
+  // the first group's ring: they then complete while those loads are in
+  // flight instead of delaying the block-id load ahead of them (a wait for
+  // a load also waits for every store issued before it).  A wave with more
+  // fill (wide rows of short requests) issues it first, so it drains while
+  // the block ids load.  A wave without units issues them after its empty
+  // loop.
   const int F = s_fill[batch];
-  int f = (int)((int64_t)F * w / nw);
+  const int f0 = (int)((int64_t)F * w / nw);
   const int f1 = (int)((int64_t)F * (w + 1) / nw);
-  if (f < f1) {
-    int b = find(s_fill, f);
-    const float ninf = __uint_as_float(kNegInfBits);
-    const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
-    for (; f < f1; ++f) {
-      while (s_fill[b + 1] <= f) ++b;
-      const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
+  auto fill = [&]() {
+    if (f0 < f1) {
+      int b = find(s_fill, f0);
+      const float ninf = __uint_as_float(kNegInfBits);
+      const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
+      for (int f = f0; f < f1; ++f) {
+        while (s_fill[b + 1] <= f) ++b;
+        const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
 #pragma unroll
-      for (int r = 0; r < NN; ++r) {
-        float* row = logits + ((int64_t)b * NN + r) * stride;
-        if (vec) {
-          if (col + 4 * lane < stride) store_logit4<NT>(row + col + 4 * lane, ninf4);
-        } else {
+        for (int r = 0; r < NN; ++r) {
+          float* row = logits + ((int64_t)b * NN + r) * stride;
+          if (vec) {
+            if (col + 4 * lane < stride) store_logit4<NT>(row + col + 4 * lane, ninf4);
+          } else {
 #pragma unroll
-          for (int k = 0; k < kFillCols / 64; ++k)
-            if (col + 64 * k + lane < stride) store_logit<NT>(row + col + 64 * k + lane, ninf);
+            for (int k = 0; k < kFillCols / 64; ++k)
+              if (col + 64 * k + lane < stride) store_logit<NT>(row + col + 64 * k + lane, ninf);
+          }
         }
       }
     }
-  }
+  };
+  const bool fill_first = f1 - f0 > kLateFill;
+  if (fill_first) fill();
+  bool pending = true;
+  auto early_stores = [&]() {
+    if (!pending) return;
+    pending = false;
+    for (int r = w * 64 + lane; r < batch * NN; r += nw * 64) {
+      const int b = r / NN, j = r - b * NN;
+      if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
+      if (row_req_out) row_req_out[r] = b;
+    }
+    if (!fill_first) fill();
+  };
   const int U = s_unit[batch];
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
@@ -368,9 +388,10 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       }
     }
     dispatch_group<NN, DEPTH, kCap, HIST>(n, cache, num_blocks, q, myblk, qa, wf, c0, s_ctx[b],
-                                          stage + (u - sa) * kBlock, kSlots, s_hist);
+                                          stage + (u - sa) * kBlock, kSlots, s_hist, early_stores);
     u += n;
   }
+  early_stores();
   if (sa < u1) flush(sa, u1, bs);
   if constexpr (HIST) {
     if (qb >= 0) flush_hist(qb);
