@@ -366,6 +366,22 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   int qb = -1;
   v8i qa[NN][4];
   float4 wf[NN][4];
+  // The block ids of the wave's units, 64 at a time, in one vector load:
+  // lane i holds the id of unit ub + i (its request found by walking the
+  // prefix from b, the request of unit ub).  Groups take theirs by lane
+  // shuffle, so only every 64th unit waits for a block-id round trip.
+  int ub = u0, ids = -1;
+  auto load_ids = [&]() {
+    const int uu = ub + lane;
+    int id = -1;
+    if (uu < u1) {
+      int bl = b;
+      while (s_unit[bl + 1] <= uu) ++bl;
+      id = bt[(int64_t)bl * bt_stride + (uu - s_unit[bl])];
+    }
+    ids = id;
+  };
+  if (u < u1) load_ids();
   while (u < u1) {
     while (s_unit[b + 1] <= u) ++b;
     const int n = min(kCap, min(u1, s_unit[b + 1]) - u);  // 1..kCap units of request b
@@ -375,7 +391,12 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       bs = b;
     }
     const int c0 = u - s_unit[b];
-    const int myblk = lane < n ? bt[(int64_t)b * bt_stride + c0 + lane] : -1;
+    if (u + n > ub + 64) {  // wave-uniform
+      ub = u;
+      load_ids();
+    }
+    const int sid = __shfl(ids, (u - ub + lane) & 63, 64);
+    const int myblk = lane < n ? sid : -1;
     if (b != qb) {
       if constexpr (HIST) {
         if (qb >= 0) flush_hist(qb);
