@@ -55,7 +55,6 @@ constexpr int kDecodeDepth = SAI_DECODE_DEPTH;
 constexpr int kDecodeCap = SAI_DECODE_CAP;
 constexpr int kStageFloats = SAI_DECODE_STAGE;
 constexpr int kFillCols = 256;  // -inf fill piece: one float4 per lane
-constexpr int kLateFill = 2;    // fill pieces a wave issues after its first K loads
 constexpr int64_t kPlainStoreMaxBytes = 8 << 20;  // decode logits written with plain stores
 
 
@@ -114,11 +113,11 @@ __device__ __forceinline__ float score_row(const KFrag& kf, const v8i (&qa)[4], 
 // global store sits in the loop, so no K load ever queues behind one.
 // With HIST every visible logit of row r also counts into bin (order key >>
 // 22) of the wave's LDS histogram hist[r * kHistBins ..] (an LDS atomic).
-template <int NN, int DEPTH, int NS, bool HIST, typename Hook>
+template <int NN, int DEPTH, int NS, bool HIST>
 __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, int64_t num_blocks,
                                             const uint8_t* __restrict__ dummy, int myblk,
                                             const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                            int ctx, float* st, int slots, int* hist, Hook& hook) {
+                                            int ctx, float* st, int slots, int* hist) {
   const int lane = threadIdx.x & 63;
   KFrag buf[DEPTH];
   bool okb[DEPTH];
@@ -136,7 +135,6 @@ __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, i
 #pragma unroll
   for (int i = 0; i < NS; ++i) {
     if (i + DEPTH - 1 < NS) issue(i + DEPTH - 1);
-    if (i == 0) hook();  // work that can go out while the first block loads
     const KFrag& cur = buf[i % DEPTH];
     const int col = (c0 + i) * kBlock + lane;
 #pragma unroll
@@ -153,16 +151,16 @@ __device__ __forceinline__ void score_group(const uint8_t* __restrict__ cache, i
 }
 
 // Calls score_group with NS == n (1 <= n <= NS; n is wave-uniform).
-template <int NN, int DEPTH, int NS, bool HIST, typename Hook>
+template <int NN, int DEPTH, int NS, bool HIST>
 __device__ __forceinline__ void dispatch_group(int n, const uint8_t* __restrict__ cache, int64_t num_blocks,
                                                const uint8_t* __restrict__ dummy, int myblk,
                                                const v8i (&qa)[NN][4], const float4 (&wf)[NN][4], int c0,
-                                               int ctx, float* st, int slots, int* hist, Hook& hook) {
+                                               int ctx, float* st, int slots, int* hist) {
   if (n == NS || NS == 1) {
-    score_group<NN, DEPTH, NS, HIST>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots, hist, hook);
+    score_group<NN, DEPTH, NS, HIST>(cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots, hist);
   } else if constexpr (NS > 1) {
     dispatch_group<NN, DEPTH, NS - 1, HIST>(n, cache, num_blocks, dummy, myblk, qa, wf, c0, ctx, st, slots,
-                                            hist, hook);
+                                            hist);
   }
 }
 
@@ -266,6 +264,11 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   const int w = __builtin_amdgcn_readfirstlane(lg * 4 + wid);
   const int nw = G * 4;
 
+  for (int r = w * 64 + lane; r < batch * NN; r += nw * 64) {
+    const int b = r / NN, j = r - b * NN;
+    if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
+    if (row_req_out) row_req_out[r] = b;
+  }
 
   // last b in [0, batch) with pre[b] <= u (pre non-decreasing, pre[0] = 0
   // <= u; called wave-uniformly): a coarse ballot over every cs-th entry,
@@ -306,54 +309,31 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
     }
   };
 
-  // Stores that need only the context lengths: the row lengths and
-  // requests, and the -inf fill, split into pieces of kFillCols columns and
-  // shared out like the units.  A wave with at most kLateFill pieces issues
-  // them (and the row lengths) right after its first block's K loads, from
-  // the first group's ring: they then complete while those loads are in
-  // flight instead of delaying the block-id load ahead of them (a wait for
-  // a load also waits for every store issued before it).  A wave with more
-  // fill (wide rows of short requests) issues it first, so it drains while
-  // the block ids load.  A wave without units issues them after its empty
-  // loop.
+  // The -inf fill needs only the context lengths, so its stores go out
+  // before the K stream starts and complete while the first loads wait.
   const int F = s_fill[batch];
-  const int f0 = (int)((int64_t)F * w / nw);
+  int f = (int)((int64_t)F * w / nw);
   const int f1 = (int)((int64_t)F * (w + 1) / nw);
-  auto fill = [&]() {
-    if (f0 < f1) {
-      int b = find(s_fill, f0);
-      const float ninf = __uint_as_float(kNegInfBits);
-      const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
-      for (int f = f0; f < f1; ++f) {
-        while (s_fill[b + 1] <= f) ++b;
-        const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
+  if (f < f1) {
+    int b = find(s_fill, f);
+    const float ninf = __uint_as_float(kNegInfBits);
+    const float4 ninf4 = make_float4(ninf, ninf, ninf, ninf);
+    for (; f < f1; ++f) {
+      while (s_fill[b + 1] <= f) ++b;
+      const int64_t col = (int64_t)(s_unit[b + 1] - s_unit[b]) * kBlock + (int64_t)(f - s_fill[b]) * kFillCols;
 #pragma unroll
-        for (int r = 0; r < NN; ++r) {
-          float* row = logits + ((int64_t)b * NN + r) * stride;
-          if (vec) {
-            if (col + 4 * lane < stride) store_logit4<NT>(row + col + 4 * lane, ninf4);
-          } else {
+      for (int r = 0; r < NN; ++r) {
+        float* row = logits + ((int64_t)b * NN + r) * stride;
+        if (vec) {
+          if (col + 4 * lane < stride) store_logit4<NT>(row + col + 4 * lane, ninf4);
+        } else {
 #pragma unroll
-            for (int k = 0; k < kFillCols / 64; ++k)
-              if (col + 64 * k + lane < stride) store_logit<NT>(row + col + 64 * k + lane, ninf);
-          }
+          for (int k = 0; k < kFillCols / 64; ++k)
+            if (col + 64 * k + lane < stride) store_logit<NT>(row + col + 64 * k + lane, ninf);
         }
       }
     }
-  };
-  const bool fill_first = f1 - f0 > kLateFill;
-  if (fill_first) fill();
-  bool pending = true;
-  auto early_stores = [&]() {
-    if (!pending) return;
-    pending = false;
-    for (int r = w * 64 + lane; r < batch * NN; r += nw * 64) {
-      const int b = r / NN, j = r - b * NN;
-      if (row_len_out) row_len_out[r] = max(s_ctx[b] - NN + j + 1, 0);
-      if (row_req_out) row_req_out[r] = b;
-    }
-    if (!fill_first) fill();
-  };
+  }
   const int U = s_unit[batch];
   const int u0 = (int)((int64_t)U * w / nw);
   const int u1 = (int)((int64_t)U * (w + 1) / nw);
@@ -366,22 +346,6 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
   int qb = -1;
   v8i qa[NN][4];
   float4 wf[NN][4];
-  // The block ids of the wave's units, 64 at a time, in one vector load:
-  // lane i holds the id of unit ub + i (its request found by walking the
-  // prefix from b, the request of unit ub).  Groups take theirs by lane
-  // shuffle, so only every 64th unit waits for a block-id round trip.
-  int ub = u0, ids = -1;
-  auto load_ids = [&]() {
-    const int uu = ub + lane;
-    int id = -1;
-    if (uu < u1) {
-      int bl = b;
-      while (s_unit[bl + 1] <= uu) ++bl;
-      id = bt[(int64_t)bl * bt_stride + (uu - s_unit[bl])];
-    }
-    ids = id;
-  };
-  if (u < u1) load_ids();
   while (u < u1) {
     while (s_unit[b + 1] <= u) ++b;
     const int n = min(kCap, min(u1, s_unit[b + 1]) - u);  // 1..kCap units of request b
@@ -391,12 +355,7 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       bs = b;
     }
     const int c0 = u - s_unit[b];
-    if (u + n > ub + 64) {  // wave-uniform
-      ub = u;
-      load_ids();
-    }
-    const int sid = __shfl(ids, (u - ub + lane) & 63, 64);
-    const int myblk = lane < n ? sid : -1;
+    const int myblk = lane < n ? bt[(int64_t)b * bt_stride + c0 + lane] : -1;
     if (b != qb) {
       if constexpr (HIST) {
         if (qb >= 0) flush_hist(qb);
@@ -409,10 +368,9 @@ __global__ __launch_bounds__(256) void paged_logits_kernel(
       }
     }
     dispatch_group<NN, DEPTH, kCap, HIST>(n, cache, num_blocks, q, myblk, qa, wf, c0, s_ctx[b],
-                                          stage + (u - sa) * kBlock, kSlots, s_hist, early_stores);
+                                          stage + (u - sa) * kBlock, kSlots, s_hist);
     u += n;
   }
-  early_stores();
   if (sa < u1) flush(sa, u1, bs);
   if constexpr (HIST) {
     if (qb >= 0) flush_hist(qb);
