@@ -767,6 +767,12 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   const int packed = ngt | (neq << 12);
   const int inc = wave_scan_dpp(packed);
   if (lane == 63) s_wsum[wid] = inc;
+  // One-pass rows write each winner's index and slot id from the thread that
+  // holds it (its output position is known once the counts are scanned), so
+  // the block-table row goes out with the counts; segment and merge passes
+  // stage their output in LDS and write it coalesced.
+  constexpr bool kDirect = !CIN && !COUT;
+  if constexpr (EARLY && kDirect) store_bt();
   __syncthreads();
   int ex = inc - packed;
 #pragma unroll
@@ -789,8 +795,12 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
           ++eq_b;
         }
         if ((unsigned)pos < (unsigned)k) {
-          s_h0[pos] = ccol[j];
-          if (COUT) s_h1[pos] = (int)ckey[j];
+          if constexpr (kDirect) {
+            emit(pos, ccol[j]);
+          } else {
+            s_h0[pos] = ccol[j];
+            if (COUT) s_h1[pos] = (int)ckey[j];
+          }
         }
       }
     }
@@ -807,11 +817,20 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
           ++eq_b;
         }
         if ((unsigned)pos < (unsigned)k) {
-          s_h0[pos] = column(e);
-          if (COUT) s_h1[pos] = (int)key[e];
+          if constexpr (kDirect) {
+            emit(pos, column(e));
+          } else {
+            s_h0[pos] = column(e);
+            if (COUT) s_h1[pos] = (int)key[e];
+          }
         }
       }
     }
+  }
+  if constexpr (kDirect) {
+    // past nwin (a row with fewer than k keys) the indices are -1
+    for (int j = nwin + tid; j < k; j += NT) emit(j, -1);
+    return;
   }
   if constexpr (EARLY) store_bt();
   __syncthreads();
