@@ -767,12 +767,14 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   const int packed = ngt | (neq << 12);
   const int inc = wave_scan_dpp(packed);
   if (lane == 63) s_wsum[wid] = inc;
-  // One-pass rows write each winner's index and slot id from the thread that
-  // holds it (its output position is known once the counts are scanned), so
-  // the block-table row goes out with the counts; segment and merge passes
-  // stage their output in LDS and write it coalesced.
-  constexpr bool kDirect = !CIN && !COUT;
-  if constexpr (EARLY && kDirect) store_bt();
+  // One-pass rows of the few-row launches write each winner's index and slot
+  // id from the thread that holds it (its output position is known once the
+  // counts are scanned), so the block-table row goes out with the counts.
+  // Many-row launches (whose outputs are large: scattered writes cost more
+  // than the barrier) and segment and merge passes stage their output in
+  // LDS and write it coalesced.
+  constexpr bool kDirect = EARLY && !CIN && !COUT;
+  if constexpr (kDirect) store_bt();
   __syncthreads();
   int ex = inc - packed;
 #pragma unroll
