@@ -290,11 +290,13 @@ int mqa_logits_chunked(const void* q_fp8, const float* weights, const void* k_fp
  *   out_idx  [rows, k] int32 (output)
  *   workspace / workspace_bytes: scratch of at least
  *   topk_workspace_bytes(rows, logits_stride, k) bytes (may be NULL if that
- *   is 0); contents need no initialisation.  Rows wider than 16384 columns
- *   are cut into 16384-column segments whose k winners (key and column) go
- *   to the workspace, 8 * rows * segments * k bytes, and are then merged;
- *   rows too wide for the merge (segments * k > 16384) need none.  A
- *   missing or short workspace returns SAI_EWORKSPACE and launches nothing.
+ *   is 0); contents need no initialisation.  Rows of at most 16384
+ *   columns, and of at most 65536 when rows < 512, are selected in one
+ *   pass and need none.  Other rows wider than 16384 columns are cut into
+ *   16384-column segments whose k winners (key and column) go to the
+ *   workspace, 8 * rows * segments * k bytes, and are then merged; rows too
+ *   wide for the merge (segments * k > 16384) need none.  A missing or
+ *   short workspace returns SAI_EWORKSPACE and launches nothing.
  */
 size_t topk_workspace_bytes(int32_t rows, int64_t logits_stride, int32_t k);
 int topk_rows(const float* logits, int64_t logits_stride, const int32_t* row_len,
@@ -354,8 +356,8 @@ int topk_rows_slots(const float* logits, int64_t logits_stride, const int32_t* r
  *               the two calls unchanged and leaves hist untouched.
  *   hist_bytes  its size; SAI_EWORKSPACE if it is used and smaller than
  *               paged_mqa_topk_hist_bytes(rows, logits_stride).
- *   workspace   as for topk_rows_slots (needed only for rows wider than
- *               16384 columns, which never use hist).
+ *   workspace   as for topk_rows_slots (needed only for rows cut into
+ *               segments, see topk_workspace_bytes; those never use hist).
  * Errors: those of both calls, all checked before anything is launched.
  * A histogram that is not zero before the call changes no result (the
  * selection checks its bound as it checks a sampled one), only the time.
@@ -381,13 +383,13 @@ size_t paged_mqa_topk_hist_bytes(int32_t rows, int64_t logits_stride);
  * hipMalloc, hipFree or any allocating routine.
  *
  * Same arguments (minus the workspace), outputs and errors as
- * topk_rows_slots.  Rows wider than 16384 columns keep their segment
- * candidates in a buffer built into the library: a file-scope device array
- * of SAI_NOALLOC_SCRATCH_BYTES (16 MiB) that each device holds from the
+ * topk_rows_slots.  Rows cut into segments keep their segment candidates
+ * in a buffer built into the library: a file-scope device array of
+ * SAI_NOALLOC_SCRATCH_BYTES (16 MiB) that each device holds from the
  * library's load until the process ends.  A problem whose
  * topk_workspace_bytes(rows, logits_stride, k) exceeds that returns
- * SAI_ESCRATCH and launches nothing (e.g. 256 rows of 65536 columns at
- * k = 2048 fit exactly; 257 do not).  The first call on a device resolves
+ * SAI_ESCRATCH and launches nothing (e.g. 128 rows of 131072 columns at
+ * k = 2048 fit exactly; 129 do not).  The first call on a device resolves
  * that device's array address (hipGetSymbolAddress, with the stream's
  * device made current for the lookup); the address is then kept.  Every
  * call on a device shares its one array, so calls that overlap on the same

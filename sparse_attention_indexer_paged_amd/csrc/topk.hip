@@ -18,9 +18,11 @@
 // with an exact radix select as the fallback.  On the 1024-thread shapes
 // the keys at or above the sample's bound (about 1.3 k of the row) are
 // first compacted into LDS in position order, so the later phases handle 4
-// keys per thread instead of 8-16.  Rows too wide for the
-// segment-and-merge plan take topk_row_kernel, which streams the row from
-// L2 for each of three radix rounds (11, 11, 10 key bits).
+// keys per thread instead of 8-16.  topk_wide_kernel takes rows of up to
+// 65536 columns whole when the launch has few rows (one workgroup per row,
+// no candidate round trip).  Rows too wide for the segment-and-merge plan
+// take topk_row_kernel, which streams the row from L2 for each of three
+// radix rounds (11, 11, 10 key bits).
 #include <atomic>
 #include <type_traits>
 
@@ -44,7 +46,96 @@ __device__ __forceinline__ void load4(const float* __restrict__ x, int i, int n,
   }
 }
 
-// VEC: rows are 16-byte aligned, so 4 consecutive columns load as one float4.
+// Exact top-k of one row of n > k columns read from memory, by NT
+// threads: three radix rounds over the row (11, 11, 10 key bits), each
+// re-reading it, then an ordered output pass that hands every winner's
+// output slot and column to emit(j, i).  LDS: hist holds kBins ints, scan
+// NT/64 + 1, sel 6.  VEC: rows are 16-byte aligned, so 4 consecutive
+// columns load as one float4.
+template <int NT, bool VEC, class Emit>
+__device__ __forceinline__ void stream_select(const float* __restrict__ x, int n, int k, int* hist,
+                                              int* scan, uint32_t (*sel)[2], Emit emit) {
+  static_assert(2 * NT >= kBins, "two bins per thread cover the histogram");
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0, pmask = 0;
+  int need = k;  // winners still to place among keys matching the prefix
+  const int shifts[3] = {21, 10, 0};
+  const uint32_t dmask[3] = {0x7FFu, 0x7FFu, 0x3FFu};
+  for (int round = 0; round < 3; ++round) {
+    const int sh = shifts[round];
+    const uint32_t dm = dmask[round];
+    const int nb = (int)dm + 1;
+    for (int i = tid; i < kBins; i += NT) hist[i] = 0;
+    if (tid == 0) sel[round][0] = sel[round][1] = 0;
+    __syncthreads();
+    for (int i = tid * 4; i < n; i += NT * 4) {
+      float v[4];
+      load4<VEC>(x, i, n, v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (i + e < n) {
+          const uint32_t key = f32_order_key(v[e]);
+          if ((key & pmask) == prefix) atomicAdd(&hist[(key >> sh) & dm], 1);
+        }
+      }
+    }
+    __syncthreads();
+    // thread t owns bins nb-1-2t and nb-2-2t (descending), scanned in thread order
+    const int bhi = nb - 1 - 2 * tid, blo = nb - 2 - 2 * tid;
+    const int hhi = bhi >= 0 ? hist[bhi] : 0;
+    const int hlo = blo >= 0 ? hist[blo] : 0;
+    int total;
+    const int before = block_exclusive_scan<NT>(hhi + hlo, scan, &total);
+    if (bhi >= 0 && before < need && need <= before + hhi) {
+      sel[round][0] = (uint32_t)bhi;
+      sel[round][1] = (uint32_t)before;
+    } else if (blo >= 0 && before + hhi < need && need <= before + hhi + hlo) {
+      sel[round][0] = (uint32_t)blo;
+      sel[round][1] = (uint32_t)(before + hhi);
+    }
+    __syncthreads();
+    prefix |= sel[round][0] << sh;
+    pmask |= dm << sh;
+    need -= (int)sel[round][1];
+  }
+  const uint32_t T = prefix;
+
+  // ordered output: tiles of NT*4 columns, thread t owns 4 consecutive
+  int gt_run = 0, eq_run = 0;
+  for (int base = 0; base < n; base += NT * 4) {
+    const int i = base + tid * 4;
+    float v[4];
+    load4<VEC>(x, i, n, v);
+    uint32_t key[4];
+    int ngt = 0, neq = 0;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      key[e] = f32_order_key(v[e]);
+      const bool in = i + e < n;
+      ngt += (in && key[e] > T);
+      neq += (in && key[e] == T);
+    }
+    int tot;
+    const int ex = block_exclusive_scan<NT>(ngt | (neq << 16), scan, &tot);
+    int gt_b = gt_run + (ex & 0xFFFF), eq_b = eq_run + (ex >> 16);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (i + e >= n) break;
+      if (key[e] > T) {
+        const int pos = gt_b + min(eq_b, need);
+        if ((unsigned)pos < (unsigned)k) emit(pos, i + e);
+        ++gt_b;
+      } else if (key[e] == T) {
+        const int pos = gt_b + eq_b;
+        if (eq_b < need && (unsigned)pos < (unsigned)k) emit(pos, i + e);
+        ++eq_b;
+      }
+    }
+    gt_run += tot & 0xFFFF;
+    eq_run += tot >> 16;
+  }
+}
+
 template <bool VEC>
 __global__ __launch_bounds__(kThreads) void topk_row_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
@@ -61,85 +152,8 @@ __global__ __launch_bounds__(kThreads) void topk_row_kernel(
     for (int j = tid; j < k; j += kThreads) o[j] = j < n ? j : -1;
     return;
   }
-  const float* x = logits + (int64_t)r * stride;
-
-  uint32_t prefix = 0, pmask = 0;
-  int need = k;  // winners still to place among keys matching the prefix
-  const int shifts[3] = {21, 10, 0};
-  const uint32_t dmask[3] = {0x7FFu, 0x7FFu, 0x3FFu};
-  for (int round = 0; round < 3; ++round) {
-    const int sh = shifts[round];
-    const uint32_t dm = dmask[round];
-    const int nb = (int)dm + 1;
-    for (int i = tid; i < kBins; i += kThreads) s_hist[i] = 0;
-    if (tid == 0) s_sel[round][0] = s_sel[round][1] = 0;
-    __syncthreads();
-    for (int i = tid * 4; i < n; i += kThreads * 4) {
-      float v[4];
-      load4<VEC>(x, i, n, v);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (i + e < n) {
-          const uint32_t key = f32_order_key(v[e]);
-          if ((key & pmask) == prefix) atomicAdd(&s_hist[(key >> sh) & dm], 1);
-        }
-      }
-    }
-    __syncthreads();
-    // thread t owns bins nb-1-2t and nb-2-2t (descending), scanned in thread order
-    const int bhi = nb - 1 - 2 * tid, blo = nb - 2 - 2 * tid;
-    const int hhi = bhi >= 0 ? s_hist[bhi] : 0;
-    const int hlo = blo >= 0 ? s_hist[blo] : 0;
-    int total;
-    const int before = block_exclusive_scan<kThreads>(hhi + hlo, s_scan, &total);
-    if (bhi >= 0 && before < need && need <= before + hhi) {
-      s_sel[round][0] = (uint32_t)bhi;
-      s_sel[round][1] = (uint32_t)before;
-    } else if (blo >= 0 && before + hhi < need && need <= before + hhi + hlo) {
-      s_sel[round][0] = (uint32_t)blo;
-      s_sel[round][1] = (uint32_t)(before + hhi);
-    }
-    __syncthreads();
-    prefix |= s_sel[round][0] << sh;
-    pmask |= dm << sh;
-    need -= (int)s_sel[round][1];
-  }
-  const uint32_t T = prefix;
-
-  // ordered output: tiles of kThreads*4 columns, thread t owns 4 consecutive
-  int gt_run = 0, eq_run = 0;
-  for (int base = 0; base < n; base += kThreads * 4) {
-    const int i = base + tid * 4;
-    float v[4];
-    load4<VEC>(x, i, n, v);
-    uint32_t key[4];
-    int ngt = 0, neq = 0;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      key[e] = f32_order_key(v[e]);
-      const bool in = i + e < n;
-      ngt += (in && key[e] > T);
-      neq += (in && key[e] == T);
-    }
-    int tot;
-    const int ex = block_exclusive_scan<kThreads>(ngt | (neq << 16), s_scan, &tot);
-    int gt_b = gt_run + (ex & 0xFFFF), eq_b = eq_run + (ex >> 16);
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      if (i + e >= n) break;
-      if (key[e] > T) {
-        const int pos = gt_b + min(eq_b, need);
-        if ((unsigned)pos < (unsigned)k) o[pos] = i + e;
-        ++gt_b;
-      } else if (key[e] == T) {
-        const int pos = gt_b + eq_b;
-        if (eq_b < need && (unsigned)pos < (unsigned)k) o[pos] = i + e;
-        ++eq_b;
-      }
-    }
-    gt_run += tot & 0xFFFF;
-    eq_run += tot >> 16;
-  }
+  stream_select<kThreads, VEC>(logits + (int64_t)r * stride, n, k, s_hist, s_scan, s_sel,
+                               [&](int j, int32_t i) { o[j] = i; });
 }
 
 // Inclusive wave64 prefix sum on DPP: shifts of 1, 2, 4, 8 within each row of
@@ -172,6 +186,7 @@ __device__ __forceinline__ uint32_t wave_max_dpp(uint32_t v) {
 #define SAI_TOPK_MANY_WGS 512
 #endif
 constexpr int kSegCols = 16384;              // columns per segment of a wide row
+constexpr int kWideCols = 65536;             // widest row one workgroup takes whole
 constexpr int kManyWgs = SAI_TOPK_MANY_WGS;  // from this many workgroups on, use small ones
 constexpr int kCandMax = 64;               // threshold-bin keys resolved by brute force
 constexpr int kCompCap = 4096;             // keys at or above the sampled bound kept in LDS
@@ -193,7 +208,9 @@ struct BinPick {
 // loads; a DPP scan of the lane sums in lane order (descending bins) finds
 // the lane holding the need-th element, which walks its bins downwards; the
 // result is broadcast from that lane.
-template <int NB>
+// ROLLED: the walk is a loop over groups of 4 bins (fewer registers, for
+// callers that hold many values in registers across the pick).
+template <int NB, bool ROLLED = false>
 __device__ __forceinline__ BinPick pick_bin(const int* hist, int need, bool clamp_to_total = false) {
   constexpr int PER = NB / 64;
   const int lane = threadIdx.x & 63;
@@ -213,7 +230,7 @@ __device__ __forceinline__ BinPick pick_bin(const int* hist, int need, bool clam
   // branch-free walk from the lane's top bin down: the bins whose running
   // total stays below need are the ones above the chosen bin
   int run = 0, nbelow = 0, sum_above = 0;
-#pragma unroll
+#pragma unroll(ROLLED ? 1 : PER / 4)
   for (int j = PER - 4; j >= 0; j -= 4) {
     const int4 v = *reinterpret_cast<const int4*>(hist + lo + j);
     const int h4[4] = {v.w, v.z, v.y, v.x};  // bins lo+j+3 .. lo+j
@@ -848,14 +865,295 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   }
 }
 
+// One-pass selection of rows wider than one segment (up to kWideCols
+// columns) in launches of few rows: one 1024-thread workgroup per row, the
+// row held in registers once, with no candidate round trip through memory.
+//
+// Thread t holds the float4 groups t, t + 1024, ... of the row (coalesced
+// loads, and rows of any length spread over all threads).  2048 evenly
+// spaced columns, loaded beside the row, are the sample: the 11-bit digit
+// histogram of their keys, then the next 11 bits of the samples in the
+// chosen digit, give key_lo, the sampled bound on the k-th largest key with
+// the same 30 % rank margin, to 22 key bits.  The logits at or above it
+// (about 1.3 k) are compacted into LDS in any order (a wave reserves its
+// slots with one atomic), and the linear histogram, the threshold-bin rank
+// and the output run on 4 compacted keys per thread.  The output marks the
+// winners in two column bitmaps (above T, equal to T); each thread then owns
+// 64 consecutive columns of them, and a scan of the per-thread counts puts
+// every winner at its ascending-column slot.  A row the compacted keys
+// cannot settle (more than kCompCap keys at or above the bound, fewer than
+// k, an unusable value range or threshold bin) takes the exact radix select
+// over the row in memory instead.
+template <bool VEC>
+__global__ __launch_bounds__(kThreads) void topk_wide_kernel(
+    const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
+    int32_t k, int32_t* __restrict__ out_idx, SlotMap sm) {
+  constexpr int NT = kThreads, kWaves = NT / 64, G = kWideCols / 4 / NT, CPER = kCompCap / NT;
+  constexpr int S = 2048;  // sampled columns
+  constexpr int kMapWords = kWideCols / 32;
+  __shared__ __align__(16) int s_h0[kBins];  // sample digits
+  __shared__ __align__(16) int s_h1[kBins];  // linear bins
+  __shared__ __align__(16) int s_h2[kBins];  // next 11 bits of the samples in the chosen digit
+  __shared__ __align__(16) uint32_t s_ck[kCompCap];  // compacted keys, then the winner bitmaps
+  __shared__ uint16_t s_cp[kCompCap];                // their columns
+  static_assert(2 * kMapWords <= kCompCap, "the bitmaps fit the key list");
+  uint32_t* const s_bgt = s_ck;              // bit c: column c is above T
+  uint32_t* const s_beq = s_ck + kMapWords;  // bit c: column c equals T
+  __shared__ uint32_t s_cand[kCandMax];
+  __shared__ int s_wsum[kWaves + 1];
+  __shared__ uint32_t s_misc[3];  // [0] threshold-bin keys, [1] largest sampled key, [2] compacted
+  __shared__ int s_pick[3];
+  extern __shared__ int32_t s_bt[];  // [bt_stride] when bt_lds
+
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  const int r = blockIdx.x;
+  const int n = (int)min((int64_t)max(row_len[r], 0), stride);
+  const int32_t req = sm.out ? sm.row_req[r] : 0;
+  const bool bt_lds = sm.out && sm.bt_stride <= kBtLds;
+  if (bt_lds) {  // published by the first barrier below
+    const bool okr = req >= 0 && req < sm.batch;
+    for (int c = tid; c < (int)sm.bt_stride; c += NT)
+      s_bt[c] = okr ? sm.bt[(int64_t)req * sm.bt_stride + c] : -1;
+  }
+  auto emit = [&](int j, int32_t i) {  // final index j of row r
+    out_idx[(int64_t)r * k + j] = i;
+    if (sm.out) {
+      int32_t slot = -1;
+      if (bt_lds) {
+        if (i >= 0 && i / 64 < (int)sm.bt_stride) {
+          const int32_t blk = s_bt[i / 64];
+          slot = blk >= 0 ? blk * 64 + i % 64 : -1;
+        }
+      } else {
+        slot = slot_of(sm, req, i);
+      }
+      sm.out[(int64_t)r * k + j] = slot;
+    }
+  };
+  if (n <= k) {  // every column wins
+    __syncthreads();
+    for (int j = tid; j < k; j += NT) emit(j, j < n ? j : -1);
+    return;
+  }
+  const float* x = logits + (int64_t)r * stride;
+
+  // the row: group g = tid + j*NT holds columns 4g..4g+3; groups past the
+  // row are not loaded, and columns past n read as NaN (never selected)
+  const int ng = (n + 3) >> 2;
+  float v[4 * G];
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (j * NT < ng) {
+      const int g = min(tid + j * NT, ng - 1);
+      if (VEC) {  // 4g + 3 < stride: the stride is a multiple of 4 and >= n
+        const float4 f = *reinterpret_cast<const float4*>(x + 4 * g);
+        v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[4 * j + i] = x[min(4 * g + i, n - 1)];
+      }
+    }
+  }
+  // the sample: columns floor(s*n/S), s < S, two per thread
+  const float sv0 = x[(int)(((uint32_t)tid * (uint32_t)n) / S)];
+  const float sv1 = x[(int)(((uint32_t)(tid + NT) * (uint32_t)n) / S)];
+  for (int i = tid; i < kBins; i += NT) {
+    s_h0[i] = 0;
+    s_h1[i] = 0;
+    s_h2[i] = 0;
+  }
+  if (tid < 3) s_misc[tid] = 0u;
+  const float qnan = __uint_as_float(0x7FC00000u);
+#pragma unroll
+  for (int j = 0; j < G; ++j) {
+    if (j * NT >= ng) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[4 * j + i] = qnan;
+    } else if ((j + 1) * NT * 4 > n) {  // the groups that hold column n - 1
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * (tid + j * NT) + i >= n) v[4 * j + i] = qnan;
+    }
+  }
+  __syncthreads();  // histograms clear; s_bt published
+
+  auto pick = [&](const int* h, int nd, bool clamp = false) {
+    if (wid == 0) {
+      const BinPick p = pick_bin<kBins, true>(h, nd, clamp);
+      if (lane == 0) {
+        s_pick[0] = p.bin;
+        s_pick[1] = p.above;
+        s_pick[2] = p.found;
+      }
+    }
+    __syncthreads();
+    return BinPick{s_pick[0], s_pick[1], s_pick[2] != 0};
+  };
+  auto fallback = [&]() {
+    __syncthreads();  // every wave is past its reads of the histograms and candidates
+    stream_select<NT, VEC>(x, n, k, s_h1, s_wsum, reinterpret_cast<uint32_t(*)[2]>(s_cand), emit);
+  };
+
+  // 1. key_lo: the m-th largest sampled key to 22 bits (all S samples are
+  // columns of the row; NaNs have key 1)
+  const uint32_t sk0 = sel_key(sv0), sk1 = sel_key(sv1);
+  atomicAdd(&s_h0[sk0 >> 21], 1);
+  atomicAdd(&s_h0[sk1 >> 21], 1);
+  const uint32_t wmax = wave_max_dpp(max(sk0, sk1));
+  if (lane == 63) atomicMax(&s_misc[1], wmax);
+  __syncthreads();
+  // k*S*13 < 2^26 and n*10 < 2^20: 32-bit arithmetic
+  const int m = min(S, (int)(((uint32_t)k * S * 13u + (uint32_t)n * 10u - 1u) / ((uint32_t)n * 10u)) + 8);
+  const BinPick pc = pick(s_h0, m);
+  if ((sk0 >> 21) == (uint32_t)pc.bin) atomicAdd(&s_h2[(sk0 >> 10) & 0x7FFu], 1);
+  if ((sk1 >> 21) == (uint32_t)pc.bin) atomicAdd(&s_h2[(sk1 >> 10) & 0x7FFu], 1);
+  __syncthreads();
+  const BinPick pf = pick(s_h2, m - pc.above);
+  const uint32_t key_lo = ((uint32_t)pc.bin << 21) | (pf.found ? (uint32_t)pf.bin << 10 : 0u);
+  const uint32_t key_top = max(s_misc[1], key_lo);
+  const float v_lo = order_key_value(key_lo);
+  const float range = order_key_value(key_top) - v_lo;
+  const float scale = 2048.0f / range;
+  auto fbin = [&](uint32_t kk) {
+    return (int)fminf((order_key_value(kk) - v_lo) * scale, (float)(kBins - 1));
+  };
+  // a finite, non-empty range (anything else: the radix select)
+  if (!(pc.found && isfinite(v_lo) && isfinite(range) && range > 0.0f && isfinite(scale))) {
+    fallback();
+    return;
+  }
+
+  // 2. compaction of the logits >= v_lo, i.e. the keys >= key_lo (v_lo is
+  // the finite float whose key is key_lo; NaN compares false)
+  {
+    int cnt = 0;
+#pragma unroll
+    for (int e = 0; e < 4 * G; ++e) cnt += v[e] >= v_lo;
+    const int incl = wave_scan_dpp(cnt);
+    int wbase = 0;
+    if (lane == 63) wbase = (int)atomicAdd(&s_misc[2], (uint32_t)incl);
+    int off = __builtin_amdgcn_readlane(wbase, 63) + incl - cnt;
+#pragma unroll
+    for (int j = 0; j < G; ++j) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (v[4 * j + i] >= v_lo) {
+          if (off < kCompCap) {
+            s_ck[off] = sel_key(v[4 * j + i]);
+            s_cp[off] = (uint16_t)(4 * (tid + j * NT) + i);
+          }
+          ++off;
+        }
+      }
+    }
+  }
+  __syncthreads();
+  const int total = (int)s_misc[2];
+  if (total < k || total > kCompCap) {
+    fallback();
+    return;
+  }
+  uint32_t ckey[CPER];
+  int32_t ccol[CPER];
+#pragma unroll
+  for (int j = 0; j < CPER; ++j) {
+    const int i = tid + j * NT;
+    ckey[j] = i < total ? s_ck[i] : 0u;
+    ccol[j] = i < total ? (int32_t)s_cp[i] : -1;
+  }
+
+  // 3. linear bins over [v_lo, v_top]; the threshold bin's keys ranked by
+  // brute force give T
+#pragma unroll
+  for (int j = 0; j < CPER; ++j)
+    if (ckey[j] != 0u) atomicAdd(&s_h1[fbin(ckey[j])], 1);
+  __syncthreads();
+  // every thread has its compacted keys: the key list becomes the bitmaps
+  for (int i = tid; i < 2 * kMapWords; i += NT) s_ck[i] = 0u;
+  const BinPick p1 = pick(s_h1, k);
+  if (p1.found) {
+#pragma unroll
+    for (int j = 0; j < CPER; ++j) {
+      if (ckey[j] != 0u && fbin(ckey[j]) == p1.bin) {
+        const uint32_t sl = atomicAdd(&s_misc[0], 1u);
+        if (sl < (uint32_t)kCandMax) s_cand[sl] = ckey[j];
+      }
+    }
+  }
+  __syncthreads();
+  uint32_t T = 0;
+  int need = 0;  // keys equal to T that win (lowest columns first)
+  bool ok = p1.found && s_misc[0] <= (uint32_t)kCandMax;
+  if (ok) {  // every wave computes the same from the same LDS contents
+    const int nc = (int)s_misc[0];
+    const int need1 = k - p1.above;
+    const uint32_t c = lane < nc ? s_cand[lane] : 0u;
+    int gt = 0, ge = 0;
+    for (int j = 0; j < nc; ++j) {
+      const uint32_t cj = __builtin_amdgcn_readlane(c, j);
+      gt += cj > c;
+      ge += cj >= c;
+    }
+    const uint64_t hm = __ballot(lane < nc && gt < need1 && need1 <= ge);
+    if (hm != 0) {
+      const int src = (int)__builtin_ctzll(hm);
+      T = __builtin_amdgcn_readlane(c, src);
+      need = need1 - __builtin_amdgcn_readlane(gt, src);
+    } else {
+      ok = false;
+    }
+  }
+  if (!ok) {
+    fallback();
+    return;
+  }
+
+  // 4. ordered output through the bitmaps: thread t owns columns
+  // [64t, 64t + 64); counts packed as (equal << 12) | above (above-T totals
+  // stay below k <= 2048, equal totals at most kCompCap)
+#pragma unroll
+  for (int j = 0; j < CPER; ++j) {
+    if (ckey[j] > T) atomicOr(&s_bgt[ccol[j] >> 5], 1u << (ccol[j] & 31));
+    else if (ckey[j] == T && ckey[j] != 0u) atomicOr(&s_beq[ccol[j] >> 5], 1u << (ccol[j] & 31));
+  }
+  __syncthreads();
+  const uint2 g2 = reinterpret_cast<const uint2*>(s_bgt)[tid];
+  const uint2 e2 = reinterpret_cast<const uint2*>(s_beq)[tid];
+  const uint64_t gm = (uint64_t)g2.x | ((uint64_t)g2.y << 32);
+  const uint64_t em = (uint64_t)e2.x | ((uint64_t)e2.y << 32);
+  const int packed = __popcll(gm) | (__popcll(em) << 12);
+  const int inc = wave_scan_dpp(packed);
+  if (lane == 63) s_wsum[wid] = inc;
+  __syncthreads();
+  int ex = inc - packed;
+#pragma unroll
+  for (int w = 0; w < kWaves; ++w) ex += w < wid ? s_wsum[w] : 0;
+  int gt_b = ex & 0xFFF, eq_b = ex >> 12;
+  uint64_t all = gm | em;
+  while (all != 0) {
+    const int b = (int)__builtin_ctzll(all);
+    all &= all - 1;
+    int pos = -1;
+    if ((gm >> b) & 1u) {
+      pos = gt_b + min(eq_b, need);
+      ++gt_b;
+    } else {
+      if (eq_b < need) pos = gt_b + eq_b;
+      ++eq_b;
+    }
+    if ((unsigned)pos < (unsigned)k) emit(pos, 64 * tid + b);
+  }
+}
+
 // How topk_rows handles a row pitch: rows up to kSegCols columns are
-// selected in one pass; wider rows are cut into kSegCols-column segments
-// whose winners are merged by a second pass, as long as a row's candidate
-// lists fit one workgroup (16384 slots); wider still take the streaming
-// kernel.  Workgroup shape: with at least kManyWgs workgroups the smallest
-// of 256 or 512 threads x 4..32 positions that holds the work, so several
-// workgroups share a CU; with fewer, 1024 threads x 4..16 positions, which
-// shortens each workgroup's chain.
+// selected in one pass; in launches of fewer than kManyWgs rows, rows up to
+// kWideCols columns too (topk_wide_kernel); other wider rows are cut into
+// kSegCols-column segments whose winners are merged by a second pass, as
+// long as a row's candidate lists fit one workgroup (16384 slots); wider
+// still take the streaming kernel.  Workgroup shape: with at least kManyWgs
+// workgroups the smallest of 256 or 512 threads x 4..32 positions that
+// holds the work, so several workgroups share a CU; with fewer, 1024
+// threads x 4..16 positions, which shortens each workgroup's chain.
 struct Shape {
   int nt, vpt;  // nt == 0: no register-resident shape holds the work
 };
@@ -881,14 +1179,16 @@ struct TopkPlan {
   Shape seg;    // segment pass
   Shape merge;  // merge pass
   bool stream;  // neither: the streaming kernel
+  bool wide;    // one pass of topk_wide_kernel
 };
 
 TopkPlan plan_for(int64_t stride, int k, int64_t rows) {
-  if (stride <= kSegCols) return {shape_for(stride, rows, 16), 0, {0, 0}, {0, 0}, false};
+  if (stride <= kSegCols) return {shape_for(stride, rows, 16), 0, {0, 0}, {0, 0}, false, false};
+  if (stride <= kWideCols && rows < kManyWgs) return {{0, 0}, 0, {0, 0}, {0, 0}, false, true};
   const int64_t nseg = (stride + kSegCols - 1) / kSegCols;
   const Shape merge = shape_for(nseg * k, rows);
-  if (merge.nt == 0) return {{0, 0}, 0, {0, 0}, {0, 0}, true};
-  return {{0, 0}, (int)nseg, shape_for(kSegCols, rows * nseg), merge, false};
+  if (merge.nt == 0) return {{0, 0}, 0, {0, 0}, {0, 0}, true, false};
+  return {{0, 0}, (int)nseg, shape_for(kSegCols, rows * nseg), merge, false, false};
 }
 
 template <int NT, int VPT, bool CIN, bool COUT>
@@ -977,7 +1277,15 @@ int topk_impl(const float* logits, int64_t logits_stride, const int32_t* row_len
     if (!workspace || workspace_bytes < need) return SAI_EWORKSPACE;
     if ((int64_t)rows * p.nseg > 0x7FFFFFFF) return SAI_EUNSUPPORTED;
   }
-  if (p.one.nt) {
+  if (p.wide) {
+    const size_t dyn = sm.out && sm.bt_stride <= kBtLds ? (size_t)sm.bt_stride * sizeof(int32_t) : 0;
+    if (vec)
+      launch(topk_wide_kernel<true>, dim3(ur), dim3(kThreads), dyn, stream, logits, logits_stride,
+             row_len, k, out_idx, sm);
+    else
+      launch(topk_wide_kernel<false>, dim3(ur), dim3(kThreads), dyn, stream, logits, logits_stride,
+             row_len, k, out_idx, sm);
+  } else if (p.one.nt) {
     launch_shape<false, false>(p.one, vec, ur, logits, logits_stride, row_len, k, 1, nullptr, nullptr,
                                out_idx, nullptr, nullptr, sm, stream);
   } else if (p.nseg > 0) {

@@ -83,10 +83,15 @@ def test_validation_needs_no_gpu(lib):
 
 
 def test_topk_workspace_query(lib):
-    # rows up to 16384 wide need none; wider rows keep k (key, column)
-    # candidates per 16384-column segment; past 8 segments none again
+    # rows up to 16384 wide need none, nor rows up to 65536 wide in
+    # launches of fewer than 512 rows (one pass); other wider rows keep k
+    # (key, column) candidates per 16384-column segment; past 8 segments
+    # none again
     assert binding.topk_workspace_bytes(64, 16384, 2048) == 0
-    assert binding.topk_workspace_bytes(256, 65536, 2048) == 256 * 4 * 2048 * 8
+    assert binding.topk_workspace_bytes(256, 65536, 2048) == 0
+    assert binding.topk_workspace_bytes(511, 65536, 2048) == 0
+    assert binding.topk_workspace_bytes(512, 65536, 2048) == 512 * 4 * 2048 * 8
+    assert binding.topk_workspace_bytes(64, 65537, 2048) == 64 * 5 * 2048 * 8
     assert binding.topk_workspace_bytes(32, 131072, 2048) == 32 * 8 * 2048 * 8
     assert binding.topk_workspace_bytes(32, 131073, 2048) == 0
     assert binding.topk_workspace_bytes(4, 300000, 100) == 4 * 19 * 100 * 8
@@ -101,7 +106,7 @@ def test_topk_rows_slots_host_validation(lib):
     assert lib.topk_rows_slots(fake, 256, fake, fake, fake, 4, 2, 3, 8, fake, nul, nul, 0, nul) == SAI_EINVAL
     assert lib.topk_rows_slots(fake, 256, fake, fake, fake, -1, 2, 3, 8, fake, fake, nul, 0, nul) == SAI_EINVAL
     assert lib.topk_rows_slots(fake, 256, fake, fake, fake, 4, 2, 3, 0, fake, fake, nul, 0, nul) == SAI_EUNSUPPORTED
-    assert lib.topk_rows_slots(fake, 65536, fake, fake, fake, 4, 2, 3, 2048, fake, fake, nul, 0, nul) == SAI_EWORKSPACE
+    assert lib.topk_rows_slots(fake, 131072, fake, fake, fake, 4, 2, 3, 2048, fake, fake, nul, 0, nul) == SAI_EWORKSPACE
     assert lib.topk_rows_slots(nul, 16, nul, nul, nul, 0, 0, 0, 8, nul, nul, nul, 0, nul) == SAI_OK
 
 
@@ -112,9 +117,9 @@ def test_topk_rows_slots_noalloc_host_validation(lib):
     fake = ctypes.c_void_p(4096)
     nul = ctypes.c_void_p(0)
     f = lib.topk_rows_slots_noalloc
-    assert binding.topk_workspace_bytes(256, 65536, 2048) == 16 << 20
-    assert f(fake, 65536, fake, fake, fake, 1024, 256, 257, 2048, fake, fake, nul) == -5   # SAI_ESCRATCH
-    assert f(fake, 131072, fake, fake, fake, 2048, 32, 129, 2048, fake, fake, nul) == -5   # 128 fit
+    assert binding.topk_workspace_bytes(128, 131072, 2048) == 16 << 20
+    assert f(fake, 131072, fake, fake, fake, 2048, 32, 129, 2048, fake, fake, nul) == -5   # SAI_ESCRATCH
+    assert f(fake, 65536, fake, fake, fake, 1024, 256, 512, 2048, fake, fake, nul) == -5   # 32 MiB
     assert binding.status_string(-5).startswith("SAI_ESCRATCH")
     assert f(fake, 65536, fake, fake, fake, 1024, 256, 3, 0, fake, fake, nul) == SAI_EUNSUPPORTED
     assert f(fake, 65536, fake, fake, fake, 1024, 256, 3, 2049, fake, fake, nul) == SAI_EUNSUPPORTED
@@ -151,8 +156,8 @@ def test_paged_mqa_topk_slots_host_checks(lib):
     assert call(logits=nul) == SAI_EINVAL
     assert call(stride=0) == SAI_EINVAL
     assert call(hist_bytes=2 * 4096 - 4) == SAI_EWORKSPACE
-    # rows wider than 16384 columns take the segmented selection, which needs workspace
-    assert call(stride=65536, hist=nul, hist_bytes=0, k=2048) == SAI_EWORKSPACE
+    # rows cut into segments need workspace
+    assert call(stride=131072, hist=nul, hist_bytes=0, k=2048) == SAI_EWORKSPACE
 
 
 def test_fused_producer_host_checks(lib):
@@ -176,8 +181,8 @@ def test_fused_producer_host_checks(lib):
 def test_topk_missing_workspace_is_rejected(lib):
     fake = ctypes.c_void_p(4096)
     nul = ctypes.c_void_p(0)
-    assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, nul, 0, nul) == SAI_EWORKSPACE
-    assert lib.topk_rows(fake, 65536, fake, 8, 2048, fake, fake, 100, nul) == SAI_EWORKSPACE
+    assert lib.topk_rows(fake, 131072, fake, 8, 2048, fake, nul, 0, nul) == SAI_EWORKSPACE
+    assert lib.topk_rows(fake, 131072, fake, 8, 2048, fake, fake, 100, nul) == SAI_EWORKSPACE
 
 
 def test_time_next_launch_host_checks(lib):

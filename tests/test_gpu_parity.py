@@ -331,11 +331,13 @@ def test_topk_many_rows_small_workgroups(rows, width):
     assert np.array_equal(slots.cpu().numpy(), O.topk_to_global_slots(want, req, bt))
 
 
-def test_topk_unaligned_stride():
-    _say("topk_rows: odd stride")
+@pytest.mark.parametrize("width", [4099, 40001])
+def test_topk_unaligned_stride(width):
+    _say(f"topk_rows: odd stride {width}")
     rng = np.random.default_rng(4)
-    L = rng.standard_normal((5, 4099)).astype(np.float32)
-    lens = np.array([4099, 3000, 2049, 4098, 100], np.int32)
+    L = rng.standard_normal((5, width)).astype(np.float32)
+    L[3] = np.round(L[3] * 2)                              # heavy ties: the exact fallbacks
+    lens = np.array([width, 3000, 2049, width - 1, 100], np.int32)
     full = torch.from_numpy(L).to(DEV)
     got = sai.topk_rows(full, torch.from_numpy(lens).to(DEV), 2048)
     assert np.array_equal(got.cpu().numpy(), O.topk_rows(L, lens, 2048))
@@ -367,6 +369,7 @@ def test_topk_rows_slots_matches_the_two_calls(width):
     rows, k = 7, 2048
     L = rng.standard_normal((rows, width)).astype(np.float32)
     L[3, ::5] = 1.5                                          # ties at the threshold
+    L[1] = np.round(L[1] * 2)                                # heavy ties: the exact fallbacks
     lens = np.array([width, width - 1, 2048, min(width, 3000), 5, 0, width // 2], np.int32)
     nblk = -(-width // 64)
     bt = rng.permutation(4 * nblk)[: 3 * nblk].reshape(3, nblk).astype(np.int32)
@@ -696,7 +699,8 @@ def test_producers_graph_capture_replays_match_eager():
             assert torch.equal(a, b)
 
 
-@pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000])
+@pytest.mark.parametrize("width", [1000, 4096, 4097, 8192, 16385, 32768, 32769, 40000, 65536, 65537,
+                                   100000])
 def test_topk_every_row_width_path(width):
     """Row widths on both sides of each register-resident size and the
     streaming kernel beyond them; rows of every length class."""

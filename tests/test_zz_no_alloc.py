@@ -69,27 +69,29 @@ def _check(case, k, label):
 
 
 def test_noalloc_matches_workspace_entry_on_shrinking_calls():
-    # 256 rows x 4 segments x 2048 candidates x 8 B fill the buffer exactly;
+    # 128 rows x 8 segments x 2048 candidates x 8 B fill the buffer exactly;
     # then fewer rows and segments, then a smaller k over the same buffer
-    _check(_case(256, 65536, seed=1), 2048, "call 1 (whole buffer)")
-    _check(_case(8, 40000, seed=2), 2048, "call 2 (smaller)")
-    _check(_case(5, 33000, seed=3), 300, "call 3 (smaller k)")
+    _check(_case(128, 131072, seed=1), 2048, "call 1 (whole buffer)")
+    _check(_case(8, 100000, seed=2), 2048, "call 2 (smaller)")
+    _check(_case(5, 70000, seed=3), 300, "call 3 (smaller k)")
 
 
 def test_noalloc_one_pass_and_streaming_rows():
-    # rows that need no scratch: one pass (<= 16384 columns) and rows past
-    # the segment-and-merge limit (streaming kernel, slots mapped afterwards)
+    # rows that need no scratch: one pass (<= 16384 columns, and <= 65536 in
+    # launches of few rows) and rows past the segment-and-merge limit
+    # (streaming kernel, slots mapped afterwards)
     _check(_case(64, 16384, seed=4), 2048, "one pass")
+    _check(_case(16, 65536, seed=6), 2048, "one pass, wide rows")
     _check(_case(3, 140000, seed=5), 2048, "streaming")
 
 
 def test_noalloc_rejects_problems_past_the_buffer():
-    L = torch.zeros((257, 65536), dtype=torch.float32, device=DEV)
-    ln = torch.full((257,), 65536, dtype=torch.int32, device=DEV)
-    rq = torch.zeros((257,), dtype=torch.int32, device=DEV)
-    bt = torch.zeros((1, 1024), dtype=torch.int32, device=DEV)
-    idx = torch.full((257, 2048), 7, dtype=torch.int32, device=DEV)
-    slots = torch.full((257, 2048), 7, dtype=torch.int32, device=DEV)
+    L = torch.zeros((129, 131072), dtype=torch.float32, device=DEV)
+    ln = torch.full((129,), 131072, dtype=torch.int32, device=DEV)
+    rq = torch.zeros((129,), dtype=torch.int32, device=DEV)
+    bt = torch.zeros((1, 2048), dtype=torch.int32, device=DEV)
+    idx = torch.full((129, 2048), 7, dtype=torch.int32, device=DEV)
+    slots = torch.full((129, 2048), 7, dtype=torch.int32, device=DEV)
     assert _noalloc(L, ln, rq, bt, 2048, idx, slots) == -5      # SAI_ESCRATCH, nothing launched
     torch.cuda.synchronize()
     assert (idx == 7).all() and (slots == 7).all()
