@@ -65,6 +65,7 @@ PREFILL_COUNTERS = {"prefill_8192": os.path.join(ROOT, "profiles", "mqa_logits_p
 TOPK_COUNTERS = {
     "decode_b64_ctx4k-16k": os.path.join(ROOT, "profiles", "topk_rows_slots_decode_b64_counters.txt"),
     "prefill_8192": os.path.join(ROOT, "profiles", "topk_rows_slots_prefill_8192_counters.txt"),
+    "mtp_decode_b128_n2_ctx2k-64k": os.path.join(ROOT, "profiles", "topk_rows_slots_mtp_b128_n2_counters.txt"),
 }
 COPY_BYTES = 256 << 20
 BF16_PEAK_TFLOPS = 2500.0
