@@ -325,8 +325,13 @@ __device__ __forceinline__ int32_t slot_of(const SlotMap& sm, int32_t b, int32_t
 // row's histogram is read once and set back to zero for the next call.  A
 // wrong histogram costs speed, never exactness (the bound is checked like a
 // sampled one).
+//
+// Launches of many workgroups (without EARLY) are throughput-bound: they ask
+// the compiler for 8 waves per SIMD (at most 64 registers, so 2-8
+// workgroups share a CU instead of 1-2), and their bin picks walk the bins
+// in a loop, which needs far fewer registers than the unrolled walk.
 template <int NT, int VPT, bool VEC, bool CIN, bool COUT, bool EARLY, bool HIST = false>
-__global__ __launch_bounds__(NT) void topk_select_kernel(
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EARLY ? 1 : 8))) void topk_select_kernel(
     const float* __restrict__ logits, int64_t stride, const int32_t* __restrict__ row_len,
     int32_t k, int32_t nseg, const uint32_t* __restrict__ c_key, const int32_t* __restrict__ c_col,
     int32_t* __restrict__ out_idx, uint32_t* __restrict__ o_key, int32_t* __restrict__ o_col,
@@ -337,8 +342,8 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   // Compaction (see below) on the 1024-thread shapes with at least 8 keys
   // per thread: CPER = 4 compacted keys per thread, kCompCap in all.  (On
   // the many-workgroup 512-thread shapes it measured even or slower: 8192
-  // rows of <= 8192 even, the 4-segment MTP pass 52 -> 64 us, its extra
-  // registers costing a wave per SIMD.)
+  // rows of <= 8192 even, segment passes of 256 rows x 4 segments 52 -> 64
+  // us, its extra registers costing a wave per SIMD.)
   constexpr int CPER = kCompCap / NT;
   constexpr bool kComp = !CIN && NT == 1024 && VPT >= 2 * CPER;
   __shared__ __align__(16) int s_h0[kBins];
@@ -548,7 +553,7 @@ __global__ __launch_bounds__(NT) void topk_select_kernel(
   auto pick = [&](const int* h, int nd, auto nb_tag, bool clamp = false) {
     constexpr int NB = decltype(nb_tag)::value;
     if (wid == 0) {
-      const BinPick p = pick_bin<NB>(h, nd, clamp);
+      const BinPick p = pick_bin<NB, !EARLY>(h, nd, clamp);
       if (lane == 0) {
         s_pick[0] = p.bin;
         s_pick[1] = p.above;
@@ -1161,7 +1166,7 @@ struct Shape {
 // max_vpt: one-pass launches of many rows stop at 16 positions per thread
 // (then 1024 threads): 32-position shapes were slower there (16384-column
 // rows: 404 -> 286 us, 8192-column rows: 150 -> 140 us); segment passes keep
-// 32 (the 4-segment MTP pass: 50.6 us with 512 x 32, 56.1 with 1024 x 16).
+// 32 (256 rows x 4 segments: 50.6 us with 512 x 32, 56.1 with 1024 x 16).
 Shape shape_for(int64_t n, int64_t wgs, int max_vpt = 32) {
   if (wgs >= kManyWgs) {
     for (int nt : {256, 512})
