@@ -224,12 +224,12 @@ def test_topk_adversarial_rows(k):
     assert np.array_equal(got.cpu().numpy(), want)
 
 
-@pytest.mark.parametrize("k", [2048, 37])
-def test_topk_adversarial_wide_rows(k):
-    """The same rows 40000 wide: three segments per row whose winners are
-    merged, ties and fallbacks in both passes."""
-    _say(f"topk_rows: adversarial rows 40000 wide, k={k}")
-    L, lens = _adversarial_rows(40000)
+@pytest.mark.parametrize("k,width", [(2048, 40000), (37, 40000), (2048, 100000), (37, 100000)])
+def test_topk_adversarial_wide_rows(k, width):
+    """The same rows 40000 wide (one pass) and 100000 wide (seven segments
+    whose winners are merged): ties and the exact fallbacks of every pass."""
+    _say(f"topk_rows: adversarial rows {width} wide, k={k}")
+    L, lens = _adversarial_rows(width)
     got = sai.topk_rows(torch.from_numpy(L).to(DEV), torch.from_numpy(lens).to(DEV), k)
     want = O.topk_rows(L, lens, k)
     assert np.array_equal(got.cpu().numpy(), want)
@@ -257,7 +257,7 @@ def _nan_rows(W):
     return L, lens
 
 
-@pytest.mark.parametrize("width", [9000, 40000, 140000])
+@pytest.mark.parametrize("width", [9000, 40000, 100000, 140000])
 def test_topk_nan_ranks_last(width):
     """NaN ranks below -inf and NaNs tie by index on every selection path
     (one pass, segments + merge, streaming), as the oracle ranks them."""
