@@ -879,10 +879,12 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EARLY ? 1 : 
 // spaced columns, loaded beside the row, are the sample: the 11-bit digit
 // histogram of their keys, then the next 11 bits of the samples in the
 // chosen digit, give key_lo, the sampled bound on the k-th largest key with
-// the same 30 % rank margin, to 22 key bits.  The logits at or above it
-// (about 1.3 k) are compacted into LDS in any order (a wave reserves its
-// slots with one atomic), and the linear histogram, the threshold-bin rank
-// and the output run on 4 compacted keys per thread.  The output marks the
+// the same 30 % rank margin, to 22 key bits.  The columns of the logits at
+// or above it (about 1.3 k) are compacted into LDS in any order (each
+// thread marks its qualifying registers in a bit mask and writes only
+// those columns; a wave reserves its slots with one atomic), and the
+// linear histogram, the threshold-bin rank and the output run on 4
+// compacted keys per thread, read back from the row.  The output marks the
 // winners in two column bitmaps (above T, equal to T); each thread then owns
 // 64 consecutive columns of them, and a scan of the per-thread counts puts
 // every winner at its ascending-column slot.  A row the compacted keys
@@ -900,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   __shared__ __align__(16) int s_h1[kBins];  // linear bins
   __shared__ __align__(16) int s_h2[kBins];  // next 11 bits of the samples in the chosen digit
   __shared__ __align__(16) uint32_t s_ck[kCompCap];  // compacted keys, then the winner bitmaps
-  __shared__ uint16_t s_cp[kCompCap];                // their columns
+  __shared__ uint16_t s_cp[kCompCap + 1];            // their columns (slot kCompCap: past the capacity)
   static_assert(2 * kMapWords <= kCompCap, "the bitmaps fit the key list");
   uint32_t* const s_bgt = s_ck;              // bit c: column c is above T
   uint32_t* const s_beq = s_ck + kMapWords;  // bit c: column c equals T
@@ -1030,26 +1032,23 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
 
   // 2. compaction of the logits >= v_lo, i.e. the keys >= key_lo (v_lo is
   // the finite float whose key is key_lo; NaN compares false)
+  // Each thread marks its qualifying positions in a 64-bit mask and writes
+  // only their columns (a loop over the set bits, about 3 per thread); the
+  // few compacted logits are read back from the row (in L2) as keys.
   {
-    int cnt = 0;
+    uint64_t qm = 0;
 #pragma unroll
-    for (int e = 0; e < 4 * G; ++e) cnt += v[e] >= v_lo;
+    for (int e = 0; e < 4 * G; ++e) qm |= (uint64_t)(v[e] >= v_lo) << e;
+    const int cnt = __popcll(qm);
     const int incl = wave_scan_dpp(cnt);
     int wbase = 0;
     if (lane == 63) wbase = (int)atomicAdd(&s_misc[2], (uint32_t)incl);
     int off = __builtin_amdgcn_readlane(wbase, 63) + incl - cnt;
-#pragma unroll
-    for (int j = 0; j < G; ++j) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        if (v[4 * j + i] >= v_lo) {
-          if (off < kCompCap) {
-            s_ck[off] = sel_key(v[4 * j + i]);
-            s_cp[off] = (uint16_t)(4 * (tid + j * NT) + i);
-          }
-          ++off;
-        }
-      }
+    while (qm != 0) {
+      const int e = (int)__builtin_ctzll(qm);
+      qm &= qm - 1;
+      s_cp[min(off, kCompCap)] = (uint16_t)(4 * (tid + (e >> 2) * NT) + (e & 3));
+      ++off;
     }
   }
   __syncthreads();
@@ -1063,9 +1062,10 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
 #pragma unroll
   for (int j = 0; j < CPER; ++j) {
     const int i = tid + j * NT;
-    ckey[j] = i < total ? s_ck[i] : 0u;
     ccol[j] = i < total ? (int32_t)s_cp[i] : -1;
   }
+#pragma unroll
+  for (int j = 0; j < CPER; ++j) ckey[j] = ccol[j] >= 0 ? sel_key(x[ccol[j]]) : 0u;
 
   // 3. linear bins over [v_lo, v_top]; the threshold bin's keys ranked by
   // brute force give T
