@@ -562,12 +562,15 @@ def test_decode_pipeline_graph_capture_replays_match_eager():
             assert torch.equal(a, b)
 
 
-def test_wide_row_pipeline_graph_capture_replays_match_eager():
-    """Rows wider than one top-k segment (segment pass, candidate lists in
-    the workspace, merge pass) captured in a hipGraph: every replay equals
-    the eager result, with eager work between replays."""
-    _say("hipGraph capture of the decode pipeline, 40960-column rows (segments + merge)")
-    wl = synth.custom(4, 2, [40000, 20000, 3000, 17000], num_blocks=1500, bt_width=640, seed=47)
+@pytest.mark.parametrize("ctx,num_blocks,bt_width", [([40000, 20000, 3000, 17000], 1500, 640),
+                                                     ([70000, 30000, 3000, 66000], 3000, 1100)])
+def test_wide_row_pipeline_graph_capture_replays_match_eager(ctx, num_blocks, bt_width):
+    """Rows wider than one top-k segment captured in a hipGraph: 40960
+    columns (one pass of the wide-row kernel) and 70400 columns (segment
+    pass, candidate lists in the workspace, merge pass).  Every replay
+    equals the eager result, with eager work between replays."""
+    _say(f"hipGraph capture of the decode pipeline, {bt_width * 64}-column rows")
+    wl = synth.custom(4, 2, ctx, num_blocks=num_blocks, bt_width=bt_width, seed=47)
     g = GpuWorkload(wl)
     q = g.q_fp8.view(4, 2, 64, 128)
     eager = sai.decode_indexer(q, g.w_eff, g.pool, g.block_table, g.ctx)
