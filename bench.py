@@ -31,8 +31,9 @@ global slot ids the last indexer step produced, timed after the indexer's
 timed region with its own roofline (bf16 MFMA peak), and the oracle's decode
 on three sampled rows as its CPU baseline and parity check (--no-mla skips it),
 and a third, "fused_producers": the rotary + fp8 quantiser + cache write (K)
-and rotary + quantiser + weight fold (q) kernels timed on their own with their
-HBM rooflines (--no-producers skips it).
+and rotary + quantiser + weight fold (q) kernels, and the plain K writer and
+query producer, timed on their own with their HBM rooflines (--no-producers
+skips it).
 """
 import argparse
 import ctypes
@@ -451,15 +452,17 @@ PRODUCER_ROPE_DIM = 64
 
 
 def producer_leg(torch, lib, dev, ev, arm, s_ptr, n_k=65536, n_q=4096, reps=10):
-    """The fused producers timed on their own (dispatch-carried events),
-    after the indexer's timed region, into a cache of their own: the K
+    """The producers timed on their own (dispatch-carried events), after
+    the indexer's timed region, into a cache of their own: the fused K
     writer rotates, quantises and scatters n_k bf16 K rows to random slots
-    of a 2048-block cache; the query producer rotates and quantises n_q query
-    rows and folds their scales into the head weights.  Both are byte movers:
-    HBM roofline on their algorithmic bytes (K: 256 B in, 8 B position, 8 B
-    slot, the position's cos and sin rows, 132 B out per token; q: 16 KB in,
-    8 B position, cos and sin rows, 256 B weights in, 8 KB codes + 256 B
-    folded weights + 4 B scale out per row)."""
+    of a 2048-block cache; the fused query producer rotates and quantises
+    n_q query rows and folds their scales into the head weights; the plain
+    K writer and query producer do the same without the rotation.  All are
+    byte movers: HBM roofline on their algorithmic bytes (K: 256 B in, 8 B
+    slot, 132 B out per token, plus 8 B position and the position's cos and
+    sin rows when rotating; q: 16 KB in, 256 B weights in, 8 KB codes +
+    256 B folded weights + 4 B scale out per row, plus 8 B position and cos
+    and sin rows when rotating)."""
     g = torch.Generator(device=dev)
     g.manual_seed(11)
     half = PRODUCER_ROPE_DIM // 2
@@ -488,11 +491,20 @@ def producer_leg(torch, lib, dev, ev, arm, s_ptr, n_k=65536, n_q=4096, reps=10):
         return lib.indexer_q_rope_quant(P_(q), P_(qpos), P_(cos), P_(sin), P, PRODUCER_ROPE_DIM, P_(w), n_q,
                                         P_(qf), P_(weff), P_(qs), s_ptr)
 
+    # the plain (rotation-free) producers on the same inputs
+    def kplain():
+        return lib.indexer_k_cache_write(P_(k), k.stride(0), P_(slots), n_k, P_(cache), nb, s_ptr)
+
+    def qplain():
+        return lib.indexer_q_quant(P_(q), P_(w), n_q, P_(qf), P_(weff), P_(qs), s_ptr)
+
     res = {}
     table_row = 2 * half * 4
-    for name, call, units, per in (("indexer_k_rope_cache_write", kcall, n_k, 256 + 8 + 8 + table_row + 132),
-                                   ("indexer_q_rope_quant", qcall, n_q,
-                                    16384 + 8 + table_row + 256 + 8192 + 256 + 4)):
+    for name, call, units, per, rope in (
+            ("indexer_k_rope_cache_write", kcall, n_k, 256 + 8 + 8 + table_row + 132, PRODUCER_ROPE_DIM),
+            ("indexer_q_rope_quant", qcall, n_q, 16384 + 8 + table_row + 256 + 8192 + 256 + 4, PRODUCER_ROPE_DIM),
+            ("indexer_k_cache_write", kplain, n_k, 256 + 8 + 132, 0),
+            ("indexer_q_quant", qplain, n_q, 16384 + 256 + 8192 + 256 + 4, 0)):
         for _ in range(2):
             assert call() == 0
         e0, e1 = ev.create(reps), ev.create(reps)
@@ -504,7 +516,7 @@ def producer_leg(torch, lib, dev, ev, arm, s_ptr, n_k=65536, n_q=4096, reps=10):
         ev.destroy(e0 + e1)
         alg = units * per
         gbps = alg / t / 1e9
-        res[name] = {"units": units, "rope_dim": PRODUCER_ROPE_DIM, "avg_launch_us": round(t * 1e6, 3),
+        res[name] = {"units": units, "rope_dim": rope, "avg_launch_us": round(t * 1e6, 3),
                      "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
                                   "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None,
                                   "alg_bytes_per_launch": alg}}
