@@ -892,8 +892,9 @@ __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(EARLY ? 1 : 
 // linear histogram, the threshold-bin rank and the output run on 4
 // compacted keys per thread, read back from the row.  The output marks the
 // winners in two column bitmaps (above T, equal to T); each thread then owns
-// 64 consecutive columns of them, and a scan of the per-thread counts puts
-// every winner at its ascending-column slot.  A row the compacted keys
+// 16, 32 or 64 consecutive columns of them (as the row's length needs, so
+// the winners spread over all threads), and a scan of the per-thread counts
+// puts every winner at its ascending-column slot.  A row the compacted keys
 // cannot settle (more than kCompCap keys at or above the bound, fewer than
 // k, an unusable value range or threshold bin) takes the exact radix select
 // over the row in memory instead.
@@ -1120,18 +1121,30 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   }
 
   // 4. ordered output through the bitmaps: thread t owns columns
-  // [64t, 64t + 64); counts packed as (equal << 12) | above (above-T totals
-  // stay below k <= 2048, equal totals at most kCompCap)
+  // [Ct, Ct + C), C = 16, 32 or 64 as the row needs (so the winners of a
+  // shorter row spread over all threads too); counts packed as
+  // (equal << 12) | above (above-T totals stay below k <= 2048, equal
+  // totals at most kCompCap)
 #pragma unroll
   for (int j = 0; j < CPER; ++j) {
     if (ckey[j] > T) atomicOr(&s_bgt[ccol[j] >> 5], 1u << (ccol[j] & 31));
     else if (ckey[j] == T && ckey[j] != 0u) atomicOr(&s_beq[ccol[j] >> 5], 1u << (ccol[j] & 31));
   }
   __syncthreads();
-  const uint2 g2 = reinterpret_cast<const uint2*>(s_bgt)[tid];
-  const uint2 e2 = reinterpret_cast<const uint2*>(s_beq)[tid];
-  const uint64_t gm = (uint64_t)g2.x | ((uint64_t)g2.y << 32);
-  const uint64_t em = (uint64_t)e2.x | ((uint64_t)e2.y << 32);
+  const int cs = n <= 16 * NT ? 4 : n <= 32 * NT ? 5 : 6;  // log2 C, uniform
+  uint64_t gm, em;
+  if (cs == 6) {
+    const uint2 g2 = reinterpret_cast<const uint2*>(s_bgt)[tid];
+    const uint2 e2 = reinterpret_cast<const uint2*>(s_beq)[tid];
+    gm = (uint64_t)g2.x | ((uint64_t)g2.y << 32);
+    em = (uint64_t)e2.x | ((uint64_t)e2.y << 32);
+  } else if (cs == 5) {
+    gm = s_bgt[tid];
+    em = s_beq[tid];
+  } else {
+    gm = (s_bgt[tid >> 1] >> (16 * (tid & 1))) & 0xFFFFu;
+    em = (s_beq[tid >> 1] >> (16 * (tid & 1))) & 0xFFFFu;
+  }
   const int packed = __popcll(gm) | (__popcll(em) << 12);
   const int inc = wave_scan_dpp(packed);
   if (lane == 63) s_wsum[wid] = inc;
@@ -1152,7 +1165,7 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
       if (eq_b < need) pos = gt_b + eq_b;
       ++eq_b;
     }
-    if ((unsigned)pos < (unsigned)k) emit(pos, 64 * tid + b);
+    if ((unsigned)pos < (unsigned)k) emit(pos, (tid << cs) + b);
   }
 }
 
