@@ -908,11 +908,10 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   __shared__ __align__(16) int s_h0[kBins];  // sample digits
   __shared__ __align__(16) int s_h1[kBins];  // linear bins
   __shared__ __align__(16) int s_h2[kBins];  // next 11 bits of the samples in the chosen digit
-  __shared__ __align__(16) uint32_t s_ck[kCompCap];  // compacted keys, then the winner bitmaps
-  __shared__ uint16_t s_cp[kCompCap + 1];            // their columns (slot kCompCap: past the capacity)
-  static_assert(2 * kMapWords <= kCompCap, "the bitmaps fit the key list");
-  uint32_t* const s_bgt = s_ck;              // bit c: column c is above T
-  uint32_t* const s_beq = s_ck + kMapWords;  // bit c: column c equals T
+  __shared__ __align__(16) uint32_t s_map[2 * kMapWords];  // the winner bitmaps
+  __shared__ uint16_t s_cp[kCompCap + 1];  // compacted columns (slot kCompCap: past the capacity)
+  uint32_t* const s_bgt = s_map;              // bit c: column c is above T
+  uint32_t* const s_beq = s_map + kMapWords;  // bit c: column c equals T
   __shared__ uint32_t s_cand[kCandMax];
   __shared__ int s_wsum[kWaves + 1];
   __shared__ uint32_t s_misc[3];  // [0] threshold-bin keys, [1] largest sampled key, [2] compacted
@@ -1080,8 +1079,8 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   for (int j = 0; j < CPER; ++j)
     if (ckey[j] != 0u) atomicAdd(&s_h1[fbin(ckey[j])], 1);
   __syncthreads();
-  // every thread has its compacted keys: the key list becomes the bitmaps
-  for (int i = tid; i < 2 * kMapWords; i += NT) s_ck[i] = 0u;
+  // the bitmaps are cleared here and published by the pick's barrier
+  for (int i = tid; i < 2 * kMapWords; i += NT) s_map[i] = 0u;
   const BinPick p1 = pick(s_h1, k);
   if (p1.found) {
 #pragma unroll
