@@ -921,6 +921,17 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
   const int r = blockIdx.x;
   const int n = (int)min((int64_t)max(row_len[r], 0), stride);
+  // Partner row r ^ 8 runs on the same XCD (workgroup g on XCD g mod 8):
+  // this workgroup loads one word of each 128-byte line of the upper half
+  // of a partner longer than kSegCols, so that half reaches the shared L2
+  // through this CU's miss queue while the partner's own queue works on its
+  // lower half (a long row arrives at about 32 GB/s through one CU).  The
+  // word is folded into a value nothing reads.
+  const int pr = min(r ^ 8, (int)gridDim.x - 1);
+  const int np = (int)min((int64_t)max(row_len[pr], 0), stride);
+  const int pline = (np >> 6) + tid;  // line of this thread's word: upper half, one line per thread
+  const float* pfa =
+      np > kSegCols && 32 * pline < np ? logits + (int64_t)pr * stride + 32 * pline : logits;
   const int32_t req = sm.out ? sm.row_req[r] : 0;
   const bool bt_lds = sm.out && sm.bt_stride <= kBtLds;
   if (bt_lds) {  // published by the first barrier below
@@ -970,6 +981,8 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
   // the sample: columns floor(s*n/S), s < S, two per thread
   const float sv0 = x[(int)(((uint32_t)tid * (uint32_t)n) / S)];
   const float sv1 = x[(int)(((uint32_t)(tid + NT) * (uint32_t)n) / S)];
+  const float pfv = *pfa;         // the partner's word, issued after this row's loads
+  asm volatile("" ::: "memory");  // keeps it here: its value is used only at the end
   for (int i = tid; i < kBins; i += NT) {
     s_h0[i] = 0;
     s_h1[i] = 0;
@@ -1166,6 +1179,7 @@ __global__ __launch_bounds__(kThreads) void topk_wide_kernel(
     }
     if ((unsigned)pos < (unsigned)k) emit(pos, (tid << cs) + b);
   }
+  if (__float_as_uint(pfv) == 0x7FC00001u && k < 0) out_idx[0] = 0;  // never true (k >= 1)
 }
 
 // How topk_rows handles a row pitch: rows up to kSegCols columns are
