@@ -591,45 +591,60 @@ __global__ __launch_bounds__(512) void sparse_mla_decode_wide_kernel(
     for (int c = 0; c < nchunks; ++c) {
       const MlaChunkBf& b = buf[cur];
       const uint8_t* kvb = reinterpret_cast<const uint8_t*>(&b.kv[0][0]);
-      // partial S^T over this wave's two tiles (each scaled) and RoPE step,
-      // tokens n (acc 0) and 16+n (acc 1)
       v4f s0 = zero, s1 = zero;
+      auto qk = [&]() __attribute__((always_inline)) {
+        // partial S^T over this wave's two tiles (each scaled) and RoPE step,
+        // tokens n (acc 0) and 16+n (acc 1)
 #pragma unroll
-      for (int w2 = 0; w2 < 2; ++w2) {
-        const int w = 2 * dh + w2;
-        v4f a0 = zero, a1 = zero;
+        for (int w2 = 0; w2 < 2; ++w2) {
+          const int w = 2 * dh + w2;
+          v4f a0 = zero, a1 = zero;
 #pragma unroll
-        for (int st4 = 0; st4 < 4; ++st4) {
-          // chunk 16w + 4 st4 + g: bits 3+ are constant, bits 0-2 come from the lane
-          const uint8_t* rp = kvb + (st4 & 1 ? qk1 : qk0) + ((16 * w + 8 * (st4 >> 1)) << 4);
-          const uint4 c0 = *reinterpret_cast<const uint4*>(rp);
-          const uint4 c1 = *reinterpret_cast<const uint4*>(rp + 16 * kMlaKv * 2);
-          a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c0), qa[4 * w2 + st4], a0, 0, 0, 0);
-          a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c1), qa[4 * w2 + st4], a1, 0, 0, 0);
+          for (int st4 = 0; st4 < 4; ++st4) {
+            // chunk 16w + 4 st4 + g: bits 3+ are constant, bits 0-2 come from the lane
+            const uint8_t* rp = kvb + (st4 & 1 ? qk1 : qk0) + ((16 * w + 8 * (st4 >> 1)) << 4);
+            const uint4 c0 = *reinterpret_cast<const uint4*>(rp);
+            const uint4 c1 = *reinterpret_cast<const uint4*>(rp + 16 * kMlaKv * 2);
+            a0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c0), qa[4 * w2 + st4], a0, 0, 0, 0);
+            a1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(c1), qa[4 * w2 + st4], a1, 0, 0, 0);
+          }
+          s0 += a0 * *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
+          s1 += a1 * *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
         }
-        s0 += a0 * *reinterpret_cast<const v4f*>(&b.sct[w][4 * g]);
-        s1 += a1 * *reinterpret_cast<const v4f*>(&b.sct[w][16 + 4 * g]);
+        {
+          const uint4 p0 = b.pe[n][(4 * dh + g) ^ sw];
+          const uint4 p1 = b.pe[16 + n][(4 * dh + g) ^ sw];
+          s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp, s0, 0, 0, 0);
+          s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp, s1, 0, 0, 0);
+        }
+        // the pair's halves meet in LDS; both waves form the same sum
+        // (x + y == y + x), hence the same softmax state
+        xs[c & 1][hw][dh][0][lane] = s0;
+        xs[c & 1][hw][dh][1][lane] = s1;
+      };
+      auto stage = [&]() __attribute__((always_inline)) {
+        // One barrier a chunk: before it, stage chunk c+1 into the third
+        // buffer (its last reader, chunk c-2's P.V, finished before every wave
+        // reached the previous barrier) and issue the loads of chunk c+2; after
+        // it, the partial scores and chunk c+1 are visible.  The partial
+        // scores alternate between two arrays for the same reason.  Past the
+        // end these touch only valid addresses and are never read.
+        mla_stage8_to_lds_bf(buf[nxt], st);
+        st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
+                        block_stride);
+        id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
+      };
+      // Waves are dealt to the four SIMDs in turn, so waves hw and hw+4 (the
+      // two halves of one head block) share a SIMD.  They take the two tasks
+      // before the barrier in opposite orders, so that one's MFMAs run while
+      // the other converts and stores the next chunk.
+      if (dh == 0) {
+        qk();
+        stage();
+      } else {
+        stage();
+        qk();
       }
-      {
-        const uint4 p0 = b.pe[n][(4 * dh + g) ^ sw];
-        const uint4 p1 = b.pe[16 + n][(4 * dh + g) ^ sw];
-        s0 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p0), qp, s0, 0, 0, 0);
-        s1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(p1), qp, s1, 0, 0, 0);
-      }
-      // the pair's halves meet in LDS; both waves form the same sum
-      // (x + y == y + x), hence the same softmax state
-      xs[c & 1][hw][dh][0][lane] = s0;
-      xs[c & 1][hw][dh][1][lane] = s1;
-      // One barrier a chunk: before it, stage chunk c+1 into the third
-      // buffer (its last reader, chunk c-2's P.V, finished before every wave
-      // reached the previous barrier) and issue the loads of chunk c+2; after
-      // it, the partial scores and chunk c+1 are visible.  The partial
-      // scores alternate between two arrays for the same reason.  Past the
-      // end these touch only valid addresses and are never read.
-      mla_stage8_to_lds_bf(buf[nxt], st);
-      st = mla_gather8(cache, id, base0 + (c + 2) * kMlaChunk, lim, num_slots, (uint32_t)block_size,
-                      block_stride);
-      id = mla_load_id(srow, base0 + (c + 3) * kMlaChunk, lim);
       __syncthreads();
       s0 += xs[c & 1][hw][dh ^ 1][0][lane];
       s1 += xs[c & 1][hw][dh ^ 1][1][lane];
